@@ -1,0 +1,253 @@
+"""CPU oracle for the batch-invariant int8 linear layer (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+CPU-baseline leg of the benchmark may import this package.  The product path
+(the HIP library and its Python binding) never imports, loads or calls it,
+and it imports nothing from the product package.
+
+The arithmetic lives in ``oracle.c`` (plain scalar C, one binary32 operation
+per expression, no fused multiply-add); this module only marshals numpy
+arrays through ctypes.  bf16 and fp16 tensors travel as their uint16 bit
+patterns.  Every function cites, in ``oracle.c``, the passage of the pages it
+follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+# gcc flags: one rounding per float operation, no contraction, no fast-math,
+# no host-specific instruction selection.
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c11",
+          "-Wall", "-Wextra", "-pthread"]
+
+OK = 0
+ERR_ARGS = -1
+ERR_OVERFLOW = -2
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc and return its path."""
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    f32 = ctypes.c_float
+    sig = {
+        "oracle_f32_add": (f32, [f32, f32]),
+        "oracle_f32_sub": (f32, [f32, f32]),
+        "oracle_f32_mul": (f32, [f32, f32]),
+        "oracle_f32_div": (f32, [f32, f32]),
+        "oracle_i32_to_f32": (f32, [ctypes.c_int32]),
+        "oracle_bf16_rne": (ctypes.c_uint16, [ctypes.c_uint32]),
+        "oracle_bf16_to_f32": (f32, [ctypes.c_uint16]),
+        "oracle_fp16_to_f32": (f32, [ctypes.c_uint16]),
+        "oracle_epilogue": (ctypes.c_uint16, [ctypes.c_int32, f32, f32]),
+        "oracle_block_partial": (f32, [ctypes.c_int32, f32, ctypes.c_uint16]),
+        "oracle_tree_sum": (f32, [P, I64]),
+        "oracle_dot_i8": (ctypes.c_int, [P, P, I64, P]),
+        "oracle_quantize_token": (ctypes.c_int, [P, I64, I64, P, P]),
+        "oracle_quantize_block32": (ctypes.c_int, [P, I64, I64, P, P]),
+        "oracle_w8a8": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, ctypes.c_int]),
+        "oracle_blockq8": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, ctypes.c_int]),
+        "oracle_argmax_row": (ctypes.c_int32, [P, I64]),
+        "oracle_lm_head_argmax": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, ctypes.c_int]),
+        "oracle_pow2_nearest": (f32, [f32]),
+        "oracle_pow2_requant": (ctypes.c_int, [P, P, I64, I64, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _arr(a, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.dtype(dtype):
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def _check(status: int, what: str):
+    if status == ERR_OVERFLOW:
+        raise OracleError(f"{what}: int32 accumulator overflow (int64 shadow differs)")
+    if status != OK:
+        raise OracleError(f"{what}: status {status}")
+
+
+# --- scalar primitives (one binary32 operation each) ------------------------
+
+def f32_add(a, b) -> np.float32:
+    return np.float32(_load().oracle_f32_add(float(np.float32(a)), float(np.float32(b))))
+
+
+def f32_sub(a, b) -> np.float32:
+    return np.float32(_load().oracle_f32_sub(float(np.float32(a)), float(np.float32(b))))
+
+
+def f32_mul(a, b) -> np.float32:
+    return np.float32(_load().oracle_f32_mul(float(np.float32(a)), float(np.float32(b))))
+
+
+def f32_div(a, b) -> np.float32:
+    return np.float32(_load().oracle_f32_div(float(np.float32(a)), float(np.float32(b))))
+
+
+def i32_to_f32(v: int) -> np.float32:
+    return np.float32(_load().oracle_i32_to_f32(int(v)))
+
+
+def bf16_rne(bits: int) -> int:
+    """fp32 bit pattern -> bf16 bit pattern, round to nearest even."""
+    return int(_load().oracle_bf16_rne(int(bits) & 0xFFFFFFFF))
+
+
+def bf16_to_f32(h: int) -> np.float32:
+    return np.float32(_load().oracle_bf16_to_f32(int(h)))
+
+
+def fp16_to_f32(h: int) -> np.float32:
+    return np.float32(_load().oracle_fp16_to_f32(int(h)))
+
+
+def epilogue(acc: int, s_a, s_w) -> int:
+    """bf16 bits of (fl32(acc) * s_a) * s_w."""
+    return int(_load().oracle_epilogue(int(acc), float(np.float32(s_a)), float(np.float32(s_w))))
+
+
+def block_partial(isum: int, d_a, d_w_bits: int) -> np.float32:
+    return np.float32(_load().oracle_block_partial(int(isum), float(np.float32(d_a)), int(d_w_bits)))
+
+
+def tree_sum(leaves) -> np.float32:
+    a = _arr(np.asarray(leaves, dtype=np.float32), np.float32)
+    return np.float32(_load().oracle_tree_sum(_ptr(a), a.size))
+
+
+def dot_i8(a, w) -> int:
+    a = _arr(a, np.int8)
+    w = _arr(w, np.int8)
+    assert a.size == w.size
+    out = np.zeros(1, np.int32)
+    _check(_load().oracle_dot_i8(_ptr(a), _ptr(w), a.size, _ptr(out)), "dot_i8")
+    return int(out[0])
+
+
+# --- tensor operations -------------------------------------------------------
+
+def quantize_token(x_bits: np.ndarray):
+    """x bf16 bits uint16 [b, K] -> (q int8 [b, K], s fp32 [b])."""
+    x = _arr(x_bits, np.uint16)
+    b, K = x.shape
+    q = np.empty((b, K), np.int8)
+    s = np.empty((b,), np.float32)
+    _check(_load().oracle_quantize_token(_ptr(x), b, K, _ptr(q), _ptr(s)), "quantize_token")
+    return q, s
+
+
+def quantize_block32(x_bits: np.ndarray):
+    """x bf16 bits uint16 [b, K] -> (q int8 [b, K], d fp32 [b, K/32])."""
+    x = _arr(x_bits, np.uint16)
+    b, K = x.shape
+    q = np.empty((b, K), np.int8)
+    d = np.empty((b, K // 32), np.float32)
+    _check(_load().oracle_quantize_block32(_ptr(x), b, K, _ptr(q), _ptr(d)), "quantize_block32")
+    return q, d
+
+
+def w8a8(q, s_a, w, s_w, nthreads: int = 0) -> np.ndarray:
+    """-> y bf16 bits uint16 [b, N]."""
+    q = _arr(q, np.int8)
+    s_a = _arr(s_a, np.float32)
+    w = _arr(w, np.int8)
+    s_w = _arr(s_w, np.float32)
+    b, K = q.shape
+    N, K2 = w.shape
+    assert K == K2 and s_a.shape == (b,) and s_w.shape == (N,)
+    y = np.empty((b, N), np.uint16)
+    _check(_load().oracle_w8a8(_ptr(q), _ptr(s_a), _ptr(w), _ptr(s_w), b, N, K, _ptr(y), nthreads), "w8a8")
+    return y
+
+
+def blockq8(q, d_a, w, d_w_bits, nthreads: int = 0) -> np.ndarray:
+    """q int8 [b,K], d_a fp32 [b,K/32], w int8 [N,K], d_w fp16 bits [N,K/32] -> y bf16 bits [b,N]."""
+    q = _arr(q, np.int8)
+    d_a = _arr(d_a, np.float32)
+    w = _arr(w, np.int8)
+    d_w = _arr(d_w_bits, np.uint16)
+    b, K = q.shape
+    N = w.shape[0]
+    assert w.shape == (N, K) and d_a.shape == (b, K // 32) and d_w.shape == (N, K // 32)
+    y = np.empty((b, N), np.uint16)
+    _check(_load().oracle_blockq8(_ptr(q), _ptr(d_a), _ptr(w), _ptr(d_w), b, N, K, _ptr(y), nthreads),
+           "blockq8")
+    return y
+
+
+def argmax_row(y_bits) -> int:
+    y = _arr(y_bits, np.uint16)
+    return int(_load().oracle_argmax_row(_ptr(y), y.size))
+
+
+def lm_head_argmax(q, s_a, w, s_w, nthreads: int = 0):
+    """-> (logits bf16 bits uint16 [b, N], argmax int32 [b])."""
+    q = _arr(q, np.int8)
+    s_a = _arr(s_a, np.float32)
+    w = _arr(w, np.int8)
+    s_w = _arr(s_w, np.float32)
+    b, K = q.shape
+    N = w.shape[0]
+    logits = np.empty((b, N), np.uint16)
+    am = np.empty((b,), np.int32)
+    _check(_load().oracle_lm_head_argmax(_ptr(q), _ptr(s_a), _ptr(w), _ptr(s_w), b, N, K, _ptr(logits),
+                                         _ptr(am), nthreads), "lm_head_argmax")
+    return logits, am
+
+
+def pow2_nearest(s) -> np.float32:
+    return np.float32(_load().oracle_pow2_nearest(float(np.float32(s))))
+
+
+def pow2_requant(w, s_w):
+    """-> (w' int8 [N, K], s' fp32 [N])."""
+    w = _arr(w, np.int8)
+    s_w = _arr(s_w, np.float32)
+    N, K = w.shape
+    wo = np.empty((N, K), np.int8)
+    so = np.empty((N,), np.float32)
+    _check(_load().oracle_pow2_requant(_ptr(w), _ptr(s_w), N, K, _ptr(wo), _ptr(so)), "pow2_requant")
+    return wo, so

@@ -1,0 +1,436 @@
+/*
+ * CPU oracle for the batch-invariant int8 linear layer of decode and
+ * speculative-verify passes.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file: only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header, table or helper
+ * with the HIP library.
+ *
+ * It is deliberately plain and slow: scalar loops, one IEEE-754 binary32
+ * operation per C expression, no blocking, no vectorisation, no fused
+ * multiply-add.  Build with `gcc -O2 -ffp-contract=off` (no -ffast-math, no
+ * -march=native) on x86-64, where float arithmetic is SSE scalar with one
+ * rounding per operation and FLT_EVAL_METHOD == 0.
+ *
+ * Sources (page title, then section / table):
+ *  [P1] "why speculative decoding changed my output"
+ *       - "floats care about order": fp32 addition is not associative; near
+ *         1e8 neighbouring floats are 8 apart.
+ *       - "the mat-vec kernel": int8 activations in blocks of 32, four int8
+ *         products summed exactly into int32 per instruction, each block's
+ *         integer result scaled into an fp32 accumulator.
+ *  [P2] "My speculative decoder got slower"
+ *       - "We're nowhere near SOL": a vocab head that returns only the
+ *         winning token.
+ *       - "Two matmul schedules that survived": split-K changes where a
+ *         float running sum is rounded.
+ *  [P3] "Deterministic LLM Inference Across GPU Kernels: Power-of-Two INT8
+ *       Quantization Scales and the Limits of Tolerance-Based Conformance"
+ *       - Abstract and Fig. 1: W8A8 integer accumulation is exact and
+ *         order-independent under a no-overflow bound; weight scales moved to
+ *         their nearest power of two with the weights re-rounded.
+ *       - Table II: the epilogue faults F1-F5, whose negation fixes the
+ *         canonical epilogue (acc * s_a) * s_w in fp32 with one
+ *         round-to-nearest-even to bfloat16.
+ *
+ * Where the pages leave a step open, the reading taken is stated at the
+ * function that implements it.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARGS (-1)
+#define ORACLE_ERR_OVERFLOW (-2)
+#define ORACLE_ERR_THREAD (-3)
+
+/* ------------------------------------------------------------------------ */
+/* Scalar primitives.  Each is one binary32 operation with the default       */
+/* round-to-nearest-even mode.  Exported so that tests can pin them.         */
+/* ------------------------------------------------------------------------ */
+
+float oracle_f32_add(float a, float b) { return a + b; }
+float oracle_f32_sub(float a, float b) { return a - b; }
+float oracle_f32_mul(float a, float b) { return a * b; }
+float oracle_f32_div(float a, float b) { return a / b; }
+/* int32 -> binary32, rounded to nearest even (cvtsi2ss under the default
+ * MXCSR mode).  Inexact once |v| > 2^24. */
+float oracle_i32_to_f32(int32_t v) { return (float)v; }
+
+static uint32_t f32_bits(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return u;
+}
+
+static float bits_f32(uint32_t u) {
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* binary32 -> bfloat16, round to nearest, ties to even.  A NaN keeps its sign
+ * and is made quiet; overflow carries into the exponent and gives +-Inf;
+ * subnormals are rounded like any other value (no flush to zero). */
+uint16_t oracle_bf16_rne(uint32_t u) {
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+/* bfloat16 -> binary32 is exact: the 16 bits become the high half. */
+float oracle_bf16_to_f32(uint16_t h) { return bits_f32((uint32_t)h << 16); }
+
+/* IEEE binary16 -> binary32, exact, decoded from the field definitions. */
+float oracle_fp16_to_f32(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int exp = (h >> 10) & 0x1F;
+    int man = h & 0x3FF;
+    float mag;
+    if (exp == 0)
+        mag = ldexpf((float)man, -24); /* subnormal: man * 2^-24 */
+    else if (exp == 31)
+        mag = man ? NAN : INFINITY;
+    else
+        mag = ldexpf((float)(man | 0x400), exp - 25); /* 1.man * 2^(exp-15) */
+    return sign ? -mag : mag;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Activation quantization.                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Quantize n bf16 values with one shared scale.  [P1 "the mat-vec kernel"]
+ * gives int8 activations with a float scale; the configuration text gives
+ * the scale as absmax / 127.  Readings taken:
+ *   s = fl(amax / 127) with a correctly rounded division;
+ *   q = clamp(rint_half_even(fl(x / s)), -127, 127), division not a
+ *       reciprocal multiply, so -128 never appears;
+ *   an all-zero group gives s = 0 and q = 0.
+ * |x| and the max are exact; bf16 -> fp32 is exact. */
+static float quantize_group(const uint16_t *x, int64_t n, int8_t *q) {
+    float amax = 0.0f;
+    for (int64_t k = 0; k < n; ++k) {
+        float v = fabsf(oracle_bf16_to_f32(x[k]));
+        if (v > amax) amax = v;
+    }
+    float s = oracle_f32_div(amax, 127.0f);
+    if (s == 0.0f) {
+        for (int64_t k = 0; k < n; ++k) q[k] = 0;
+        return 0.0f;
+    }
+    for (int64_t k = 0; k < n; ++k) {
+        float r = rintf(oracle_f32_div(oracle_bf16_to_f32(x[k]), s));
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        q[k] = (int8_t)r;
+    }
+    return s;
+}
+
+/* Per-token quantization: x bf16 [b, K] -> q int8 [b, K], s fp32 [b]. */
+int oracle_quantize_token(const uint16_t *x, int64_t b, int64_t K, int8_t *q, float *s) {
+    if (!x || !q || !s || b < 0 || K < 1) return ORACLE_ERR_ARGS;
+    for (int64_t t = 0; t < b; ++t) s[t] = quantize_group(x + t * K, K, q + t * K);
+    return ORACLE_OK;
+}
+
+/* Per-32-block quantization: x bf16 [b, K] -> q int8 [b, K],
+ * d fp32 [b, K/32]; each aligned 32-element block has its own scale
+ * ([P1 "the mat-vec kernel"]: activations are int8 in blocks of 32). */
+int oracle_quantize_block32(const uint16_t *x, int64_t b, int64_t K, int8_t *q, float *d) {
+    if (!x || !q || !d || b < 0 || K < 32 || K % 32) return ORACLE_ERR_ARGS;
+    int64_t m = K / 32;
+    for (int64_t t = 0; t < b; ++t)
+        for (int64_t j = 0; j < m; ++j)
+            d[t * m + j] = quantize_group(x + t * K + 32 * j, 32, q + t * K + 32 * j);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exact integer dot product.                                                */
+/* ------------------------------------------------------------------------ */
+
+/* sum_k a[k] * w[k] accumulated in int32 (wrapping arithmetic, so that an
+ * overflow is defined behaviour here) with an int64 shadow.  [P3 Abstract,
+ * Fig. 1]: under a no-overflow bound the int32 sum is exact, so its value is
+ * independent of the order of the additions.  Returns 0 and stores the sum,
+ * or returns ORACLE_ERR_OVERFLOW when the int32 and int64 sums differ. */
+static int dot_i8(const int8_t *a, const int8_t *w, int64_t n, int32_t *out) {
+    uint32_t acc32 = 0;
+    int64_t acc64 = 0;
+    for (int64_t k = 0; k < n; ++k) {
+        int32_t p = (int32_t)a[k] * (int32_t)w[k];
+        acc32 += (uint32_t)p;
+        acc64 += p;
+    }
+    int32_t v = (int32_t)acc32;
+    *out = v;
+    return ((int64_t)v == acc64) ? ORACLE_OK : ORACLE_ERR_OVERFLOW;
+}
+
+/* Exported for tests: the int32 dot product of two int8 vectors. */
+int oracle_dot_i8(const int8_t *a, const int8_t *w, int64_t n, int32_t *out) {
+    if (!a || !w || !out || n < 0) return ORACLE_ERR_ARGS;
+    return dot_i8(a, w, n, out);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Epilogue and block partial.                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Canonical W8A8 epilogue, [P3 Table II] read as the negation of its five
+ * faults: fp32 scales (not F1), no rounding between the two multiplies
+ * (not F2), (acc * s_a) * s_w in that order (not F3), round to nearest even
+ * on output (not F4), scales applied once after the integer sum (not F5).
+ *   y = bf16( fl( fl( fl32(acc) * s_a ) * s_w ) ) */
+uint16_t oracle_epilogue(int32_t acc, float s_a, float s_w) {
+    float a = oracle_i32_to_f32(acc);
+    float t = oracle_f32_mul(a, s_a);
+    float y = oracle_f32_mul(t, s_w);
+    return oracle_bf16_rne(f32_bits(y));
+}
+
+/* One 32-block partial of the block-quantized product.  [P1 "the mat-vec
+ * kernel"] says only that each block's integer result is scaled into fp32;
+ * the order is read to mirror the W8A8 epilogue: (fl32(isum) * d_a) * d_w,
+ * with the fp16 weight scale widened exactly to fp32. */
+float oracle_block_partial(int32_t isum, float d_a, uint16_t d_w) {
+    float a = oracle_i32_to_f32(isum);
+    float t = oracle_f32_mul(a, d_a);
+    return oracle_f32_mul(t, oracle_fp16_to_f32(d_w));
+}
+
+/* ------------------------------------------------------------------------ */
+/* The canonical pairwise tree.                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Root of the tree over leaves [lo, lo + size) where size is a power of
+ * two; leaves at index >= m are +0.0f.  Defined recursively: a single leaf
+ * is itself; otherwise root(left half) + root(right half) in one fl-add.
+ * This is the same as combining adjacent pairs in index order, level by
+ * level. */
+static float tree_rec(const float *leaf, int64_t m, int64_t lo, int64_t size) {
+    if (size == 1) return lo < m ? leaf[lo] : 0.0f;
+    int64_t h = size / 2;
+    float left = tree_rec(leaf, m, lo, h);
+    float right = tree_rec(leaf, m, lo + h, h);
+    return oracle_f32_add(left, right);
+}
+
+static int64_t pow2_ceil(int64_t m) {
+    int64_t L = 1;
+    while (L < m) L *= 2;
+    return L;
+}
+
+/* Canonical tree over m leaves, zero-padded to L = 2^ceil(log2 m).  The fixed
+ * order answers [P1 "the mat-vec kernel"] (the stock block grouping changed
+ * with the token count) and [P2 "Two matmul schedules that survived"]
+ * (split-K moved the rounding points).  Reading: adjacent pairs in index
+ * order, +0.0f leaves added literally. */
+float oracle_tree_sum(const float *leaf, int64_t m) {
+    if (m < 1) return 0.0f;
+    return tree_rec(leaf, m, 0, pow2_ceil(m));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Thread pool over output rows.  Each output element is computed by exactly  */
+/* one thread, start to finish, so the thread count cannot change a result.  */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int op; /* 0 = w8a8, 1 = blockq8 */
+    const int8_t *q;
+    const float *sa;   /* s_a [b] or d_a [b, K/32] */
+    const int8_t *w;
+    const float *sw;   /* s_w [N] (w8a8) */
+    const uint16_t *dw; /* d_w fp16 [N, K/32] (blockq8) */
+    int64_t b, N, K;
+    uint16_t *y;
+    int64_t n0, n1;
+    int status;
+} rows_job;
+
+static void w8a8_rows(rows_job *j) {
+    for (int64_t n = j->n0; n < j->n1; ++n) {
+        const int8_t *wr = j->w + n * j->K;
+        for (int64_t t = 0; t < j->b; ++t) {
+            int32_t acc;
+            if (dot_i8(j->q + t * j->K, wr, j->K, &acc) != ORACLE_OK) j->status = ORACLE_ERR_OVERFLOW;
+            j->y[t * j->N + n] = oracle_epilogue(acc, j->sa[t], j->sw[n]);
+        }
+    }
+}
+
+static void blockq8_rows(rows_job *j) {
+    int64_t m = j->K / 32;
+    float *leaf = (float *)malloc(sizeof(float) * (size_t)m);
+    if (!leaf) {
+        j->status = ORACLE_ERR_ARGS;
+        return;
+    }
+    for (int64_t n = j->n0; n < j->n1; ++n) {
+        const int8_t *wr = j->w + n * j->K;
+        for (int64_t t = 0; t < j->b; ++t) {
+            for (int64_t i = 0; i < m; ++i) {
+                int32_t isum;
+                dot_i8(j->q + t * j->K + 32 * i, wr + 32 * i, 32, &isum); /* |isum| <= 32*128*128 */
+                leaf[i] = oracle_block_partial(isum, j->sa[t * m + i], j->dw[n * m + i]);
+            }
+            float root = oracle_tree_sum(leaf, m);
+            j->y[t * j->N + n] = oracle_bf16_rne(f32_bits(root));
+        }
+    }
+    free(leaf);
+}
+
+static void *rows_worker(void *arg) {
+    rows_job *j = (rows_job *)arg;
+    if (j->op == 0)
+        w8a8_rows(j);
+    else
+        blockq8_rows(j);
+    return NULL;
+}
+
+static int run_rows(rows_job proto, int nthreads) {
+    if (nthreads <= 0) nthreads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > proto.N) nthreads = (int)proto.N;
+    rows_job jobs[256];
+    pthread_t th[256];
+    int started[256];
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = proto;
+        jobs[i].n0 = proto.N * i / nthreads;
+        jobs[i].n1 = proto.N * (i + 1) / nthreads;
+        jobs[i].status = ORACLE_OK;
+        started[i] = 0;
+    }
+    int status = ORACLE_OK;
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, rows_worker, &jobs[i]) == 0)
+            started[i] = 1;
+        else
+            rows_worker(&jobs[i]); /* fall back to running it here */
+    }
+    rows_worker(&jobs[0]);
+    for (int i = 1; i < nthreads; ++i)
+        if (started[i]) pthread_join(th[i], NULL);
+    for (int i = 0; i < nthreads; ++i)
+        if (jobs[i].status != ORACLE_OK) status = jobs[i].status;
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The linear layers.                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* W8A8 linear: q int8 [b, K], s_a fp32 [b], w int8 [N, K], s_w fp32 [N]
+ * -> y bf16 [b, N].  acc = sum_k q[t,k] * w[n,k] exactly in int32
+ * ([P3 Abstract, Fig. 1]), then the canonical epilogue ([P3 Table II]).
+ * Returns ORACLE_ERR_OVERFLOW if any int32 sum left the int32 range. */
+int oracle_w8a8(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int64_t b,
+                int64_t N, int64_t K, uint16_t *y, int nthreads) {
+    if (!q || !s_a || !w || !s_w || !y || b < 0 || N < 1 || K < 1) return ORACLE_ERR_ARGS;
+    if (b == 0) return ORACLE_OK;
+    rows_job j = {0, q, s_a, w, s_w, NULL, b, N, K, y, 0, N, ORACLE_OK};
+    return run_rows(j, nthreads);
+}
+
+/* Block-quantized (q8_0-style) linear: q int8 [b, K], d_a fp32 [b, K/32],
+ * w int8 [N, K], d_w fp16 [N, K/32] -> y bf16 [b, N].  Per 32-block an exact
+ * int32 sum and the block partial, then the canonical tree over the K/32
+ * partials and one rounding to bf16.  [P1 "the mat-vec kernel"]; the tree
+ * reading is at oracle_tree_sum. */
+int oracle_blockq8(const int8_t *q, const float *d_a, const int8_t *w, const uint16_t *d_w,
+                   int64_t b, int64_t N, int64_t K, uint16_t *y, int nthreads) {
+    if (!q || !d_a || !w || !d_w || !y || b < 0 || N < 1 || K < 32 || K % 32) return ORACLE_ERR_ARGS;
+    if (b == 0) return ORACLE_OK;
+    rows_job j = {1, q, d_a, w, NULL, d_w, b, N, K, y, 0, N, ORACLE_OK};
+    return run_rows(j, nthreads);
+}
+
+/* Argmax over one row of bf16 logits: the smallest index whose value equals
+ * the row maximum, comparing the fp32 values of the bf16 numbers (so +0 and
+ * -0 are equal).  [P2 "We're nowhere near SOL"] describes a head returning
+ * only the winning token; the pages do not say how ties break ([P2 "Why the
+ * decoders disagreed?"] shows a real bf16 tie), so the lowest index wins. */
+int32_t oracle_argmax_row(const uint16_t *y, int64_t N) {
+    int32_t best = 0;
+    float bv = oracle_bf16_to_f32(y[0]);
+    for (int64_t n = 1; n < N; ++n) {
+        float v = oracle_bf16_to_f32(y[n]);
+        if (v > bv) {
+            bv = v;
+            best = (int32_t)n;
+        }
+    }
+    return best;
+}
+
+/* LM head for a verify pass: W8A8 logits for every vocab row, then the
+ * per-token argmax.  logits bf16 [b, N] must be provided (the oracle always
+ * materialises them); argmax int32 [b]. */
+int oracle_lm_head_argmax(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w,
+                          int64_t b, int64_t N, int64_t K, uint16_t *logits, int32_t *argmax,
+                          int nthreads) {
+    if (!argmax || !logits) return ORACLE_ERR_ARGS;
+    int st = oracle_w8a8(q, s_a, w, s_w, b, N, K, logits, nthreads);
+    if (st != ORACLE_OK) return st;
+    for (int64_t t = 0; t < b; ++t) argmax[t] = oracle_argmax_row(logits + t * N, N);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Power-of-two weight-scale requantization (offline weight preparation).    */
+/* ------------------------------------------------------------------------ */
+
+/* Nearest power of two to |s| with the sign of s.  [P3 Abstract] says only
+ * "nearest"; reading: write |s| = m * 2^E with m in [1, 2), take 2^E when
+ * m < 1.5 and 2^(E+1) otherwise (linear distance, a tie at m = 1.5 goes to
+ * the larger power).  s = 0 maps to 0. */
+float oracle_pow2_nearest(float s) {
+    if (s == 0.0f) return 0.0f;
+    int e;
+    float f = frexpf(fabsf(s), &e); /* |s| = f * 2^e, f in [0.5, 1) */
+    float p = (f < 0.75f) ? ldexpf(1.0f, e - 1) : ldexpf(1.0f, e);
+    return s < 0.0f ? -p : p;
+}
+
+/* Requantize W8A8 weights to power-of-two scales, re-rounding the weights
+ * ([P3 Abstract]: rewriting the scales without re-rounding the weights was
+ * the artefact; the intervention that works requantizes).  Per row n:
+ *   s'  = nearest power of two of s_w[n]
+ *   w'  = clamp(rint_half_even(w * s / s'), -127, 127)
+ * w * s has at most 8 + 24 significant bits and s' is a power of two, so the
+ * quotient is exact in double and the only rounding is the final rint.
+ * A zero scale gives s' = 0 and w' = 0. */
+int oracle_pow2_requant(const int8_t *w, const float *s_w, int64_t N, int64_t K, int8_t *w_out,
+                        float *s_out) {
+    if (!w || !s_w || !w_out || !s_out || N < 1 || K < 1) return ORACLE_ERR_ARGS;
+    for (int64_t n = 0; n < N; ++n) {
+        float s = s_w[n];
+        float sp = oracle_pow2_nearest(s);
+        s_out[n] = sp;
+        for (int64_t k = 0; k < K; ++k) {
+            if (sp == 0.0f) {
+                w_out[n * K + k] = 0;
+                continue;
+            }
+            double r = rint((double)w[n * K + k] * (double)s / (double)sp);
+            if (r > 127.0) r = 127.0;
+            if (r < -127.0) r = -127.0;
+            w_out[n * K + k] = (int8_t)r;
+        }
+    }
+    return ORACLE_OK;
+}

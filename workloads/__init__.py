@@ -1,0 +1,219 @@
+"""Seeded synthetic inputs shared by the oracle side and the GPU side.
+
+This module draws random numbers and lays them out; it holds none of the
+arithmetic of the method itself (no activation quantization, no integer dot
+products, no epilogue, no tree, no argmax, no scale requantization).  Both
+the tests and the benchmark take their inputs from here, so the oracle and
+the HIP library always see the same bytes.
+
+Recipes (numpy ``Generator(PCG64(seed))``; draws happen in the order listed):
+  * int8 weights: ``integers(-127, 128)``, uniform on [-127, 127];
+  * per-output-channel fp32 scales: log-uniform on [1e-3, 1e-1];
+  * activations: ``standard_normal`` as fp32, rounded to bf16 (round to
+    nearest even, by torch's CPU conversion);
+  * outlier channels: ``round(0.01 * K)`` channel indices from a seeded
+    permutation, the same for every token, scaled by 20 in fp32 and rounded
+    to bf16 again;
+  * q8_0-style block weights: real weights ``standard_normal``, per aligned
+    32-block an fp16 scale ``d = fp16(amax / 127)`` and int8 codes
+    ``clamp(rint(w / d), -127, 127)`` (0 where d == 0).  This is the
+    preparation of a weight file, not a step of the linear layer.
+
+The layer shapes follow Qwen3 models (hidden size, intermediate size and the
+packed qkv / gate_up projections); no model weights are used or needed.
+
+bf16 and fp16 tensors are returned as their uint16 bit patterns.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+# -- shapes -------------------------------------------------------------------
+
+# (name, K, N): input features K, output features N.
+TINY = ("tiny", 512, 256)
+QWEN3_8B = [("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 24576), ("down", 12288, 4096)]
+QWEN3_14B = [("qkv", 5120, 7168), ("o", 5120, 5120), ("gate_up", 5120, 34816), ("down", 17408, 5120)]
+BLOCKQ8_SHAPES = [("bq8_4096", 4096, 4096), ("bq8_12288", 12288, 4096)]
+LM_HEAD = ("lm_head", 4096, 151936)
+
+SEED_TINY = 1001
+SEED_8B = 2001
+SEED_BQ8 = 3001
+SEED_14B = 4001
+SEED_LM_HEAD = 5001
+
+TOKENS_TINY = 5
+TOKENS_8B = 512
+TOKENS_BQ8 = 16
+TOKENS_14B = 512
+TOKENS_LM_HEAD = 64
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest even) with torch's CPU conversion."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def int8_weights(g: np.random.Generator, N: int, K: int) -> np.ndarray:
+    return g.integers(-127, 128, size=(N, K), dtype=np.int8)
+
+
+def log_uniform_scales(g: np.random.Generator, n: int, lo: float = 1e-3, hi: float = 1e-1) -> np.ndarray:
+    return np.exp(g.uniform(np.log(lo), np.log(hi), size=n)).astype(np.float32)
+
+
+def normal_bf16(g: np.random.Generator, b: int, K: int) -> np.ndarray:
+    return f32_to_bf16_bits(g.standard_normal(size=(b, K), dtype=np.float32))
+
+
+def add_outlier_channels(g: np.random.Generator, x_bits: np.ndarray, frac: float = 0.01,
+                         factor: float = 20.0) -> tuple[np.ndarray, np.ndarray]:
+    """Scale round(frac*K) seeded channels by `factor` (fp32) and re-round to bf16."""
+    K = x_bits.shape[1]
+    n_out = int(round(frac * K))
+    idx = np.sort(g.permutation(K)[:n_out])
+    x = bf16_bits_to_f32(x_bits).copy()
+    x[:, idx] = x[:, idx] * np.float32(factor)
+    return f32_to_bf16_bits(x), idx
+
+
+def q8_0_weights(g: np.random.Generator, N: int, K: int) -> tuple[np.ndarray, np.ndarray]:
+    """q8_0-style weight file: int8 codes [N, K] and fp16 block scales [N, K/32] (uint16 bits)."""
+    assert K % 32 == 0
+    w = g.standard_normal(size=(N, K // 32, 32), dtype=np.float32)
+    amax = np.abs(w).max(axis=2)
+    d16 = (amax / np.float32(127.0)).astype(np.float32).astype(np.float16)
+    d32 = d16.astype(np.float32)
+    safe = np.where(d32 == 0, np.float32(1.0), d32)
+    codes = np.rint(w / safe[:, :, None])
+    codes = np.clip(codes, -127, 127)
+    codes = np.where((d32 == 0)[:, :, None], 0, codes).astype(np.int8)
+    return codes.reshape(N, K), d16.view(np.uint16).copy()
+
+
+# -- whole-config generators -----------------------------------------------------
+
+@dataclass
+class W8A8Layer:
+    name: str
+    K: int
+    N: int
+    w: np.ndarray        # int8 [N, K]
+    s_w: np.ndarray      # fp32 [N]
+    x: np.ndarray        # bf16 bits [T, K]
+    outliers: np.ndarray | None
+
+
+def w8a8_layer(name: str, K: int, N: int, seed: int, tokens: int, outliers: bool) -> W8A8Layer:
+    g = rng(seed)
+    w = int8_weights(g, N, K)
+    s_w = log_uniform_scales(g, N)
+    x = normal_bf16(g, tokens, K)
+    idx = None
+    if outliers:
+        x, idx = add_outlier_channels(g, x)
+    return W8A8Layer(name, K, N, w, s_w, x, idx)
+
+
+def tiny_layer() -> W8A8Layer:
+    name, K, N = TINY
+    return w8a8_layer(name, K, N, SEED_TINY, TOKENS_TINY, outliers=False)
+
+
+def qwen3_8b_layer(i: int, tokens: int = TOKENS_8B) -> W8A8Layer:
+    name, K, N = QWEN3_8B[i]
+    return w8a8_layer(name, K, N, SEED_8B + i, tokens, outliers=True)
+
+
+def qwen3_14b_layer(i: int, tokens: int = TOKENS_14B) -> W8A8Layer:
+    name, K, N = QWEN3_14B[i]
+    return w8a8_layer(name, K, N, SEED_14B + i, tokens, outliers=True)
+
+
+def lm_head_layer(tokens: int = TOKENS_LM_HEAD) -> W8A8Layer:
+    name, K, N = LM_HEAD
+    return w8a8_layer(name, K, N, SEED_LM_HEAD, tokens, outliers=False)
+
+
+@dataclass
+class BlockQ8Layer:
+    name: str
+    K: int
+    N: int
+    w: np.ndarray        # int8 [N, K]
+    d_w: np.ndarray      # fp16 bits [N, K/32]
+    x: np.ndarray        # bf16 bits [T, K]
+
+
+def blockq8_layer(i: int, tokens: int = TOKENS_BQ8) -> BlockQ8Layer:
+    name, K, N = BLOCKQ8_SHAPES[i]
+    g = rng(SEED_BQ8 + i)
+    w, d_w = q8_0_weights(g, N, K)
+    x = normal_bf16(g, tokens, K)
+    return BlockQ8Layer(name, K, N, w, d_w, x)
+
+
+# -- crafted inputs for the block tree ------------------------------------------
+
+FP16_ONE = 0x3C00           # 1.0
+FP16_2P15 = 0x7800          # 2^15
+
+
+def tree_witness_operands(K: int, groups_per_row: list[list[tuple[int, int]]], b: int = 1):
+    """Operands whose block partials are the leaf pattern [2^27, 1, -2^27, 1].
+
+    Every block of the shared activations holds q = 1 at its first element and
+    q = 64 at its second, with d_a = 1.  Row r of the weights places, for each
+    (p, h) in groups_per_row[r], the four leaves at blocks p, p+h, p+2h, p+3h
+    (p a multiple of 4h, so that the pattern spans one aligned subtree):
+      2^27  : w = +64 at the second element, d_w = 2^15  (isum = 4096)
+      1     : w = 1 at the first element,    d_w = 1     (isum = 1)
+      -2^27 : w = -64 at the second element, d_w = 2^15
+    Every other block of the row has w = 0 (a +0 leaf).
+
+    Returns q int8 [b, K], d_a fp32 [b, K/32], w int8 [R, K], d_w fp16 bits [R, K/32].
+    """
+    m = K // 32
+    R = len(groups_per_row)
+    q = np.zeros((b, K), np.int8)
+    q[:, 0::32] = 1
+    q[:, 1::32] = 64
+    d_a = np.ones((b, m), np.float32)
+    w = np.zeros((R, K), np.int8)
+    d_w = np.full((R, m), FP16_ONE, np.uint16)
+    for r, groups in enumerate(groups_per_row):
+        for p, h in groups:
+            assert p % (4 * h) == 0 and p + 3 * h < m, (p, h, m)
+            for j, kind in zip((p, p + h, p + 2 * h, p + 3 * h), ("big+", "one", "big-", "one")):
+                if kind == "one":
+                    w[r, 32 * j] = 1
+                else:
+                    w[r, 32 * j + 1] = 64 if kind == "big+" else -64
+                    d_w[r, j] = FP16_2P15
+    return q, d_a, w, d_w
+
+
+def negative_zero_operands(K: int, N: int = 4, b: int = 1):
+    """Operands whose every block partial is -0: all activation codes 0 and
+    d_a = -1, weights and d_w arbitrary (here 1).  The sum of -0 leaves is -0;
+    adding the +0 leaves of a zero-padded tree turns it into +0."""
+    m = K // 32
+    q = np.zeros((b, K), np.int8)
+    d_a = np.full((b, m), -1.0, np.float32)
+    w = np.ones((N, K), np.int8)
+    d_w = np.full((N, m), FP16_ONE, np.uint16)
+    return q, d_a, w, d_w
