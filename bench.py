@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark: W8A8 mat-vec weight GB/s on Qwen3-8B-shaped decode linears at b = 1..8.
+
+One step is a speculative-verify sweep over the four W8A8 decode layers of a
+Qwen3-8B-shaped transformer block (qkv 4096->6144, o 4096->4096, gate_up
+4096->24576, down 12288->4096) at every width b = 1..8: for each (b, layer)
+the bf16 activations are quantized per token (quantize_activations) and the
+int8 weights are streamed once (w8a8_linear).  The 32 (b, layer) passes use
+8 distinct copies of the weights (1.5 GB) so that no pass finds its weights
+in the 256 MB Infinity Cache.  Inputs are seeded synthetic data resident in
+HBM before timing; the step is replayed from a HIP graph.
+
+value = weight bytes streamed per step (int8 weights + fp32 scales) / step
+time, in GB/s.  The roofline object times the dominant kernel (the W8A8
+mat-vec) alone with HIP events on the stream it runs on.  The cpu_baseline
+object times the CPU oracle on the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--detail]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W8A8 matvec weight GB/s (% HBM peak) at b=1..8; batch-variant rows = 0"
+HBM_PEAK_GBS = 8000.0
+COPIES = 8
+B_LIST = list(range(1, 9))
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--detail", action="store_true", help="per-(layer, b) kernel timings")
+    p.add_argument("--prefill", action="store_true", help="also time the b=512 prefill pass")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import invariant_quantized_decode_token_amd as iqd
+    import workloads as W
+
+    iqd.load()  # fails loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs, resident in HBM ------------------------------------------
+    layers = [W.qwen3_8b_layer(i, tokens=8) for i in range(4)]
+    wsets, swsets = [], []
+    for L in layers:
+        w0 = torch.from_numpy(L.w).to(dev)
+        wsets.append([w0] + [w0.clone() for _ in range(COPIES - 1)])
+        swsets.append(torch.from_numpy(L.s_w).to(dev))
+    xs = [torch.from_numpy(L.x.view(np.int16)).view(torch.bfloat16).to(dev) for L in layers]
+    qs = [torch.empty((8, L.K), dtype=torch.int8, device=dev) for L in layers]
+    sas = [torch.empty((8,), dtype=torch.float32, device=dev) for L in layers]
+    ys = [torch.empty((8, L.N), dtype=torch.bfloat16, device=dev) for L in layers]
+
+    def layer_bytes(L):
+        return L.N * L.K + 4 * L.N
+
+    def algo_bytes(L, b):  # what one w8a8_linear call must move
+        return L.N * L.K + 4 * L.N + b * L.K + 4 * b + 2 * b * L.N
+
+    step_weight_bytes = sum(layer_bytes(L) for L in layers) * len(B_LIST)
+
+    def step(quantize=True):
+        for bi, b in enumerate(B_LIST):
+            c = bi % COPIES
+            for li, L in enumerate(layers):
+                if quantize:
+                    iqd.quantize_activations(xs[li][:b], q=qs[li][:b], scale=sas[li][:b])
+                iqd.w8a8_linear(qs[li][:b], sas[li][:b], wsets[li][c], swsets[li], y=ys[li][:b])
+
+    def capture(fn):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(g, reps):
+        st = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(reps):
+            g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps  # ms per replay
+
+    # ---- the step ------------------------------------------------------------
+    g_step = capture(step)
+    for _ in range(args.warmup):
+        g_step.replay()
+    torch.cuda.synchronize()
+    ms = time_graph(g_step, args.steps)
+    value = step_weight_bytes / (ms * 1e-3) / 1e9
+
+    # ---- dominant kernel alone: the W8A8 mat-vec launches of the step -----------
+    g_mv = capture(lambda: step(quantize=False))
+    for _ in range(3):
+        g_mv.replay()
+    ms_mv = time_graph(g_mv, args.steps)
+    n_launch = len(B_LIST) * len(layers)
+    mv_bytes = sum(algo_bytes(L, b) for b in B_LIST for L in layers)
+    avg_us = ms_mv * 1e3 / n_launch
+    achieved = mv_bytes / n_launch / (avg_us * 1e-6) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded int8 weights, log-uniform fp32 scales, N(0,1) bf16 activations with 1% x20 "
+                "outlier channels)",
+        "config": {
+            "workload": "Qwen3-8B-shaped W8A8 decode linears qkv 4096->6144, o 4096->4096, gate_up "
+                        "4096->24576, down 12288->4096; quantize + linear at every b=1..8",
+            "b": B_LIST,
+            "weight_copies": COPIES,
+            "weight_bytes_per_step": step_weight_bytes,
+            "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+            "tokens_per_s_equiv": round(sum(B_LIST) / (ms * 1e-3), 1),
+        },
+        "roofline": {
+            "kernel": "k_w8a8_matvec",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(avg_us, 3),
+            "launches_per_step": n_launch,
+        },
+        "cpu_baseline": None,
+    }
+
+    if args.detail:
+        det = []
+        for li, L in enumerate(layers):
+            for b in B_LIST:
+                def one(li=li, L=L, b=b):
+                    for c in range(COPIES):
+                        iqd.w8a8_linear(qs[li][:b], sas[li][:b], wsets[li][c], swsets[li], y=ys[li][:b])
+                g = capture(one)
+                g.replay()
+                us = time_graph(g, 20) * 1e3 / COPIES
+                det.append({"layer": L.name, "b": b, "us": round(us, 3),
+                            "weight_GBs": round(layer_bytes(L) / (us * 1e-6) / 1e9, 1)})
+        out["detail"] = det
+
+    if args.prefill:
+        pre = []
+        for li, L in enumerate(layers):
+            T = 512
+            Lp = W.qwen3_8b_layer(li, tokens=T)
+            xp = torch.from_numpy(Lp.x.view(np.int16)).view(torch.bfloat16).to(dev)
+            qp, sp = iqd.quantize_activations(xp)
+            yp = torch.empty((T, L.N), dtype=torch.bfloat16, device=dev)
+
+            def pf(li=li):
+                for c in range(COPIES):
+                    iqd.w8a8_linear(qp, sp, wsets[li][c], swsets[li], y=yp)
+            g = capture(pf)
+            g.replay()
+            us = time_graph(g, 5) * 1e3 / COPIES
+            tops = 2.0 * T * L.N * L.K / (us * 1e-6) / 1e12
+            pre.append({"layer": L.name, "b": T, "us": round(us, 2), "TOPS": round(tops, 1),
+                        "mfma_frac": round(tops / 5000.0, 4)})
+        out["prefill"] = pre
+
+    if not args.no_cpu:
+        import oracle
+
+        ncores = os.cpu_count() or 1
+        nthreads = min(ncores, 16)
+        hosts = [(oracle.quantize_token, L) for L in layers]
+        t0 = time.time()
+        passes = 0
+        while passes < 1 or time.time() - t0 < 10.0:
+            for b in B_LIST:
+                for L in layers:
+                    q, s = oracle.quantize_token(L.x[:b])
+                    oracle.w8a8(q, s, L.w, L.s_w, nthreads=nthreads)
+            passes += 1
+        dt = time.time() - t0
+        out["cpu_baseline"] = {
+            "value": round(step_weight_bytes * passes / dt / 1e9, 3),
+            "unit": "GB/s",
+            "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"{passes} full step(s): quantize + W8A8 linear for the 4 layers at b=1..8, "
+                      f"{dt:.1f} s wall",
+        }
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

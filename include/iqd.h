@@ -1,0 +1,197 @@
+/*
+ * iqd.h - batch-invariant int8 linear layer for decode and speculative-verify
+ * passes on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libiqd.so.  Every entry point enqueues work on the caller's HIP
+ * stream and returns at once; nothing is synchronised, nothing is allocated,
+ * no pointer is kept after return.  The caller owns every buffer.
+ *
+ * Common conventions
+ *  - Tensors are device-resident, row-major and contiguous: a [rows, cols]
+ *    tensor has cols contiguous.  bf16 and fp16 are IEEE bfloat16 / binary16
+ *    bit patterns in 16-bit words.
+ *  - Alignment: int8 tensors and bf16 inputs 16 bytes; fp32 / int32 tensors
+ *    4 bytes; bf16 / fp16 outputs and scales 2 bytes; workspace 16 bytes.
+ *    Violations return IQD_ERR_ALIGN.
+ *  - K (input features) must be a multiple of 16; 1 <= K <= IQD_K_MAX so that
+ *    an int32 sum of K products of int8 values cannot overflow
+ *    (128 * 128 * 131071 < 2^31).
+ *  - Arguments are validated before any launch: on error nothing is written.
+ *    Outputs must not overlap inputs (IQD_ERR_INVALID).  Inputs must be
+ *    finite; NaN or Inf inputs give unspecified (but memory-safe) results.
+ *  - A failed launch returns IQD_ERR_HIP.  Faults during execution surface
+ *    at the caller's next synchronisation of the stream.
+ *  - `stream` is a hipStream_t; NULL means the default stream.
+ *  - Calls are stateless and re-entrant; concurrent calls on different
+ *    streams are safe.
+ *
+ * The guarantee.  Every output element is a pure function of its token's
+ * row of the inputs, the weights and the scales, computed in one canonical
+ * order.  It does not depend on the number of tokens b in the call, on
+ * split_k, on the grid, on the stream or on occupancy, and it equals the
+ * plain CPU definition bit for bit.
+ *
+ * Sources (page title, then section / table / figure):
+ *  [P1] "why speculative decoding changed my output": the guarantee
+ *       speculative verification needs (a position's logits inside a batch
+ *       equal its logits decoded alone); int8 activations in blocks of 32
+ *       with float scales; per-block integer dot products scaled into fp32
+ *       ("the mat-vec kernel"); fp32 order sensitivity ("floats care about
+ *       order").
+ *  [P2] "My speculative decoder got slower": split-K changes float rounding
+ *       ("Two matmul schedules that survived"); a vocab head computing only
+ *       the winning token ("We're nowhere near SOL").
+ *  [P3] "Deterministic LLM Inference Across GPU Kernels: Power-of-Two INT8
+ *       Quantization Scales and the Limits of Tolerance-Based Conformance":
+ *       exact int32 accumulation (Abstract, Fig. 1); the epilogue faults of
+ *       Table II; power-of-two scales with re-rounded weights (Abstract).
+ */
+#ifndef IQD_H
+#define IQD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    IQD_OK = 0,
+    IQD_ERR_INVALID = -1,     /* bad shape, null pointer, aliasing, bad group */
+    IQD_ERR_ALIGN = -2,       /* pointer misaligned */
+    IQD_ERR_RANGE = -3,       /* K above IQD_K_MAX */
+    IQD_ERR_UNSUPPORTED = -4, /* split_k not allowed for this shape */
+    IQD_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+    IQD_ERR_HIP = -6          /* a HIP runtime call or launch failed */
+} iqd_status;
+
+/* Operation codes for iqd_workspace_bytes. */
+enum { IQD_OP_W8A8 = 1, IQD_OP_BLOCKQ8 = 2, IQD_OP_LM_HEAD = 3 };
+
+#define IQD_K_MAX 131071
+#define IQD_SPLIT_K_MAX 64
+
+/*
+ * quantize_activations - int8 activations with fp32 scales.
+ *
+ * [P1 "the mat-vec kernel"]: activations are int8 with a float scale, in
+ * blocks of 32 for block-quantized weights.  Per group of elements (a whole
+ * token row when group == 0, each aligned 32-element block when group == 32):
+ *     amax = max |x|                         (bf16 -> fp32 exact)
+ *     s    = fl(amax / 127)                  (correctly rounded division)
+ *     q    = clamp(rint_half_even(fl(x / s)), -127, 127)
+ * A group whose amax is 0 gets s = 0 and q = 0.
+ *
+ *   x_bf16  in   bf16 [b, K]
+ *   q       out  int8 [b, K]
+ *   scale   out  fp32 [b] (group 0) or [b, K/32] (group 32)
+ * Errors: IQD_ERR_INVALID for b < 1, K < 1, K % 16 (K % 32 for group 32),
+ * a group other than 0 or 32, or overlapping buffers.
+ */
+int quantize_activations(const void *x_bf16, int64_t b, int64_t K, int32_t group, int8_t *q,
+                         float *scale, void *stream);
+
+/*
+ * w8a8_linear - y = bf16( (fl32(sum_k q[t,k] * w[n,k]) * s_a[t]) * s_w[n] ).
+ *
+ * [P3 Abstract, Fig. 1]: the int32 sum is exact and order-free under the K
+ * bound, so any decomposition of K is allowed.  [P3 Table II]: the epilogue
+ * is the negation of faults F1-F5: fp32 scales, (acc * s_a) * s_w in that
+ * order with no rounding between, no fused multiply-add, one round to
+ * nearest even into bf16, applied once after the whole integer sum.
+ *
+ *   q      in  int8 [b, K]     s_a  in  fp32 [b]
+ *   w      in  int8 [N, K]     s_w  in  fp32 [N]
+ *   y_bf16 out bf16 [b, N]
+ *   split_k    1, or a power of two <= min(IQD_SPLIT_K_MAX, K/16): the K
+ *              range is cut into split_k int32 partial sums that a second
+ *              kernel adds (exactly) before the epilogue.  Needs workspace.
+ *   workspace  device scratch of iqd_workspace_bytes(IQD_OP_W8A8, ...) bytes
+ *              (NULL allowed when that is 0).
+ * b <= 16 streams the weights once through packed int8 dot products; larger
+ * b uses the int8 matrix-core path.  Both give identical bits.
+ * Errors: IQD_ERR_INVALID, IQD_ERR_ALIGN, IQD_ERR_RANGE, IQD_ERR_UNSUPPORTED
+ * (bad split_k), IQD_ERR_WORKSPACE, IQD_ERR_HIP.
+ */
+int w8a8_linear(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int64_t b,
+                int64_t N, int64_t K, void *y_bf16, int32_t split_k, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/*
+ * blockq8_linear - q8_0-style block-quantized linear.
+ *
+ * [P1 "the mat-vec kernel"]: per 32-element block j the integer dot product
+ * isum_j is exact; it is scaled into fp32 as the leaf
+ *     p_j = fl( fl( fl32(isum_j) * d_a[t,j] ) * fl32(d_w[n,j]) )
+ * and the m = K/32 leaves are summed by the canonical tree: pad with +0.0f
+ * leaves up to L = 2^ceil(log2 m), then add adjacent pairs in index order,
+ * level by level.  y = bf16(root), rounded to nearest even.  The tree is
+ * fixed, so the float order never depends on b, the grid or split_k
+ * ([P1 "the mat-vec kernel"]: the stock kernel's block grouping changed
+ * with the token count; [P2 "Two matmul schedules that survived"]: split-K
+ * changed the rounding).
+ *
+ *   q      in  int8 [b, K]       d_a       in  fp32 [b, K/32]
+ *   w      in  int8 [N, K]       d_w_fp16  in  fp16 [N, K/32]
+ *   y_bf16 out bf16 [b, N]
+ *   split_k    1, or a power of two with 32 * split_k <= L: split s owns the
+ *              aligned subtree of leaves [s*L/split_k, (s+1)*L/split_k); a
+ *              second kernel folds the top log2(split_k) tree levels.
+ * K must be a multiple of 32.
+ */
+int blockq8_linear(const int8_t *q, const float *d_a, const int8_t *w, const void *d_w_fp16,
+                   int64_t b, int64_t N, int64_t K, void *y_bf16, int32_t split_k, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/*
+ * lm_head_argmax - W8A8 vocab projection and the winning token per row.
+ *
+ * [P2 "We're nowhere near SOL"]: a vocab head that returns only the winning
+ * token.  logits are w8a8_linear's outputs; argmax[t] is the smallest n whose
+ * bf16 logit equals the row maximum, compared as real numbers (+0 == -0).
+ * The pages do not fix a tie rule ([P2 "Why the decoders disagreed?"] shows
+ * a real bf16 tie); the lowest index wins.
+ *
+ *   logits_bf16  out bf16 [b, N], or NULL to skip writing the logits
+ *   argmax       out int32 [b]
+ *   workspace    iqd_workspace_bytes(IQD_OP_LM_HEAD, b, N, K, 1) bytes
+ * Requires N <= 2^31 - 1.
+ */
+int lm_head_argmax(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int64_t b,
+                   int64_t N, int64_t K, void *logits_bf16, int32_t *argmax, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/*
+ * pow2_requantize - move each weight row to a power-of-two scale.
+ *
+ * [P3 Abstract]: requantizing every weight scale to its nearest power of two
+ * (re-rounding the weights, not only rewriting the scales) makes the scale
+ * multiply exact.  Per row n, with |s| = m * 2^E, m in [1, 2):
+ *     s'       = sign(s) * (m < 1.5 ? 2^E : 2^(E+1))
+ *     w'[n,k]  = clamp(rint_half_even(w[n,k] * s / s'), -127, 127)
+ * computed exactly (w * s has at most 32 significant bits; s' is a power of
+ * two).  s == 0 gives s' = 0 and w' = 0.  Offline weight preparation, not a
+ * per-token step.
+ *
+ *   w in int8 [N, K], s_w in fp32 [N]  ->  w_out int8 [N, K], s_out fp32 [N]
+ */
+int pow2_requantize(const int8_t *w, const float *s_w, int64_t N, int64_t K, int8_t *w_out,
+                    float *s_out, void *stream);
+
+/* Workspace bytes the op needs for these sizes (0 if none); 0 also for
+ * arguments the op would reject. */
+size_t iqd_workspace_bytes(int op, int64_t b, int64_t N, int64_t K, int32_t split_k);
+
+/* Static, human-readable name of a status code. */
+const char *iqd_status_str(int status);
+
+/* Name of the HIP error behind the calling thread's most recent IQD_ERR_HIP
+ * (static string; "hipSuccess" if there was none).  Diagnostics only. */
+const char *iqd_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IQD_H */

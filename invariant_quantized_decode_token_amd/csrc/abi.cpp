@@ -1,0 +1,291 @@
+// C ABI of libiqd: argument validation and dispatch to the gfx950 kernels.
+// Every check runs before any launch, so an error return leaves every
+// buffer untouched.  The library allocates nothing and never synchronises.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "../../include/iqd.h"
+#include "kernels.hpp"
+
+namespace iqd {
+
+const DeviceInfo &device_info() {
+    static DeviceInfo infos[64];
+    static bool filled[64] = {};
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!filled[dev]) {
+        int cus = 0, lds = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+            infos[dev].cus = cus;
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess &&
+            lds > 0)
+            infos[dev].max_lds = lds;
+        int ldsb = 0;
+        if (hipDeviceGetAttribute(&ldsb, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && ldsb > 0)
+            infos[dev].max_lds_block = ldsb;
+        filled[dev] = true;
+    }
+    return infos[dev];
+}
+
+}  // namespace iqd
+
+namespace {
+
+constexpr int64_t kMatvecMaxB = 16;
+constexpr int64_t kIntMax = 0x7FFFFFFF;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [p, p + n) and [r, r + m) share a byte.
+bool overlap(const void *p, size_t n, const void *r, size_t m) {
+    if (!p || !r || n == 0 || m == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + n;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(r), b1 = b0 + m;
+    return a0 < b1 && b0 < a1;
+}
+
+struct Buf {
+    const void *p;
+    size_t n;
+};
+
+// Outputs must not overlap each other or any input.
+bool any_overlap(std::initializer_list<Buf> outs, std::initializer_list<Buf> ins) {
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (auto i = ins.begin(); i != ins.end(); ++i)
+            if (overlap(o->p, o->n, i->p, i->n)) return true;
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlap(o->p, o->n, o2->p, o2->n)) return true;
+    }
+    return false;
+}
+
+bool is_pow2(int64_t v) { return v >= 1 && (v & (v - 1)) == 0; }
+
+int64_t pow2_ceil(int64_t v) {
+    int64_t L = 1;
+    while (L < v) L *= 2;
+    return L;
+}
+
+size_t round16(size_t v) { return (v + 15) / 16 * 16; }
+
+thread_local hipError_t g_last_hip = hipSuccess;
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return IQD_OK;
+    g_last_hip = e;
+    return IQD_ERR_HIP;
+}
+
+// A launch is checked with hipGetLastError, which also reports errors that an
+// earlier, unrelated runtime call of this thread left behind; clear those
+// first so that only our own launches are judged.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+int check_shape(int64_t b, int64_t N, int64_t K) {
+    if (b < 1 || N < 1 || K < 16 || K % 16 != 0) return IQD_ERR_INVALID;
+    if (b > kIntMax || N > kIntMax) return IQD_ERR_INVALID;
+    if (K > IQD_K_MAX) return IQD_ERR_RANGE;
+    return IQD_OK;
+}
+
+int w8a8_split_ok(int64_t b, int64_t K, int32_t split) {
+    if (split == 1) return IQD_OK;
+    if (b > kMatvecMaxB || !is_pow2(split) || split > IQD_SPLIT_K_MAX || split > K / 16) return IQD_ERR_UNSUPPORTED;
+    return IQD_OK;
+}
+
+int blockq8_split_ok(int64_t b, int64_t K, int32_t split) {
+    if (split == 1) return IQD_OK;
+    const int64_t L = pow2_ceil(K / 32);
+    if (b > kMatvecMaxB || !is_pow2(split) || split > IQD_SPLIT_K_MAX || 32 * static_cast<int64_t>(split) > L)
+        return IQD_ERR_UNSUPPORTED;
+    return IQD_OK;
+}
+
+size_t ws_w8a8(int64_t b, int64_t N, int32_t split) {
+    return split > 1 ? round16(static_cast<size_t>(split) * b * N * 4) : 0;
+}
+size_t ws_lm_head(int64_t b, int64_t N, bool have_logits) {
+    return have_logits ? 0 : round16(static_cast<size_t>(b) * N * 2);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *iqd_status_str(int status) {
+    switch (status) {
+        case IQD_OK: return "IQD_OK";
+        case IQD_ERR_INVALID: return "IQD_ERR_INVALID: bad shape, null pointer, aliasing or group";
+        case IQD_ERR_ALIGN: return "IQD_ERR_ALIGN: pointer misaligned";
+        case IQD_ERR_RANGE: return "IQD_ERR_RANGE: K above IQD_K_MAX (int32 accumulator bound)";
+        case IQD_ERR_UNSUPPORTED: return "IQD_ERR_UNSUPPORTED: split_k not allowed for this shape";
+        case IQD_ERR_WORKSPACE: return "IQD_ERR_WORKSPACE: workspace missing or too small";
+        case IQD_ERR_HIP: return "IQD_ERR_HIP: HIP runtime call or launch failed";
+        default: return "unknown iqd status";
+    }
+}
+
+const char *iqd_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
+
+size_t iqd_workspace_bytes(int op, int64_t b, int64_t N, int64_t K, int32_t split_k) {
+    if (check_shape(b, N, K) != IQD_OK) return 0;
+    switch (op) {
+        case IQD_OP_W8A8:
+            return w8a8_split_ok(b, K, split_k) == IQD_OK ? ws_w8a8(b, N, split_k) : 0;
+        case IQD_OP_BLOCKQ8:
+            if (K % 32 != 0 || blockq8_split_ok(b, K, split_k) != IQD_OK) return 0;
+            return split_k > 1 ? round16(static_cast<size_t>(split_k) * b * N * 4) : 0;
+        case IQD_OP_LM_HEAD:
+            return ws_lm_head(b, N, false);
+        default:
+            return 0;
+    }
+}
+
+int quantize_activations(const void *x_bf16, int64_t b, int64_t K, int32_t group, int8_t *q, float *scale,
+                         void *stream) {
+    if (!x_bf16 || !q || !scale) return IQD_ERR_INVALID;
+    if (b < 1 || K < 16 || K % 16 != 0 || b > kIntMax || K > kIntMax) return IQD_ERR_INVALID;
+    if (group != 0 && group != 32) return IQD_ERR_INVALID;
+    if (group == 32 && K % 32 != 0) return IQD_ERR_INVALID;
+    if (!aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(scale, 4)) return IQD_ERR_ALIGN;
+    const size_t ns = group == 0 ? static_cast<size_t>(b) : static_cast<size_t>(b) * (K / 32);
+    if (any_overlap({{q, static_cast<size_t>(b * K)}, {scale, ns * 4}}, {{x_bf16, static_cast<size_t>(b * K * 2)}}))
+        return IQD_ERR_INVALID;
+    clear_stale_error();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
+    if (group == 0) return hip_status(iqd::launch_quantize_token(x, static_cast<int>(b), static_cast<int>(K), q, scale, st));
+    return hip_status(iqd::launch_quantize_block32(x, static_cast<int>(b), static_cast<int>(K), q, scale, st));
+}
+
+int w8a8_linear(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int64_t b, int64_t N,
+                int64_t K, void *y_bf16, int32_t split_k, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!q || !s_a || !w || !s_w || !y_bf16) return IQD_ERR_INVALID;
+    int st = check_shape(b, N, K);
+    if (st != IQD_OK) return st;
+    st = w8a8_split_ok(b, K, split_k);
+    if (st != IQD_OK) return st;
+    if (!aligned(q, 16) || !aligned(w, 16) || !aligned(s_a, 4) || !aligned(s_w, 4) || !aligned(y_bf16, 2))
+        return IQD_ERR_ALIGN;
+    const size_t ws = ws_w8a8(b, N, split_k);
+    if (ws > 0) {
+        if (!workspace || workspace_bytes < ws) return IQD_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return IQD_ERR_ALIGN;
+    }
+    const size_t ybytes = static_cast<size_t>(b) * N * 2;
+    if (any_overlap({{y_bf16, ybytes}, {ws ? workspace : nullptr, ws}},
+                    {{q, static_cast<size_t>(b * K)}, {s_a, static_cast<size_t>(b) * 4},
+                     {w, static_cast<size_t>(N) * K}, {s_w, static_cast<size_t>(N) * 4}}))
+        return IQD_ERR_INVALID;
+    clear_stale_error();
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    uint16_t *y = static_cast<uint16_t *>(y_bf16);
+    const int bi = static_cast<int>(b), Ni = static_cast<int>(N), Ki = static_cast<int>(K);
+    if (b > kMatvecMaxB) return hip_status(iqd::launch_w8a8_mfma(q, s_a, w, s_w, bi, Ni, Ki, y, hs));
+    if (split_k == 1)
+        return hip_status(iqd::launch_w8a8_matvec(q, s_a, w, s_w, bi, Ni, Ki, y, 1, nullptr, hs));
+    int32_t *part = static_cast<int32_t *>(workspace);
+    hipError_t e = iqd::launch_w8a8_matvec(q, s_a, w, s_w, bi, Ni, Ki, nullptr, split_k, part, hs);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(iqd::launch_w8a8_combine(part, s_a, s_w, bi, Ni, split_k, y, hs));
+}
+
+int blockq8_linear(const int8_t *q, const float *d_a, const int8_t *w, const void *d_w_fp16, int64_t b, int64_t N,
+                   int64_t K, void *y_bf16, int32_t split_k, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    if (!q || !d_a || !w || !d_w_fp16 || !y_bf16) return IQD_ERR_INVALID;
+    int st = check_shape(b, N, K);
+    if (st != IQD_OK) return st;
+    if (K % 32 != 0) return IQD_ERR_INVALID;
+    st = blockq8_split_ok(b, K, split_k);
+    if (st != IQD_OK) return st;
+    if (!aligned(q, 16) || !aligned(w, 16) || !aligned(d_a, 4) || !aligned(d_w_fp16, 2) || !aligned(y_bf16, 2))
+        return IQD_ERR_ALIGN;
+    const size_t ws = split_k > 1 ? round16(static_cast<size_t>(split_k) * b * N * 4) : 0;
+    if (ws > 0) {
+        if (!workspace || workspace_bytes < ws) return IQD_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return IQD_ERR_ALIGN;
+    }
+    const size_t m = static_cast<size_t>(K / 32);
+    if (any_overlap({{y_bf16, static_cast<size_t>(b) * N * 2}, {ws ? workspace : nullptr, ws}},
+                    {{q, static_cast<size_t>(b * K)}, {d_a, static_cast<size_t>(b) * m * 4},
+                     {w, static_cast<size_t>(N) * K}, {d_w_fp16, static_cast<size_t>(N) * m * 2}}))
+        return IQD_ERR_INVALID;
+    clear_stale_error();
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    uint16_t *y = static_cast<uint16_t *>(y_bf16);
+    const uint16_t *dw = static_cast<const uint16_t *>(d_w_fp16);
+    const int Ni = static_cast<int>(N), Ki = static_cast<int>(K);
+    if (split_k == 1) {
+        // any b: chunks of at most 16 tokens (each token's row is independent of its chunk)
+        for (int64_t t0 = 0; t0 < b; t0 += kMatvecMaxB) {
+            const int bc = static_cast<int>(b - t0 < kMatvecMaxB ? b - t0 : kMatvecMaxB);
+            hipError_t e = iqd::launch_blockq8_matvec(q + t0 * K, d_a + t0 * m, w, dw, bc, Ni, Ki, y + t0 * N, 1,
+                                                      nullptr, hs);
+            if (e != hipSuccess) return hip_status(e);
+        }
+        return IQD_OK;
+    }
+    float *part = static_cast<float *>(workspace);
+    const int bi = static_cast<int>(b);
+    hipError_t e = iqd::launch_blockq8_matvec(q, d_a, w, dw, bi, Ni, Ki, nullptr, split_k, part, hs);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(iqd::launch_blockq8_combine(part, bi, Ni, split_k, y, hs));
+}
+
+int lm_head_argmax(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int64_t b, int64_t N,
+                   int64_t K, void *logits_bf16, int32_t *argmax, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    if (!q || !s_a || !w || !s_w || !argmax) return IQD_ERR_INVALID;
+    int st = check_shape(b, N, K);
+    if (st != IQD_OK) return st;
+    if (!aligned(q, 16) || !aligned(w, 16) || !aligned(s_a, 4) || !aligned(s_w, 4) || !aligned(argmax, 4) ||
+        (logits_bf16 && !aligned(logits_bf16, 2)))
+        return IQD_ERR_ALIGN;
+    const size_t ws = ws_lm_head(b, N, logits_bf16 != nullptr);
+    if (ws > 0) {
+        if (!workspace || workspace_bytes < ws) return IQD_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return IQD_ERR_ALIGN;
+    }
+    const size_t lbytes = static_cast<size_t>(b) * N * 2;
+    if (any_overlap({{logits_bf16, logits_bf16 ? lbytes : 0}, {ws ? workspace : nullptr, ws},
+                     {argmax, static_cast<size_t>(b) * 4}},
+                    {{q, static_cast<size_t>(b * K)}, {s_a, static_cast<size_t>(b) * 4},
+                     {w, static_cast<size_t>(N) * K}, {s_w, static_cast<size_t>(N) * 4}}))
+        return IQD_ERR_INVALID;
+    clear_stale_error();
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    uint16_t *logits = static_cast<uint16_t *>(logits_bf16 ? logits_bf16 : workspace);
+    const int Ni = static_cast<int>(N), Ki = static_cast<int>(K);
+    for (int64_t t0 = 0; t0 < b; t0 += kMatvecMaxB) {
+        const int bc = static_cast<int>(b - t0 < kMatvecMaxB ? b - t0 : kMatvecMaxB);
+        hipError_t e = iqd::launch_w8a8_matvec(q + t0 * K, s_a + t0, w, s_w, bc, Ni, Ki, logits + t0 * N, 1, nullptr,
+                                               hs);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return hip_status(iqd::launch_argmax_rows(logits, static_cast<int>(b), Ni, argmax, hs));
+}
+
+int pow2_requantize(const int8_t *w, const float *s_w, int64_t N, int64_t K, int8_t *w_out, float *s_out,
+                    void *stream) {
+    if (!w || !s_w || !w_out || !s_out) return IQD_ERR_INVALID;
+    if (N < 1 || K < 1 || N > kIntMax || K > kIntMax) return IQD_ERR_INVALID;
+    if (!aligned(s_w, 4) || !aligned(s_out, 4)) return IQD_ERR_ALIGN;
+    if (any_overlap({{w_out, static_cast<size_t>(N) * K}, {s_out, static_cast<size_t>(N) * 4}},
+                    {{w, static_cast<size_t>(N) * K}, {s_w, static_cast<size_t>(N) * 4}}))
+        return IQD_ERR_INVALID;
+    clear_stale_error();
+    return hip_status(iqd::launch_pow2_requant(w, s_w, static_cast<int>(N), static_cast<int>(K), w_out, s_out,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,262 @@
+// Block-quantized (q8_0-style) mat-vec, 1 <= b <= 16, gfx950.
+//
+// Per 32-element block j of a row:  isum_j = sum q*w (int32, exact) and the
+// leaf  p_j = fl( fl( fl32(isum_j) * d_a[t,j] ) * fl32(d_w[n,j]) ).
+// The m = K/32 leaves are summed by the canonical tree: zero-padded to
+// L = 2^ceil(log2 m) leaves, adjacent pairs added level by level, so the root
+// is the same for every b, grid, wave count and split.  y = bf16(root).
+//
+// Sources: "why speculative decoding changed my output", section "the mat-vec
+// kernel" (each block's exact integer result is scaled into fp32; the stock
+// kernel dealt blocks to warps by a token-count-dependent table, changing
+// the float order).  "My speculative decoder got slower", section "Two
+// matmul schedules that survived" (split-K moved the rounding points); here
+// every split owns an aligned subtree of the one fixed tree.
+//
+// Mapping (64-lane waves).  A "chunk" is 32 consecutive blocks (1 KiB of a
+// row).  Lane l reads the 16-byte half (l & 1) of block (l >> 1) of the chunk
+// with one coalesced 16-byte load per row, so a wave instruction covers the
+// chunk of one row.  The lane pairs (2i, 2i+1) add their int32 halves (the
+// first step of an integer reduce-scatter), the lanes form the fp32 leaves,
+// and fp32 reduce-scatter steps over lane masks 2, 4, 8, 16, 32 combine
+// adjacent blocks, then adjacent pairs of pairs, ... : exactly the tree
+// levels 1..5 over the chunk.  Chunk roots are combined with a binary carry
+// stack (the same tree, built left to right), the waves of a workgroup own
+// aligned sub-ranges of chunks and fold them in tree order, and API splits
+// own aligned subtrees folded by k_blockq8_combine.
+// Leaves of blocks in [m, L) are +0 (the canonical padding).  When L < 32
+// the chunk has lanes beyond the tree; their leaves are -0, the exact
+// identity of binary32 addition, so they do not disturb the root.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace iqd {
+namespace {
+
+constexpr int kBqWaves = 4;
+constexpr int kBqThreads = kBqWaves * kWave;
+constexpr int kMaxLevels = 8;  // chunk-slot tree depth: K <= 131071 -> at most 128 slots
+
+struct BqArgs {
+    const int8_t *q;
+    const float *d_a;
+    const int8_t *w;
+    const uint16_t *d_w;
+    int N, K, m, L;
+    uint16_t *y;
+    float *part;  // [split, B, N] subtree roots when split > 1
+    int split;
+    int nslots;  // max(1, L / 32) chunk slots in the whole tree
+    int ks;      // waves sharing a row group (aligned sub-ranges of slots)
+    int nsteps;
+};
+
+// Insert the root of slot i (0-based within an aligned power-of-two range)
+// into a binary carry stack; returns the value the insertion ends with,
+// which after the last slot of the range is the root of the whole range.
+__device__ __forceinline__ float carry_insert(float (&stk)[kMaxLevels], int i, float v) {
+    bool open = true;
+#pragma unroll
+    for (int l = 0; l < kMaxLevels; ++l) {
+        if (open) {
+            if ((i >> l) & 1) {
+                v = stk[l] + v;  // left subtree + right subtree
+            } else {
+                stk[l] = v;
+                open = false;
+            }
+        }
+    }
+    return v;
+}
+
+struct AddI {
+    __device__ int32_t operator()(int32_t a, int32_t b) const { return a + b; }
+};
+struct AddF {
+    __device__ float operator()(float a, float b) const { return a + b; }
+};
+
+template <int B, int RS>
+__global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
+    __shared__ float red[kBqWaves][kWave];
+    const int lane = lane_id();
+    const int wave = static_cast<int>(threadIdx.x) / kWave;
+    const int s = blockIdx.y;
+    const int K = a.K, N = a.N, m = a.m, L = a.L;
+    const int ks = a.ks;
+    const int rg = wave / ks;
+    const int kp = wave - rg * ks;
+    const int rgs = kBqWaves / ks;
+    const int nss = a.nslots / a.split;  // slots per split
+    const int nsw = nss / ks;            // slots per wave
+    const int slot0 = s * nss + kp * nsw;
+    const int half = lane & 1;
+
+    constexpr int NV = RS * B;
+    constexpr int NP = pow2_ceil(NV);
+    constexpr int NPH = NP >= 2 ? NP / 2 : 1;
+
+    for (int step = blockIdx.x; step < a.nsteps; step += gridDim.x) {
+        const int row0 = (step * rgs + rg) * RS;
+        int rows[RS];
+#pragma unroll
+        for (int r = 0; r < RS; ++r) rows[r] = min(row0 + r, N - 1);
+        float stk[kMaxLevels];
+#pragma unroll
+        for (int l = 0; l < kMaxLevels; ++l) stk[l] = 0.0f;
+        float root = 0.0f;
+        for (int i = 0; i < nsw; ++i) {
+            const int slot = slot0 + i;
+            const int j = slot * 32 + (lane >> 1);  // this lane's block
+            float cr;
+            if (slot * 32 < m) {
+                const bool live = j < m;
+                const int64_t kb = static_cast<int64_t>(j) * 32 + 16 * half;
+                int32_t isum[NP];
+#pragma unroll
+                for (int v = 0; v < NP; ++v) isum[v] = 0;
+                v4i wv[RS];
+#pragma unroll
+                for (int r = 0; r < RS; ++r)
+                    wv[r] = live ? load_stream16(a.w + static_cast<int64_t>(rows[r]) * K + kb)
+                                 : zero16();
+                float dwv[RS];
+#pragma unroll
+                for (int r = 0; r < RS; ++r)
+                    dwv[r] = live ? fp16_to_f32(a.d_w[static_cast<int64_t>(rows[r]) * m + j]) : 0.0f;
+                float dav[B];
+#pragma unroll
+                for (int t = 0; t < B; ++t) {
+                    const v4i av = live ? load16(a.q + static_cast<int64_t>(t) * K + kb) : zero16();
+                    dav[t] = live ? a.d_a[static_cast<int64_t>(t) * m + j] : 0.0f;
+#pragma unroll
+                    for (int r = 0; r < RS; ++r) isum[r * B + t] = dot16(wv[r], av, isum[r * B + t]);
+                }
+                // tree level 0 -> block sums: integer reduce-scatter over the lane pair
+                float leaf[NPH];
+                if constexpr (NP >= 2) {
+                    rs_step<1, NP>(isum, lane, AddI());
+#pragma unroll
+                    for (int v = 0; v < NPH; ++v) {
+                        const int vlo = v, vhi = v + NPH;
+                        const float da_lo = vlo < NV ? dav[vlo % B] : 0.0f;
+                        const float dw_lo = vlo < NV ? dwv[vlo / B] : 0.0f;
+                        const float da_hi = vhi < NV ? dav[vhi % B] : 0.0f;
+                        const float dw_hi = vhi < NV ? dwv[vhi / B] : 0.0f;
+                        const float da = sel(half != 0, da_hi, da_lo);
+                        const float dw = sel(half != 0, dw_hi, dw_lo);
+                        const float p = (static_cast<float>(isum[v]) * da) * dw;
+                        leaf[v] = live ? p : (j < L ? 0.0f : -0.0f);
+                    }
+                } else {
+                    const int32_t tot = isum[0] + xor_lane<1>(isum[0]);
+                    const float p = (static_cast<float>(tot) * dav[0]) * dwv[0];
+                    leaf[0] = live ? p : (j < L ? 0.0f : -0.0f);
+                }
+                // tree levels 1..5 inside the chunk: lane masks 2..32
+                cr = rs_chain<2, NPH>(leaf, lane, AddF());
+            } else {
+                cr = 0.0f;  // a slot made only of padding leaves
+            }
+            root = carry_insert(stk, i, cr);
+        }
+        if (ks > 1) {
+            red[wave][lane] = root;
+            __syncthreads();
+            if (kp == 0) {
+                if (ks == 2) {
+                    root = root + red[wave + 1][lane];
+                } else {  // ks == 4
+                    root = (root + red[wave + 1][lane]) + (red[wave + 2][lane] + red[wave + 3][lane]);
+                }
+            }
+        }
+        const int idx = reduce_scatter_index<NP>(lane);
+        if (kp == 0 && lane < NP && idx < NV) {
+            const int r = idx / B;
+            const int t = idx - r * B;
+            const int row = row0 + r;
+            if (row < N) {
+                if (a.split == 1)
+                    a.y[static_cast<int64_t>(t) * N + row] = bf16_rne(root);
+                else
+                    a.part[(static_cast<int64_t>(s) * B + t) * N + row] = root;
+            }
+        }
+        if (ks > 1) __syncthreads();
+    }
+}
+
+// Top log2(split) tree levels over the split roots, then bf16.
+__global__ __launch_bounds__(256) void k_blockq8_combine(const float *__restrict__ part, int b, int N,
+                                                         int split, uint16_t *__restrict__ y) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t total = static_cast<int64_t>(b) * N;
+    if (i >= total) return;
+    float stk[kMaxLevels];
+#pragma unroll
+    for (int l = 0; l < kMaxLevels; ++l) stk[l] = 0.0f;
+    float root = 0.0f;
+    for (int s = 0; s < split; ++s) root = carry_insert(stk, s, part[static_cast<int64_t>(s) * total + i]);
+    y[i] = bf16_rne(root);
+}
+
+template <int B>
+hipError_t launch_b(const BqArgs &base, hipStream_t st) {
+    constexpr int RS = B <= 8 ? 2 : 1;
+    BqArgs a = base;
+    const int row_groups = (a.N + RS - 1) / RS;
+    const int target = device_info().cus * 16;
+    const int nss = a.nslots / a.split;
+    int ks = 1;
+    while (ks < kBqWaves && ks * 2 <= nss && static_cast<int64_t>(row_groups) * ks * a.split < target) ks *= 2;
+    a.ks = ks;
+    const int rows_per_step = (kBqWaves / ks) * RS;
+    a.nsteps = (a.N + rows_per_step - 1) / rows_per_step;
+    int grid = device_info().cus * 8;
+    if (grid > a.nsteps) grid = a.nsteps;
+    hipLaunchKernelGGL((k_blockq8_matvec<B, RS>), dim3(grid, a.split), dim3(kBqThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_blockq8_matvec(const int8_t *q, const float *d_a, const int8_t *w,
+                                 const uint16_t *d_w, int b, int N, int K, uint16_t *y, int split,
+                                 float *part, hipStream_t st) {
+    const int m = K / 32;
+    int L = 1;
+    while (L < m) L *= 2;
+    const int nslots = L >= 32 ? L / 32 : 1;
+    BqArgs a{q, d_a, w, d_w, N, K, m, L, y, part, split, nslots, 1, 0};
+    switch (b) {
+        case 1: return launch_b<1>(a, st);
+        case 2: return launch_b<2>(a, st);
+        case 3: return launch_b<3>(a, st);
+        case 4: return launch_b<4>(a, st);
+        case 5: return launch_b<5>(a, st);
+        case 6: return launch_b<6>(a, st);
+        case 7: return launch_b<7>(a, st);
+        case 8: return launch_b<8>(a, st);
+        case 9: return launch_b<9>(a, st);
+        case 10: return launch_b<10>(a, st);
+        case 11: return launch_b<11>(a, st);
+        case 12: return launch_b<12>(a, st);
+        case 13: return launch_b<13>(a, st);
+        case 14: return launch_b<14>(a, st);
+        case 15: return launch_b<15>(a, st);
+        case 16: return launch_b<16>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_blockq8_combine(const float *part, int b, int N, int split, uint16_t *y,
+                                  hipStream_t st) {
+    const int64_t total = static_cast<int64_t>(b) * N;
+    const unsigned grid = static_cast<unsigned>((total + 255) / 256);
+    hipLaunchKernelGGL(k_blockq8_combine, dim3(grid), dim3(256), 0, st, part, b, N, split, y);
+    return hipGetLastError();
+}
+
+}  // namespace iqd

@@ -1,0 +1,48 @@
+// Host-side launchers of the gfx950 kernels (internal to libiqd).  Each
+// launcher assumes its arguments were validated by the C ABI layer and
+// returns the HIP error of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace iqd {
+
+struct DeviceInfo {
+    int cus = 256;
+    int max_lds = 160 * 1024;       // LDS per CU
+    int max_lds_block = 64 * 1024;  // LDS one workgroup may allocate
+};
+const DeviceInfo &device_info();
+
+hipError_t launch_quantize_token(const uint16_t *x, int b, int K, int8_t *q, float *s, hipStream_t st);
+hipError_t launch_quantize_block32(const uint16_t *x, int b, int K, int8_t *q, float *d, hipStream_t st);
+
+// W8A8 mat-vec, 1 <= b <= 16.  With split > 1, writes int32 partial sums
+// part[s, b, N] instead of y and needs launch_w8a8_combine afterwards.
+hipError_t launch_w8a8_matvec(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w,
+                              int b, int N, int K, uint16_t *y, int split, int32_t *part,
+                              hipStream_t st);
+hipError_t launch_w8a8_combine(const int32_t *part, const float *s_a, const float *s_w, int b, int N,
+                               int split, uint16_t *y, hipStream_t st);
+
+// W8A8 int8 matrix-core GEMM for b > 16 (prefill), same epilogue.
+hipError_t launch_w8a8_mfma(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w,
+                            int b, int N, int K, uint16_t *y, hipStream_t st);
+
+// Block-quantized mat-vec, 1 <= b <= 16.  With split > 1, writes fp32 subtree
+// roots part[s, b, N] and needs launch_blockq8_combine afterwards.
+hipError_t launch_blockq8_matvec(const int8_t *q, const float *d_a, const int8_t *w,
+                                 const uint16_t *d_w, int b, int N, int K, uint16_t *y, int split,
+                                 float *part, hipStream_t st);
+hipError_t launch_blockq8_combine(const float *part, int b, int N, int split, uint16_t *y,
+                                  hipStream_t st);
+
+// Argmax over bf16 logits [b, N]: smallest index of the row maximum.
+hipError_t launch_argmax_rows(const uint16_t *logits, int b, int N, int32_t *out, hipStream_t st);
+
+hipError_t launch_pow2_requant(const int8_t *w, const float *s, int N, int K, int8_t *w_out,
+                               float *s_out, hipStream_t st);
+
+}  // namespace iqd

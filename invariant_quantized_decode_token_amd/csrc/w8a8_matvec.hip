@@ -1,0 +1,104 @@
+// W8A8 mat-vec for decode and speculative verify (1 <= b <= 16), gfx950.
+//
+//   y[t, n] = bf16( fl( fl( fl32(acc[t, n]) * s_a[t] ) * s_w[n] ) ),
+//   acc[t, n] = sum_k q[t, k] * w[n, k]   (int32, exact)
+//
+// Sources: "Deterministic LLM Inference Across GPU Kernels: Power-of-Two INT8
+// Quantization Scales and the Limits of Tolerance-Based Conformance"
+// (Abstract, Fig. 1: exact, order-free int32 accumulation under a
+// no-overflow bound; Table II: the epilogue is the negation of faults
+// F1-F5).  "why speculative decoding changed my output", section "the mat-vec
+// kernel": the integer dot products are exact, the float order is what a
+// token-count-dependent launch geometry breaks.
+//
+// Because the K reduction is exact integer arithmetic, the decomposition of
+// K over lanes, waves and workgroups is chosen for speed alone (and may
+// depend on b); the epilogue runs once per output on the fully reduced
+// int32, so no result depends on b or on the launch shape.
+//
+// Mapping (64-lane waves):
+//  * a wave owns RS consecutive weight rows and a contiguous range of 16-byte
+//    K vectors; lane l reads vector v0 + l + 64 i of each row with a 16-byte
+//    non-temporal load (1 KiB contiguous per row per wave instruction);
+//  * the wave walks its work as a flat sequence of chunks (U vectors per lane
+//    per row) and keeps the next chunk's weights in flight while it computes
+//    the current one (a ring of D register buffers, D - 1 chunks in flight);
+//  * each 16-byte weight vector meets the same K vector of all B tokens
+//    (staged once per workgroup in LDS when they fit) through four
+//    v_dot4_i32_i8 per token, tokens in the outer loop so that only one
+//    activation vector per chunk step is live;
+//  * RS*B int32 accumulators per lane are reduce-scattered across the wave,
+//    then the `ks` waves that split the same rows along K add their partials
+//    through LDS; the owning lane applies the epilogue;
+//  * workgroups are persistent over row groups.
+#include "device.hpp"
+#include "kernels.hpp"
+#include "w8a8_matvec_impl.hpp"
+
+namespace iqd {
+namespace {
+
+// Launch configuration per token count (chosen by measurement on MI355X; the
+// numerics are identical for every entry).
+struct MvConfig {
+    int rs, u, nw, d;
+};
+
+template <int B>
+constexpr MvConfig mv_config() {
+    if constexpr (B <= 8) return {2, 1, 4, 4};
+    else return {2, 1, 4, 4};
+}
+
+template <int B>
+hipError_t launch_b(const MvArgs &base, hipStream_t st) {
+    constexpr MvConfig c = mv_config<B>();
+    return mv_launch<B, c.rs, c.u, c.nw, c.d>(base, st, device_info().cus, device_info().max_lds_block, /*ks=*/0, /*lds=*/-1,
+                                         /*grid=*/0);
+}
+
+}  // namespace
+
+hipError_t launch_w8a8_matvec(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w,
+                              int b, int N, int K, uint16_t *y, int split, int32_t *part,
+                              hipStream_t st) {
+    MvArgs a{};
+    a.q = q;
+    a.s_a = s_a;
+    a.w = w;
+    a.s_w = s_w;
+    a.N = N;
+    a.K = K;
+    a.y = y;
+    a.part = part;
+    a.split = split;
+    switch (b) {
+        case 1: return launch_b<1>(a, st);
+        case 2: return launch_b<2>(a, st);
+        case 3: return launch_b<3>(a, st);
+        case 4: return launch_b<4>(a, st);
+        case 5: return launch_b<5>(a, st);
+        case 6: return launch_b<6>(a, st);
+        case 7: return launch_b<7>(a, st);
+        case 8: return launch_b<8>(a, st);
+        case 9: return launch_b<9>(a, st);
+        case 10: return launch_b<10>(a, st);
+        case 11: return launch_b<11>(a, st);
+        case 12: return launch_b<12>(a, st);
+        case 13: return launch_b<13>(a, st);
+        case 14: return launch_b<14>(a, st);
+        case 15: return launch_b<15>(a, st);
+        case 16: return launch_b<16>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_w8a8_combine(const int32_t *part, const float *s_a, const float *s_w, int b, int N,
+                               int split, uint16_t *y, hipStream_t st) {
+    const int64_t total = static_cast<int64_t>(b) * N;
+    const unsigned grid = static_cast<unsigned>((total + 255) / 256);
+    hipLaunchKernelGGL(k_w8a8_combine, dim3(grid), dim3(256), 0, st, part, s_a, s_w, b, N, split, y);
+    return hipGetLastError();
+}
+
+}  // namespace iqd

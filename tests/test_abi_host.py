@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/iqd.h declares, and rejects bad arguments before any
+launch.  Fake, never-dereferenced pointers are used: every call below must
+return from validation."""
+import ctypes
+
+import pytest
+
+import invariant_quantized_decode_token_amd as iqd
+from invariant_quantized_decode_token_amd import _lib as L
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return iqd.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = iqd.header_functions()
+    assert set(names) == {"quantize_activations", "w8a8_linear", "blockq8_linear", "lm_head_argmax",
+                          "pow2_requantize", "iqd_workspace_bytes", "iqd_status_str", "iqd_last_hip_error"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(-6, 1):
+        s = iqd.status_str(code)
+        assert s.startswith("IQD_")
+    assert "unknown" in iqd.status_str(42)
+
+
+def test_workspace_bytes():
+    assert iqd.workspace_bytes(L.IQD_OP_W8A8, 8, 4096, 4096, 1) == 0
+    assert iqd.workspace_bytes(L.IQD_OP_W8A8, 8, 4096, 4096, 4) == 4 * 8 * 4096 * 4
+    assert iqd.workspace_bytes(L.IQD_OP_W8A8, 8, 4096, 4096, 3) == 0       # rejected split
+    assert iqd.workspace_bytes(L.IQD_OP_W8A8, 8, 4096, 131072, 1) == 0     # rejected K
+    assert iqd.workspace_bytes(L.IQD_OP_BLOCKQ8, 16, 4096, 12288, 16) == 16 * 16 * 4096 * 4
+    assert iqd.workspace_bytes(L.IQD_OP_BLOCKQ8, 16, 4096, 4096, 8) == 0   # 32*8 > L=128
+    assert iqd.workspace_bytes(L.IQD_OP_LM_HEAD, 5, 151936, 4096, 1) == (5 * 151936 * 2 + 15) // 16 * 16
+
+
+A = 1 << 20  # fake, 16-byte aligned, never dereferenced
+
+
+def ptr(v):
+    return ctypes.c_void_p(v)
+
+
+def w8a8(lib, b=4, N=64, K=256, split=1, q=A, sa=2 * A, w=3 * A, sw=4 * A, y=5 * A, ws=0, wsb=0):
+    return lib.w8a8_linear(ptr(q), ptr(sa), ptr(w), ptr(sw), b, N, K, ptr(y), split, ptr(ws), wsb, None)
+
+
+def test_w8a8_validation(lib):
+    assert w8a8(lib, q=0) == L.IQD_ERR_INVALID
+    assert w8a8(lib, b=0) == L.IQD_ERR_INVALID
+    assert w8a8(lib, N=0) == L.IQD_ERR_INVALID
+    assert w8a8(lib, K=0) == L.IQD_ERR_INVALID
+    assert w8a8(lib, K=40) == L.IQD_ERR_INVALID              # K % 16
+    assert w8a8(lib, K=131072) == L.IQD_ERR_RANGE
+    assert w8a8(lib, split=3) == L.IQD_ERR_UNSUPPORTED
+    assert w8a8(lib, split=128) == L.IQD_ERR_UNSUPPORTED
+    assert w8a8(lib, K=32, split=4) == L.IQD_ERR_UNSUPPORTED  # more splits than 16-byte vectors
+    assert w8a8(lib, b=17, split=2) == L.IQD_ERR_UNSUPPORTED
+    assert w8a8(lib, q=A + 8) == L.IQD_ERR_ALIGN
+    assert w8a8(lib, w=3 * A + 4) == L.IQD_ERR_ALIGN
+    assert w8a8(lib, sa=2 * A + 2) == L.IQD_ERR_ALIGN
+    assert w8a8(lib, y=5 * A + 1) == L.IQD_ERR_ALIGN
+    assert w8a8(lib, split=2) == L.IQD_ERR_WORKSPACE
+    assert w8a8(lib, split=2, ws=6 * A, wsb=100) == L.IQD_ERR_WORKSPACE
+    assert w8a8(lib, split=2, ws=6 * A + 4, wsb=1 << 20) == L.IQD_ERR_ALIGN
+    assert w8a8(lib, y=A + 64) == L.IQD_ERR_INVALID          # output overlaps q
+    assert w8a8(lib, y=3 * A + 100) == L.IQD_ERR_INVALID     # output overlaps w
+    assert w8a8(lib, split=2, ws=5 * A, wsb=1 << 20) == L.IQD_ERR_INVALID  # workspace overlaps y
+
+
+def test_blockq8_validation(lib):
+    def call(b=4, N=64, K=1024, split=1, dw=4 * A, ws=0, wsb=0):
+        return lib.blockq8_linear(ptr(A), ptr(2 * A), ptr(3 * A), ptr(dw), b, N, K, ptr(5 * A), split, ptr(ws), wsb,
+                                  None)
+    assert call(K=48) == L.IQD_ERR_INVALID                   # K % 32
+    assert call(K=131072 + 32) == L.IQD_ERR_RANGE
+    assert call(split=2) == L.IQD_ERR_UNSUPPORTED            # L = 32 leaves -> one split only
+    assert call(K=4096, split=8) == L.IQD_ERR_UNSUPPORTED    # 32 * 8 > 128
+    assert call(K=4096, split=4) == L.IQD_ERR_WORKSPACE
+    assert call(dw=4 * A + 1) == L.IQD_ERR_ALIGN
+
+
+def test_quantize_validation(lib):
+    def call(b=2, K=64, group=0, x=A, q=2 * A, s=3 * A):
+        return lib.quantize_activations(ptr(x), b, K, group, ptr(q), ptr(s), None)
+    assert call(group=16) == L.IQD_ERR_INVALID
+    assert call(K=48, group=32) == L.IQD_ERR_INVALID
+    assert call(K=40) == L.IQD_ERR_INVALID
+    assert call(b=0) == L.IQD_ERR_INVALID
+    assert call(x=A + 2) == L.IQD_ERR_ALIGN
+    assert call(s=3 * A + 2) == L.IQD_ERR_ALIGN
+    assert call(q=A + 16) == L.IQD_ERR_INVALID               # q overlaps x
+
+
+def test_lm_head_and_requant_validation(lib):
+    def call(logits=6 * A, argmax=7 * A, ws=0, wsb=0, N=1000):
+        return lib.lm_head_argmax(ptr(A), ptr(2 * A), ptr(3 * A), ptr(4 * A), 4, N, 256, ptr(logits), ptr(argmax),
+                                  ptr(ws), wsb, None)
+    assert call(argmax=0) == L.IQD_ERR_INVALID
+    assert call(logits=0) == L.IQD_ERR_WORKSPACE             # no logits buffer -> workspace needed
+    assert call(argmax=7 * A + 2) == L.IQD_ERR_ALIGN
+    assert lib.pow2_requantize(ptr(A), ptr(2 * A), 0, 16, ptr(3 * A), ptr(4 * A), None) == L.IQD_ERR_INVALID
+    assert lib.pow2_requantize(ptr(A), ptr(2 * A), 4, 16, ptr(A + 8), ptr(4 * A), None) == L.IQD_ERR_INVALID
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros((2, 64), dtype=torch.int8)
+    with pytest.raises(ValueError, match="GPU"):
+        iqd.w8a8_linear(q, torch.zeros(2), torch.zeros((8, 64), dtype=torch.int8), torch.zeros(8))

@@ -1,0 +1,194 @@
+"""GPU parity of activation quantization and the W8A8 linear (tolerance 0 ulp).
+
+Every GPU result is compared bit for bit with the CPU oracle on the same
+seeded inputs, and every token row at b > 1 with the same token at b = 1
+(batch invariance, the property speculative verification needs)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import assert_bits_equal, dev, host, host_bits, sample_rows, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def iqd():
+    import invariant_quantized_decode_token_amd as m
+
+    m.load()
+    return m
+
+
+def gpu_quant(iqd, x_bits):
+    q, s = iqd.quantize_activations(dev(x_bits))
+    return q, s
+
+
+# ----------------------------------------------------------------------------
+# quantization
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(5, 512), (3, 16), (2, 48), (4, 4112), (7, 12288), (1, 131056)])
+def test_quantize_token_parity(iqd, shape):
+    b, K = shape
+    x = W.normal_bf16(W.rng(K + b), b, K)
+    x[0, :] = 0  # an all-zero token: s = 0, q = 0
+    if b > 2:
+        x[1, :7] = W.f32_to_bf16_bits(np.array([1e30, -1e30, 1e-30, 3.0, -3.0, 0.0, 65504.0], np.float32))
+    oq, os_ = oracle.quantize_token(x)
+    q, s = gpu_quant(iqd, x)
+    torch().cuda.synchronize()
+    assert_bits_equal(host(q), oq, "q")
+    assert_bits_equal(host(s).view(np.uint32), os_.view(np.uint32), "s_a")
+
+
+def test_quantize_token_qwen3_activations(iqd):
+    for i in range(4):
+        L = W.qwen3_8b_layer(i, tokens=512)
+        oq, os_ = oracle.quantize_token(L.x)
+        q, s = gpu_quant(iqd, L.x)
+        assert_bits_equal(host(q), oq, f"q {L.name}")
+        assert_bits_equal(host(s).view(np.uint32), os_.view(np.uint32), f"s_a {L.name}")
+
+
+@pytest.mark.parametrize("shape", [(1, 32), (3, 96), (16, 4096), (16, 12288), (5, 4128)])
+def test_quantize_block32_parity(iqd, shape):
+    b, K = shape
+    x = W.normal_bf16(W.rng(7 * K + b), b, K)
+    x[0, :32] = 0  # a zero block
+    oq, od = oracle.quantize_block32(x)
+    q, d = iqd.quantize_activations(dev(x), group=32)
+    assert_bits_equal(host(q), oq, "q")
+    assert_bits_equal(host(d).view(np.uint32), od.view(np.uint32), "d_a")
+
+
+# ----------------------------------------------------------------------------
+# tiny config: K=512 -> N=256, 5 tokens, b = 1..5
+# ----------------------------------------------------------------------------
+
+def test_tiny_config_all_b(iqd):
+    L = W.tiny_layer()
+    oq, osa = oracle.quantize_token(L.x)
+    oy = oracle.w8a8(oq, osa, L.w, L.s_w)
+    q, sa = gpu_quant(iqd, L.x)
+    w, sw = dev(L.w), dev(L.s_w)
+    for b in range(1, 6):
+        for t0 in range(0, 5, b):
+            t1 = min(5, t0 + b)
+            y = iqd.w8a8_linear(q[t0:t1], sa[t0:t1], w, sw)
+            assert_bits_equal(host_bits(y), oy[t0:t1], f"tiny b={b} t0={t0}")
+        # the first b tokens as one pass
+        y = iqd.w8a8_linear(q[:b], sa[:b], w, sw)
+        assert_bits_equal(host_bits(y), oy[:b], f"tiny X[0:{b}]")
+
+
+# ----------------------------------------------------------------------------
+# ragged shapes, every b up to 16 and the b > 16 path, full oracle comparison
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(1, 16), (7, 48), (33, 1040), (130, 4112), (300, 12304), (67, 2064)])
+def test_ragged_shapes_full_oracle(iqd, N, K):
+    g = W.rng(N * 7919 + K)
+    w = W.int8_weights(g, N, K)
+    w[0, :16] = -128  # the ABI accepts -128
+    s_w = W.log_uniform_scales(g, N)
+    x = W.normal_bf16(g, 40, K)
+    oq, osa = oracle.quantize_token(x)
+    q, sa = gpu_quant(iqd, x)
+    wd, swd = dev(w), dev(s_w)
+    for b in list(range(1, 17)) + [17, 40]:
+        oy = oracle.w8a8(oq[:b], osa[:b], w, s_w)
+        y = iqd.w8a8_linear(q[:b], sa[:b], wd, swd)
+        assert_bits_equal(host_bits(y), oy, f"N={N} K={K} b={b}")
+
+
+def test_max_k_and_extreme_codes(iqd):
+    """K = 131056 (the largest multiple of 16 under the bound) with every
+    product at (-128)*(-128): acc = 2147287040, close to 2^31."""
+    K, N, b = 131056, 4, 3
+    q = np.full((b, K), -128, np.int8)
+    q[1] = 127
+    q[2, ::2] = 0
+    w = np.full((N, K), -128, np.int8)
+    w[1] = 127
+    s_a = np.array([1e-9, 2.5e-3, 1.0], np.float32)
+    s_w = np.array([1e-3, 3e-2, 0.5, 1e-5], np.float32)
+    oy = oracle.w8a8(q, s_a, w, s_w)
+    y = iqd.w8a8_linear(dev(q), dev(s_a), dev(w), dev(s_w))
+    assert_bits_equal(host_bits(y), oy, "max K")
+    for split in (2, 4, 64):
+        y = iqd.w8a8_linear(dev(q), dev(s_a), dev(w), dev(s_w), split_k=split)
+        assert_bits_equal(host_bits(y), oy, f"max K split {split}")
+
+
+def test_split_k_matches_oracle(iqd):
+    g = W.rng(99)
+    N, K = 200, 4096
+    w = W.int8_weights(g, N, K)
+    s_w = W.log_uniform_scales(g, N)
+    x = W.normal_bf16(g, 16, K)
+    oq, osa = oracle.quantize_token(x)
+    q, sa = gpu_quant(iqd, x)
+    for b in (1, 3, 8, 16):
+        oy = oracle.w8a8(oq[:b], osa[:b], w, s_w)
+        for split in (1, 2, 4, 8, 16, 64):
+            y = iqd.w8a8_linear(q[:b], sa[:b], dev(w), dev(s_w), split_k=split)
+            assert_bits_equal(host_bits(y), oy, f"b={b} split={split}")
+
+
+def test_errors_write_nothing(iqd):
+    t = torch()
+    g = W.rng(5)
+    N, K = 64, 256
+    q = dev(W.int8_weights(g, 4, K))
+    sa = dev(W.log_uniform_scales(g, 4))
+    w = dev(W.int8_weights(g, N, K))
+    sw = dev(W.log_uniform_scales(g, N))
+    y = t.full((4, N), 7.0, dtype=t.bfloat16, device="cuda")
+    before = host_bits(y).copy()
+    with pytest.raises(iqd.IqdError):
+        iqd.w8a8_linear(q, sa, w, sw, split_k=3, y=y)
+    with pytest.raises(iqd.IqdError):
+        iqd.w8a8_linear(q, sa, w, sw, split_k=2, y=y, workspace=t.empty(16, dtype=t.uint8, device="cuda"))
+    t.cuda.synchronize()
+    assert_bits_equal(host_bits(y), before, "canary")
+
+
+# ----------------------------------------------------------------------------
+# Qwen3-8B-shaped decode layers: b = 1..8, b = 512, split-K, sampled oracle rows
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("li", range(4))
+def test_qwen3_8b_layer_invariance_and_parity(iqd, li):
+    t = torch()
+    L = W.qwen3_8b_layer(li, tokens=512)
+    T, N = L.x.shape[0], L.N
+    oq, osa = oracle.quantize_token(L.x)
+    q, sa = gpu_quant(iqd, L.x)
+    w, sw = dev(L.w), dev(L.s_w)
+    # b = 1 for every token: the reference rows
+    y1 = t.empty((T, N), dtype=t.bfloat16, device="cuda")
+    for i in range(T):
+        iqd.w8a8_linear(q[i:i + 1], sa[i:i + 1], w, sw, y=y1[i:i + 1])
+    ref = host_bits(y1)
+    rows = sample_rows(N, 48, 2001 + li)
+    oy = oracle.w8a8(oq, osa, L.w[rows], L.s_w[rows])
+    assert_bits_equal(ref[:, rows], oy, f"{L.name} b=1 vs oracle")
+    # speculative-verify widths over the first 64 positions
+    for b in range(2, 9):
+        out = t.empty((64, N), dtype=t.bfloat16, device="cuda")
+        for t0 in range(0, 64, b):
+            t1 = min(64, t0 + b)
+            iqd.w8a8_linear(q[t0:t1], sa[t0:t1], w, sw, y=out[t0:t1])
+        assert_bits_equal(host_bits(out), ref[:64], f"{L.name} b={b} vs b=1")
+    # split-K at b = 8
+    for split in (2, 4, 8):
+        y = iqd.w8a8_linear(q[:8], sa[:8], w, sw, split_k=split)
+        assert_bits_equal(host_bits(y), ref[:8], f"{L.name} split={split}")
+    # prefill: all 512 tokens in one pass, twice (run-to-run bitwise)
+    y512 = iqd.w8a8_linear(q, sa, w, sw)
+    assert_bits_equal(host_bits(y512), ref, f"{L.name} b=512 vs b=1")
+    y512b = iqd.w8a8_linear(q, sa, w, sw)
+    assert_bits_equal(host_bits(y512b), ref, f"{L.name} b=512 second run")
