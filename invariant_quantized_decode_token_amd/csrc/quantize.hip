@@ -65,24 +65,25 @@ __device__ __forceinline__ Bf16x8 load8(const uint16_t *p) {
 
 constexpr int kQuantThreads = 256;
 
+template <int NT>
 __device__ __forceinline__ float block_amax(float m) {
 #pragma unroll
     for (int mask = 32; mask >= 1; mask >>= 1) m = fmaxf(m, shfl_xor(m, mask));
-    __shared__ float wmax[kQuantThreads / kWave];
+    __shared__ float wmax[NT / kWave];
     if (lane_id() == 0) wmax[threadIdx.x / kWave] = m;
     __syncthreads();
     float amax = wmax[0];
 #pragma unroll
-    for (int i = 1; i < kQuantThreads / kWave; ++i) amax = fmaxf(amax, wmax[i]);
+    for (int i = 1; i < NT / kWave; ++i) amax = fmaxf(amax, wmax[i]);
     return amax;
 }
 
-// One workgroup per token row, the row held in registers (VPT 16-byte
-// vectors per thread): one read of x, then the quantized write.
-template <int VPT>
-__global__ __launch_bounds__(kQuantThreads) void k_quant_token_reg(const uint16_t *__restrict__ x, int K,
-                                                                   int8_t *__restrict__ q,
-                                                                   float *__restrict__ s_out) {
+// One workgroup of NT threads per token row, the row held in registers (VPT
+// 16-byte vectors per thread): one read of x, then the quantized write.  A
+// wide workgroup keeps the per-thread chain of divisions short.
+template <int NT, int VPT>
+__global__ __launch_bounds__(NT) void k_quant_token_reg(const uint16_t *__restrict__ x, int K,
+                                                        int8_t *__restrict__ q, float *__restrict__ s_out) {
     const int t = blockIdx.x;
     const uint16_t *xr = x + static_cast<int64_t>(t) * K;
     int8_t *qr = q + static_cast<int64_t>(t) * K;
@@ -91,16 +92,16 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_token_reg(const uint16_
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-        const int v = threadIdx.x + i * kQuantThreads;
+        const int v = threadIdx.x + i * NT;
         xv[i] = Bf16x8{};
         if (v < nvec) xv[i] = load8(xr + 8 * v);
         m = fmaxf(m, amax8(xv[i]));
     }
-    const float s = block_amax(m) / 127.0f;
+    const float s = block_amax<NT>(m) / 127.0f;
     if (threadIdx.x == 0) s_out[t] = s;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-        const int v = threadIdx.x + i * kQuantThreads;
+        const int v = threadIdx.x + i * NT;
         if (v < nvec) *reinterpret_cast<int2 *>(qr + 8 * v) = quant8(xv[i], s);
     }
 }
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_token(const uint16_t *_
     const int nvec = K / 8;
     float m = 0.0f;
     for (int v = threadIdx.x; v < nvec; v += kQuantThreads) m = fmaxf(m, amax8(load8(xr + 8 * v)));
-    const float s = block_amax(m) / 127.0f;
+    const float s = block_amax<kQuantThreads>(m) / 127.0f;
     if (threadIdx.x == 0) s_out[t] = s;
     for (int v = threadIdx.x; v < nvec; v += kQuantThreads)
         *reinterpret_cast<int2 *>(qr + 8 * v) = quant8(load8(xr + 8 * v), s);
@@ -143,15 +144,19 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_block32(const uint16_t 
 }  // namespace
 
 hipError_t launch_quantize_token(const uint16_t *x, int b, int K, int8_t *q, float *s, hipStream_t st) {
-    const int vpt = (K / 8 + kQuantThreads - 1) / kQuantThreads;
-    if (vpt <= 1)
-        hipLaunchKernelGGL(k_quant_token_reg<1>, dim3(b), dim3(kQuantThreads), 0, st, x, K, q, s);
-    else if (vpt <= 2)
-        hipLaunchKernelGGL(k_quant_token_reg<2>, dim3(b), dim3(kQuantThreads), 0, st, x, K, q, s);
-    else if (vpt <= 4)
-        hipLaunchKernelGGL(k_quant_token_reg<4>, dim3(b), dim3(kQuantThreads), 0, st, x, K, q, s);
-    else if (vpt <= 8)
-        hipLaunchKernelGGL(k_quant_token_reg<8>, dim3(b), dim3(kQuantThreads), 0, st, x, K, q, s);
+    const int nvec = K / 8;
+    if (nvec <= 256)
+        hipLaunchKernelGGL((k_quant_token_reg<256, 1>), dim3(b), dim3(256), 0, st, x, K, q, s);
+    else if (nvec <= 512)
+        hipLaunchKernelGGL((k_quant_token_reg<512, 1>), dim3(b), dim3(512), 0, st, x, K, q, s);
+    else if (nvec <= 1024)
+        hipLaunchKernelGGL((k_quant_token_reg<1024, 1>), dim3(b), dim3(1024), 0, st, x, K, q, s);
+    else if (nvec <= 2048)
+        hipLaunchKernelGGL((k_quant_token_reg<1024, 2>), dim3(b), dim3(1024), 0, st, x, K, q, s);
+    else if (nvec <= 4096)
+        hipLaunchKernelGGL((k_quant_token_reg<1024, 4>), dim3(b), dim3(1024), 0, st, x, K, q, s);
+    else if (nvec <= 8192)
+        hipLaunchKernelGGL((k_quant_token_reg<1024, 8>), dim3(b), dim3(1024), 0, st, x, K, q, s);
     else
         hipLaunchKernelGGL(k_quant_token, dim3(b), dim3(kQuantThreads), 0, st, x, K, q, s);
     return hipGetLastError();

@@ -19,18 +19,21 @@
 // Mapping (64-lane waves):
 //  * a wave owns RS consecutive weight rows and a contiguous range of 16-byte
 //    K vectors; lane l reads vector v0 + l + 64 i of each row with a 16-byte
-//    non-temporal load (1 KiB contiguous per row per wave instruction);
+//    non-temporal buffer load (1 KiB contiguous per row per wave
+//    instruction).  Row starts live in scalar buffer resources whose range
+//    ends at the wave's K range, token starts in scalar offsets, so the loads
+//    need no per-lane address arithmetic and lanes past the range read zeros;
 //  * the wave walks its work as a flat sequence of chunks (U vectors per lane
 //    per row) and keeps the next chunk's weights in flight while it computes
 //    the current one (a ring of D register buffers, D - 1 chunks in flight);
 //  * each 16-byte weight vector meets the same K vector of all B tokens
-//    (staged once per workgroup in LDS when they fit) through four
+//    (read through L1/L2) through four
 //    v_dot4_i32_i8 per token, tokens in the outer loop so that only one
 //    activation vector per chunk step is live;
 //  * RS*B int32 accumulators per lane are reduce-scattered across the wave,
 //    then the `ks` waves that split the same rows along K add their partials
 //    through LDS; the owning lane applies the epilogue;
-//  * workgroups are persistent over row groups.
+//  * a workgroup may be persistent over several row groups.
 #include "device.hpp"
 #include "kernels.hpp"
 #include "w8a8_matvec_impl.hpp"
@@ -38,23 +41,40 @@
 namespace iqd {
 namespace {
 
-// Launch configuration per token count (chosen by measurement on MI355X; the
-// numerics are identical for every entry).
+// Launch configurations, chosen by a sweep on MI355X (rows per wave, chunk
+// size, waves per workgroup, ring depth, K split, LDS staging, grid) over the
+// Qwen3-8B decode shapes; the numerics are the same for every configuration.
+//  * small b: activations read through L1/L2, one workgroup per row group;
+//  * b >= 5 on large matrices: activations staged once per workgroup in LDS
+//    (16-wave workgroups, persistent over row groups), which keeps the
+//    per-lane activation reads off the vector-memory path.
 struct MvConfig {
-    int rs, u, nw, d;
+    int rs, u, nw, d, ks;
+    bool lds;
 };
 
-template <int B>
-constexpr MvConfig mv_config() {
-    if constexpr (B <= 8) return {2, 1, 4, 4};
-    else return {2, 1, 4, 4};
+constexpr int64_t kLdsMinWeightBytes = 32ll << 20;
+
+template <int B, int RS, int U, int NW, int D>
+hipError_t launch_cfg(const MvArgs &a, hipStream_t st, int ks, bool lds) {
+    const int kvec = a.K / 16;
+    if (ks > kvec / a.split) ks = 1;
+    return mv_launch<B, RS, U, NW, D>(a, st, device_info().cus, ks, /*grid*/ 0, lds);
 }
 
 template <int B>
-hipError_t launch_b(const MvArgs &base, hipStream_t st) {
-    constexpr MvConfig c = mv_config<B>();
-    return mv_launch<B, c.rs, c.u, c.nw, c.d>(base, st, device_info().cus, device_info().max_lds_block, /*ks=*/0, /*lds=*/-1,
-                                         /*grid=*/0);
+hipError_t launch_b(const MvArgs &a, hipStream_t st) {
+    const int64_t wbytes = static_cast<int64_t>(a.N) * a.K;
+    const bool big = wbytes >= kLdsMinWeightBytes && static_cast<int64_t>(B) * a.K / a.split <= 128 * 1024;
+    if constexpr (B <= 4) {
+        return launch_cfg<B, 4, 2, 4, 3>(a, st, 2, false);
+    } else if constexpr (B <= 8) {
+        if (big) return launch_cfg<B, 2, 1, 16, 2>(a, st, 2, true);
+        return launch_cfg<B, 4, 1, 4, 3>(a, st, 2, false);
+    } else {
+        if (big) return launch_cfg<B, 4, 1, 8, 2>(a, st, 1, true);
+        return launch_cfg<B, 4, 2, 4, 4>(a, st, 2, false);
+    }
 }
 
 }  // namespace

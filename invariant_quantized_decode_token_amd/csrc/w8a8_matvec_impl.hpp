@@ -31,48 +31,22 @@ struct WChunk {
     v4i v[U][RS];
 };
 
-template <int U, int RS>
-__device__ __forceinline__ WChunk<U, RS> mv_load_chunk(const int8_t *__restrict__ w, int K, int N, int row0, int vb,
-                                                       int v1) {
-    WChunk<U, RS> c;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int vu = vb + u * kWave;
-        const bool ok = vu < v1;
-#pragma unroll
-        for (int r = 0; r < RS; ++r) {
-            const int row = min(row0 + r, N - 1);  // rows past N are computed and dropped
-            c.v[u][r] = zero16();
-            if (ok) c.v[u][r] = load_stream16(w + static_cast<int64_t>(row) * K + 16 * vu);
-        }
-    }
-    return c;
+// Raw buffer resource over [base, base + bytes): a load whose offset
+// (scalar offset + lane offset + immediate) is >= bytes returns 0 without
+// touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
 }
 
-// acc[r * B + t] += <weight chunk row r, token t>, tokens outermost so that
-// one activation vector is live at a time.
-template <int B, int U, int RS, int NP, bool LDS>
-__device__ __forceinline__ void mv_compute_chunk(int32_t (&acc)[NP], const WChunk<U, RS> &c, const v4i *act,
-                                                 int nvs, int sv0, const int8_t *__restrict__ q, int K, int vb,
-                                                 int v1) {
-#pragma unroll
-    for (int t = 0; t < B; ++t) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int vu = min(vb + u * kWave, v1 - 1);  // weights are 0 past v1
-            const v4i av = LDS ? act[t * nvs + (vu - sv0)] : load16(q + static_cast<int64_t>(t) * K + 16 * vu);
-#pragma unroll
-            for (int r = 0; r < RS; ++r) acc[r * B + t] = dot16(c.v[u][r], av, acc[r * B + t]);
-        }
-    }
-}
+constexpr int kAuxStream = 2;  // non-temporal: weights are read exactly once
 
 template <int B, int RS, int U, int NW, int D, bool LDS>
 __global__ __launch_bounds__(NW * kWave) void k_w8a8_matvec(MvArgs a) {
-    extern __shared__ v4i smem[];
+    __shared__ int32_t red[NW][kWave];
+    extern __shared__ v4i act[];  // [B][nvs] activations of this split when LDS
     const int K = a.K, N = a.N;
     const int lane = lane_id();
-    const int wave = static_cast<int>(threadIdx.x) / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int s = blockIdx.y;
     const int kvec = K / 16;
     const int sv0 = s * kvec / a.split;
@@ -93,42 +67,68 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_matvec(MvArgs a) {
     constexpr int NV = RS * B;
     constexpr int NP = pow2_ceil(NV);
     static_assert(NP <= kWave, "one reduced value per lane at most");
+    static_assert(U * kWave * 16 <= 4096, "chunk offsets must fit the 12-bit immediate");
 
-    v4i *act = smem;                                                           // [B][nvs] when LDS
-    int32_t *red = reinterpret_cast<int32_t *>(smem + (LDS ? B * nvs : 0));  // [NW][64]
+    // Weight rows get one resource each, ending at this wave's K range, so
+    // lanes past v1 read zeros.  The activation resource spans all B rows: a
+    // lane past v1 may read another token's bytes (or zeros past the end),
+    // which only ever meet zero weights.
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q, B * K);
 
-    // chunk c: row group of step (c / nch), lane vector base of K chunk (c % nch)
-#define IQD_MV_ROW0(c) ((((bx + ((c) / nch) * gx) * rgs + rg) * RS))
-#define IQD_MV_VB(c) (v0 + ((c) % nch) * U * kWave + lane)
+    auto row0_of = [&](int c) __attribute__((always_inline)) {
+        return ((bx + (c / nch) * gx) * rgs + rg) * RS;
+    };
+    auto voff_of = [&](int c) __attribute__((always_inline)) {
+        return 16 * (v0 + (c % nch) * U * kWave + lane);
+    };
+    auto load_chunk = [&](int c) __attribute__((always_inline)) {
+        WChunk<U, RS> ch;
+        const int row0 = row0_of(c);
+        const int vo = voff_of(c);
+#pragma unroll
+        for (int r = 0; r < RS; ++r) {
+            const int row = min(row0 + r, N - 1);  // rows past N are computed and dropped
+            const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w + static_cast<int64_t>(row) * K, 16 * v1);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                ch.v[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wr, vo + u * kWave * 16, 0, kAuxStream);
+        }
+        return ch;
+    };
 
     int32_t acc[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) acc[i] = 0;
 
-    static_assert(D >= 2, "ring of at least two chunks");
-    WChunk<U, RS> ring[D];  // chunk c lives in ring[c % D]; D - 1 chunks stay in flight
+    auto compute_chunk = [&](const WChunk<U, RS> &ch, int c) __attribute__((always_inline)) {
+        const int vo = voff_of(c);
 #pragma unroll
-    for (int i = 0; i < D - 1; ++i)
-        if (i < total) ring[i] = mv_load_chunk<U, RS>(a.w, K, N, IQD_MV_ROW0(i), IQD_MV_VB(i), v1);
-    if (LDS) {  // after the first weight loads, so that their latency overlaps the staging
-        for (int i = threadIdx.x; i < B * nvs; i += NW * kWave) {
-            const int t = i / nvs;
-            const int v = i - t * nvs;
-            act[i] = load16(a.q + static_cast<int64_t>(t) * K + 16 * (sv0 + v));
+        for (int t = 0; t < B; ++t) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                v4i av;
+                if constexpr (LDS) {
+                    const int v = min(vo / 16 + u * kWave, v1 - 1) - sv0;  // past v1 the weights are 0
+                    av = act[t * nvs + v];
+                } else {
+                    av = __builtin_amdgcn_raw_buffer_load_b128(qr, vo + u * kWave * 16, t * K, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < RS; ++r) acc[r * B + t] = dot16(ch.v[u][r], av, acc[r * B + t]);
+            }
         }
-        __syncthreads();
-    }
+    };
 
     // Finish a row group: reduce across lanes and waves, apply the epilogue.
     auto finish = [&](int c) __attribute__((always_inline)) {
-        const int row0 = IQD_MV_ROW0(c);
+        const int row0 = row0_of(c);
         int32_t val = reduce_scatter<NP>(acc, lane, AddI32());
         const int idx = reduce_scatter_index<NP>(lane);
         if (ks > 1) {
-            red[wave * kWave + lane] = val;
+            red[wave][lane] = val;
             __syncthreads();
             if (kp == 0)
-                for (int j = 1; j < ks; ++j) val += red[(wave + j) * kWave + lane];
+                for (int j = 1; j < ks; ++j) val += red[wave + j][lane];
             __syncthreads();
         }
         if (kp == 0 && lane < NP && idx < NV) {
@@ -146,21 +146,29 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_matvec(MvArgs a) {
         for (int i = 0; i < NP; ++i) acc[i] = 0;
     };
 
+    static_assert(D >= 2, "ring of at least two chunks");
+    WChunk<U, RS> ring[D];  // chunk c lives in ring[c % D]; D - 1 chunks stay in flight
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i)
+        if (i < total) ring[i] = load_chunk(i);
+    if constexpr (LDS) {  // staged after the first weight loads, whose latency it overlaps
+        for (int i = threadIdx.x; i < B * nvs; i += NW * kWave) {
+            const int t = i / nvs;
+            act[i] = __builtin_amdgcn_raw_buffer_load_b128(qr, 16 * (sv0 + i - t * nvs), t * K, 0);
+        }
+        __syncthreads();
+    }
     for (int c0 = 0; c0 < total; c0 += D) {
 #pragma unroll
         for (int i = 0; i < D; ++i) {
             const int c = c0 + i;
             if (c < total) {
-                if (c + D - 1 < total)
-                    ring[(i + D - 1) % D] =
-                        mv_load_chunk<U, RS>(a.w, K, N, IQD_MV_ROW0(c + D - 1), IQD_MV_VB(c + D - 1), v1);
-                mv_compute_chunk<B, U, RS, NP, LDS>(acc, ring[i], act, nvs, sv0, a.q, K, IQD_MV_VB(c), v1);
+                if (c + D - 1 < total) ring[(i + D - 1) % D] = load_chunk(c + D - 1);
+                compute_chunk(ring[i], c);
                 if (c % nch == nch - 1) finish(c);
             }
         }
     }
-#undef IQD_MV_ROW0
-#undef IQD_MV_VB
 }
 
 // Exact int32 sum of the split partials, then the canonical epilogue.
@@ -178,11 +186,12 @@ __global__ __launch_bounds__(256) void k_w8a8_combine(const int32_t *__restrict_
     y[i] = w8a8_epilogue(acc, s_a[t], s_w[n]);
 }
 
-// Launch k_w8a8_matvec<B, RS, U, NW, D, ...>.  ks = 0, lds = -1 and grid = 0
-// select the automatic choice: enough (row group, K part) units for about 16
-// waves per CU, activations in LDS when they fit, a persistent grid.
+// Launch k_w8a8_matvec<B, RS, U, NW, D, LDS>.  ks = 0 picks enough
+// (row group, K part) units for about 16 waves per CU; grid = 0 gives one
+// workgroup per row-group step (with LDS: at most as many workgroups as fit,
+// persistent over the steps, so that activations are staged once each).
 template <int B, int RS, int U, int NW, int D>
-hipError_t mv_launch(MvArgs a, hipStream_t st, int cus, int lds_limit, int ks, int lds, int grid) {
+hipError_t mv_launch(MvArgs a, hipStream_t st, int cus, int ks, int grid, bool lds = false) {
     const int kvec = a.K / 16;
     const int nvs_min = kvec / a.split;
     const int nvs_max = (kvec + a.split - 1) / a.split;
@@ -197,23 +206,27 @@ hipError_t mv_launch(MvArgs a, hipStream_t st, int cus, int lds_limit, int ks, i
     a.nsteps = (a.N + rows_per_step - 1) / rows_per_step;
     const int per_wave = (nvs_max + ks - 1) / ks;
     a.nch = (per_wave + kWave * U - 1) / (kWave * U);
-    const size_t red_bytes = static_cast<size_t>(NW) * kWave * sizeof(int32_t);
-    const size_t act_bytes = static_cast<size_t>(B) * nvs_max * 16;
-    bool use_lds = lds < 0 ? (act_bytes + red_bytes <= static_cast<size_t>(lds_limit)) : lds != 0;
-    if (use_lds && act_bytes + red_bytes > static_cast<size_t>(lds_limit)) return hipErrorInvalidValue;
-    const size_t smem = use_lds ? act_bytes + red_bytes : red_bytes;
+    if (!lds) {
+        if (grid <= 0 || grid > a.nsteps) grid = a.nsteps;
+        hipLaunchKernelGGL((k_w8a8_matvec<B, RS, U, NW, D, false>), dim3(grid, a.split), dim3(NW * kWave), 0, st, a);
+        return hipGetLastError();
+    }
+    const size_t smem = static_cast<size_t>(B) * nvs_max * 16;
+    const size_t lds_total = smem + static_cast<size_t>(NW) * kWave * 4;
+    if (lds_total > 160 * 1024) return hipErrorInvalidValue;
+    if (smem > 48 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w8a8_matvec<B, RS, U, NW, D, true>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+        if (e != hipSuccess) return e;
+    }
     if (grid <= 0) {
-        int per_cu = use_lds ? static_cast<int>(static_cast<size_t>(160 * 1024) / smem) : 8;
-        const int wave_cap = 32 / NW;  // at most 32 waves per CU
+        int per_cu = static_cast<int>(static_cast<size_t>(160 * 1024) / lds_total);
+        const int wave_cap = 32 / NW;
         per_cu = per_cu < 1 ? 1 : (per_cu > wave_cap ? wave_cap : per_cu);
-        grid = cus * (per_cu > 0 ? per_cu : 1);
+        grid = cus * per_cu;
     }
     if (grid > a.nsteps) grid = a.nsteps;
-    dim3 g(grid, a.split);
-    if (use_lds)
-        hipLaunchKernelGGL((k_w8a8_matvec<B, RS, U, NW, D, true>), g, dim3(NW * kWave), smem, st, a);
-    else
-        hipLaunchKernelGGL((k_w8a8_matvec<B, RS, U, NW, D, false>), g, dim3(NW * kWave), smem, st, a);
+    hipLaunchKernelGGL((k_w8a8_matvec<B, RS, U, NW, D, true>), dim3(grid, a.split), dim3(NW * kWave), smem, st, a);
     return hipGetLastError();
 }
 
