@@ -42,6 +42,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--detail", action="store_true", help="per-(layer, b) kernel timings")
     p.add_argument("--prefill", action="store_true", help="also time the b=512 prefill pass")
+    p.add_argument("--extra", action="store_true", help="also time the block-q8 and LM-head paths")
     return p.parse_args()
 
 
@@ -203,6 +204,47 @@ def main():
             pre.append({"layer": L.name, "b": T, "us": round(us, 2), "TOPS": round(tops, 1),
                         "mfma_frac": round(tops / 5000.0, 4)})
         out["prefill"] = pre
+
+    if args.extra:
+        ext = []
+        for i in range(2):
+            Lb = W.blockq8_layer(i, tokens=16)
+            wq = torch.from_numpy(Lb.w).to(dev)
+            wqs = [wq] + [wq.clone() for _ in range(3)]
+            dw = torch.from_numpy(Lb.d_w.view(np.int16)).view(torch.float16).to(dev)
+            xb = torch.from_numpy(Lb.x.view(np.int16)).view(torch.bfloat16).to(dev)
+            qb, db = iqd.quantize_activations(xb, group=32)
+            for b in (1, 4, 8, 16):
+                yb = torch.empty((b, Lb.N), dtype=torch.bfloat16, device=dev)
+
+                def bq(b=b, yb=yb):
+                    for c in range(4):
+                        iqd.blockq8_linear(qb[:b], db[:b], wqs[c], dw, y=yb)
+                g = capture(bq)
+                g.replay()
+                us = time_graph(g, 10) * 1e3 / 4
+                by = Lb.N * Lb.K * (1 + 2 / 32)
+                ext.append({"op": "blockq8_linear", "K": Lb.K, "N": Lb.N, "b": b, "us": round(us, 2),
+                            "weight_GBs": round(by / (us * 1e-6) / 1e9, 1)})
+            del wqs, wq
+        Ll = W.lm_head_layer(tokens=8)
+        wl = torch.from_numpy(Ll.w).to(dev)
+        swl = torch.from_numpy(Ll.s_w).to(dev)
+        xl = torch.from_numpy(Ll.x.view(np.int16)).view(torch.bfloat16).to(dev)
+        ql, sl = iqd.quantize_activations(xl)
+        for b in (1, 2, 3, 5, 8):
+            am = torch.empty((b,), dtype=torch.int32, device=dev)
+            lg = torch.empty((b, Ll.N), dtype=torch.bfloat16, device=dev)
+
+            def lh(b=b, am=am, lg=lg):
+                iqd.lm_head_argmax(ql[:b], sl[:b], wl, swl, logits=lg, argmax=am)
+            g = capture(lh)
+            g.replay()
+            us = time_graph(g, 10) * 1e3
+            by = Ll.N * Ll.K + 4 * Ll.N
+            ext.append({"op": "lm_head_argmax", "K": Ll.K, "N": Ll.N, "b": b, "us": round(us, 2),
+                        "weight_GBs": round(by / (us * 1e-6) / 1e9, 1)})
+        out["extra"] = ext
 
     if not args.no_cpu:
         import oracle

@@ -14,10 +14,12 @@
 //
 // Tiling: a workgroup of 4 waves computes a BM x 128 tile of y (BM tokens,
 // 128 weight rows); waves are 2 x 2, each owning a (BM/2) x 64 sub-tile of
-// v_mfma_i32_16x16x64_i8 accumulators.  K advances 64 bytes per stage; both
-// operand tiles are staged in LDS (rows padded to 80 bytes, so that the 16
+// v_mfma_i32_16x16x64_i8 accumulators.  K advances 128 bytes per stage; both
+// operand tiles are staged in LDS (rows padded to 144 bytes, so that the 16
 // rows a fragment read touches fall on distinct banks), double-buffered, with
-// the next stage's global loads in flight during the current stage's MFMAs.
+// two stages of global loads in flight ahead of the stage being multiplied.
+// Tiles are mapped to workgroups XCD by XCD so that the M tiles sharing a
+// weight tile run on one XCD and reuse it from its L2.
 // Operand layout of the instruction (checked on MI355X): lane l holds 16
 // bytes of A row (l % 16) and of B column (l % 16) at the same K offset
 // 16 * (l / 16); result register i of lane l is D[4 * (l / 16) + i][l % 16].
@@ -28,68 +30,82 @@ namespace iqd {
 namespace {
 
 constexpr int kBN = 128;
-constexpr int kBK = 64;
-constexpr int kRowPad = 80;  // bytes per staged row
 constexpr int kMfThreads = 256;
+constexpr int kXcds = 8;      // workgroups are dealt round-robin to the 8 XCDs (L2 domains)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
     const int nr = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : static_cast<int>(bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, nr, 0x00020000);
 }
 
-template <int BM>
+// Staged row: BK bytes plus 16 of padding, so that the 16 rows one fragment
+// read touches fall on distinct LDS banks.
+template <int BK>
+constexpr int row_pad() { return BK + 16; }
+
+template <int BM, int BK>
 __global__ __launch_bounds__(kMfThreads) void k_w8a8_mfma(const int8_t *__restrict__ q, const float *__restrict__ s_a,
                                                           const int8_t *__restrict__ w, const float *__restrict__ s_w,
                                                           int M, int N, int K, uint16_t *__restrict__ y) {
     constexpr int WM = BM / 2;        // wave sub-tile rows (tokens)
     constexpr int FM = WM / 16;       // fragments along M per wave
     constexpr int FN = 64 / 16;       // fragments along N per wave
-    constexpr int A_PIECES = BM * (kBK / 16);
-    constexpr int B_PIECES = kBN * (kBK / 16);
+    constexpr int kBK = BK;
+    constexpr int kRowPad = row_pad<BK>();
+    constexpr int CPR = kBK / 16;     // 16-byte pieces per staged row
+    constexpr int A_PIECES = BM * CPR;
+    constexpr int B_PIECES = kBN * CPR;
     constexpr int PIECES = (A_PIECES + B_PIECES) / kMfThreads;
     static_assert((A_PIECES + B_PIECES) % kMfThreads == 0, "whole pieces per thread");
-    __shared__ __attribute__((aligned(16))) int8_t lds[2][(BM + kBN) * kRowPad];
+    extern __shared__ __attribute__((aligned(16))) int8_t lds[];  // [2][(BM + kBN) * kRowPad]
+    constexpr int STAGE = (BM + kBN) * kRowPad;
+
+    // Tile of this workgroup.  The M tiles of one N tile (which read the same
+    // weight rows) are given consecutive slots of one XCD, so that the
+    // weight tile is fetched into that XCD's L2 once and reused from there.
+    const int mt = (M + BM - 1) / BM;
+    const int nt = (N + kBN - 1) / kBN;
+    const int L = blockIdx.x;
+    const int xcd = L % kXcds, slot = L / kXcds;
+    const int ntile = (slot / mt) * kXcds + xcd;
+    const int mtile = slot % mt;
+    if (ntile >= nt) return;  // padding slots of the last XCD round
+    const int m0 = mtile * BM;
+    const int n0 = ntile * kBN;
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * BM;
-    const int n0 = blockIdx.x * kBN;
     const int nst = (K + kBK - 1) / kBK;
 
-    // Loads: every row of A (token) and B (weight) is a K-long byte row; the
-    // resources end at the matrix ends (rows past M or N read zeros) and a
-    // piece whose K offset is past K is redirected out of range as well.
+    // Every row of A (token) and B (weight) is a K-long byte row; the
+    // resources end at the matrix ends and a piece past K or past the last row
+    // is redirected out of range, so it reads zeros.
     const __amdgpu_buffer_rsrc_t ra = rsrc(q, static_cast<int64_t>(M) * K);
     const __amdgpu_buffer_rsrc_t rb = rsrc(w, static_cast<int64_t>(N) * K);
-    int piece_row[PIECES], piece_chunk[PIECES];
-    bool piece_is_a[PIECES];
-#pragma unroll
-    for (int p = 0; p < PIECES; ++p) {
-        const int id = tid + p * kMfThreads;
-        piece_is_a[p] = id < A_PIECES;
-        const int j = piece_is_a[p] ? id : id - A_PIECES;
-        piece_row[p] = j >> 2;
-        piece_chunk[p] = j & 3;
-    }
     auto gload = [&](int st, v4i(&regs)[PIECES]) __attribute__((always_inline)) {
 #pragma unroll
         for (int p = 0; p < PIECES; ++p) {
-            const int k = st * kBK + piece_chunk[p] * 16;
-            const int row = (piece_is_a[p] ? m0 : n0) + piece_row[p];
-            const int lim = piece_is_a[p] ? M : N;
+            const int id = tid + p * kMfThreads;
+            const bool is_a = id < A_PIECES;
+            const int j = is_a ? id : id - A_PIECES;
+            const int k = st * kBK + (j % CPR) * 16;
+            const int row = (is_a ? m0 : n0) + j / CPR;
             int off = row * K + k;
-            if (k >= K || row >= lim) off = 0x7FFFFFF0;  // out of range: zeros
-            regs[p] = piece_is_a[p] ? __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0)
-                                    : __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 2);
+            if (k >= K || row >= (is_a ? M : N)) off = 0x7FFFFFF0;
+            regs[p] = is_a ? __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0)
+                           : __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 2);
         }
     };
     auto lstore = [&](int buf, const v4i(&regs)[PIECES]) __attribute__((always_inline)) {
 #pragma unroll
         for (int p = 0; p < PIECES; ++p) {
-            const int row = piece_is_a[p] ? piece_row[p] : BM + piece_row[p];
-            *reinterpret_cast<v4i *>(&lds[buf][row * kRowPad + piece_chunk[p] * 16]) = regs[p];
+            const int id = tid + p * kMfThreads;
+            const bool is_a = id < A_PIECES;
+            const int j = is_a ? id : id - A_PIECES;
+            const int row = (is_a ? 0 : BM) + j / CPR;
+            *reinterpret_cast<v4i *>(&lds[buf * STAGE + row * kRowPad + (j % CPR) * 16]) = regs[p];
         }
     };
 
@@ -99,28 +115,40 @@ __global__ __launch_bounds__(kMfThreads) void k_w8a8_mfma(const int8_t *__restri
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-    v4i regs[PIECES];
-    gload(0, regs);
-    lstore(0, regs);
+    // Two stages of global loads in flight ahead of the one being computed.
+    v4i r0[PIECES], r1[PIECES];
+    gload(0, r0);
+    if (nst > 1) gload(1, r1);
+    lstore(0, r0);
     __syncthreads();
-    const int fr = lane & 15;           // fragment row (A) / column (B)
-    const int fk = (lane >> 4) * 16;    // K byte offset of this lane's 16 bytes
-    for (int st = 0; st < nst; ++st) {
+    const int fr = lane & 15;         // fragment row (A) / column (B)
+    const int fk = (lane >> 4) * 16;  // K byte offset of this lane's 16 bytes within 64
+    auto stage = [&](int st, v4i(&next)[PIECES], v4i(&cur_in)[PIECES]) __attribute__((always_inline)) {
         const int buf = st & 1;
-        if (st + 1 < nst) gload(st + 1, regs);
-        v4i af[FM], bfr[FN];
+        if (st + 1 < nst) lstore(buf ^ 1, cur_in);          // stage st+1, loaded one stage ago
+        if (st + 2 < nst) gload(st + 2, next);               // stage st+2 into the registers just freed
+        const int8_t *base = lds + buf * STAGE;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            af[i] = *reinterpret_cast<const v4i *>(&lds[buf][(wm * WM + i * 16 + fr) * kRowPad + fk]);
+        for (int kk = 0; kk < kBK / 64; ++kk) {
+            v4i af[FM], bfr[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            bfr[j] = *reinterpret_cast<const v4i *>(&lds[buf][(BM + wn * 64 + j * 16 + fr) * kRowPad + fk]);
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const v4i *>(base + (wm * WM + i * 16 + fr) * kRowPad + kk * 64 + fk);
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+            for (int j = 0; j < FN; ++j)
+                bfr[j] = *reinterpret_cast<const v4i *>(base + (BM + wn * 64 + j * 16 + fr) * kRowPad + kk * 64 + fk);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        if (st + 1 < nst) lstore(buf ^ 1, regs);
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
         __syncthreads();
+    };
+    // r0 is free after stage 0's store; stage st stores st+1 from the other set.
+    for (int st = 0; st < nst; st += 2) {
+        stage(st, r0, r1);
+        if (st + 1 < nst) stage(st + 1, r1, r0);
     }
 
     // Epilogue: lane l, register r of fragment (i, j) is token
@@ -141,6 +169,20 @@ __global__ __launch_bounds__(kMfThreads) void k_w8a8_mfma(const int8_t *__restri
     }
 }
 
+template <int BM, int BK>
+hipError_t launch_tiles(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int b, int N, int K,
+                        uint16_t *y, hipStream_t st) {
+    const size_t smem = static_cast<size_t>(2) * (BM + kBN) * row_pad<BK>();
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w8a8_mfma<BM, BK>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+    if (e != hipSuccess) return e;
+    const int mt = (b + BM - 1) / BM;
+    const int nt = (N + kBN - 1) / kBN;
+    const int nt_pad = (nt + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((k_w8a8_mfma<BM, BK>), dim3(mt * nt_pad), dim3(kMfThreads), smem, st, q, s_a, w, s_w, b, N, K, y);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_w8a8_mfma(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int b, int N, int K,
@@ -156,14 +198,9 @@ hipError_t launch_w8a8_mfma(const int8_t *q, const float *s_a, const int8_t *w, 
         }
         return hipSuccess;
     }
-    const int nt = (N + kBN - 1) / kBN;
-    // 128-token tiles when they leave enough workgroups for the chip, else 64.
-    if (static_cast<int64_t>((b + 127) / 128) * nt >= 2 * device_info().cus) {
-        hipLaunchKernelGGL(k_w8a8_mfma<128>, dim3(nt, (b + 127) / 128), dim3(kMfThreads), 0, st, q, s_a, w, s_w, b, N, K, y);
-    } else {
-        hipLaunchKernelGGL(k_w8a8_mfma<64>, dim3(nt, (b + 63) / 64), dim3(kMfThreads), 0, st, q, s_a, w, s_w, b, N, K, y);
-    }
-    return hipGetLastError();
+    // 64-token tiles with 128-byte K stages measured fastest on every
+    // Qwen3-8B layer at b = 512 (against 128-token tiles and 64-byte stages).
+    return launch_tiles<64, 128>(q, s_a, w, s_w, b, N, K, y, st);
 }
 
 }  // namespace iqd
