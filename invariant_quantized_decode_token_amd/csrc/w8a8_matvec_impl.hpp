@@ -29,6 +29,7 @@ struct AddI32 {
 template <int U, int RS>
 struct WChunk {
     v4i v[U][RS];
+    float sw;  // weight scale of the output this lane writes for the chunk's row group
 };
 
 // Raw buffer resource over [base, base + bytes): a load whose offset
@@ -81,8 +82,22 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_matvec(MvArgs a) {
     auto voff_of = [&](int c) __attribute__((always_inline)) {
         return 16 * (v0 + (c % nch) * U * kWave + lane);
     };
+    // The output this lane writes after the reduction (if any) is fixed by its
+    // lane index: token t_out of row r_out of the row group.  Its scales are
+    // fetched as soon as the row group is known, so that their latency hides
+    // behind the weight stream instead of following it.
+    const int idx = reduce_scatter_index<NP>(lane);
+    const bool writer = kp == 0 && lane < NP && idx < NV;
+    const int r_out = idx / B;
+    const int t_out = idx - r_out * B;
+    const float sa_out = (writer && a.split == 1) ? a.s_a[t_out] : 0.0f;
+    auto scale_of = [&](int c) __attribute__((always_inline)) {
+        const int row = min(row0_of(c) + r_out, N - 1);
+        return (writer && a.split == 1) ? a.s_w[row] : 0.0f;
+    };
     auto load_chunk = [&](int c) __attribute__((always_inline)) {
         WChunk<U, RS> ch;
+        ch.sw = scale_of(c);
         const int row0 = row0_of(c);
         const int vo = voff_of(c);
 #pragma unroll
@@ -119,11 +134,11 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_matvec(MvArgs a) {
         }
     };
 
+
     // Finish a row group: reduce across lanes and waves, apply the epilogue.
-    auto finish = [&](int c) __attribute__((always_inline)) {
+    auto finish = [&](int c, float sw_out) __attribute__((always_inline)) {
         const int row0 = row0_of(c);
         int32_t val = reduce_scatter<NP>(acc, lane, AddI32());
-        const int idx = reduce_scatter_index<NP>(lane);
         if (ks > 1) {
             red[wave][lane] = val;
             __syncthreads();
@@ -131,15 +146,13 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_matvec(MvArgs a) {
                 for (int j = 1; j < ks; ++j) val += red[wave + j][lane];
             __syncthreads();
         }
-        if (kp == 0 && lane < NP && idx < NV) {
-            const int r = idx / B;
-            const int t = idx - r * B;
-            const int row = row0 + r;
+        if (writer) {
+            const int row = row0 + r_out;
             if (row < N) {
                 if (a.split == 1)
-                    a.y[static_cast<int64_t>(t) * N + row] = w8a8_epilogue(val, a.s_a[t], a.s_w[row]);
+                    a.y[static_cast<int64_t>(t_out) * N + row] = w8a8_epilogue(val, sa_out, sw_out);
                 else
-                    a.part[(static_cast<int64_t>(s) * B + t) * N + row] = val;
+                    a.part[(static_cast<int64_t>(s) * B + t_out) * N + row] = val;
             }
         }
 #pragma unroll
@@ -165,7 +178,7 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_matvec(MvArgs a) {
             if (c < total) {
                 if (c + D - 1 < total) ring[(i + D - 1) % D] = load_chunk(c + D - 1);
                 compute_chunk(ring[i], c);
-                if (c % nch == nch - 1) finish(c);
+                if (c % nch == nch - 1) finish(c, ring[i].sw);
             }
         }
     }
