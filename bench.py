@@ -11,8 +11,10 @@ in the 256 MB Infinity Cache.  Inputs are seeded synthetic data resident in
 HBM before timing; the step is replayed from a HIP graph.
 
 value = weight bytes streamed per step (int8 weights + fp32 scales) / step
-time, in GB/s.  The roofline object times the dominant kernel (the W8A8
-mat-vec) alone with HIP events on the stream it runs on.  The cpu_baseline
+time, in GB/s.  The roofline object times the dominant kernels (the 32 W8A8
+mat-vec launches of the step: the dot4 kernel k_w8a8_matvec and the
+matrix-core kernel k_w8a8_mfvec, chosen per shape) alone with HIP events on
+the stream they run on.  The cpu_baseline
 object times the CPU oracle on the same step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--detail]
@@ -155,7 +157,7 @@ def main():
     avg_us = ms_mv * 1e3 / n_launch
     achieved = mv_bytes / n_launch / (avg_us * 1e-6) / 1e9
 
-    traffic = committed_traffic("k_w8a8_matvec")
+    traffic = committed_traffic("w8a8_decode_matvec")
 
     out = {
         "metric": METRIC,
@@ -181,7 +183,8 @@ def main():
             "tokens_per_s_equiv": round(sum(B_LIST) / (ms * 1e-3), 1),
         },
         "roofline": {
-            "kernel": "k_w8a8_matvec",
+            "kernel": "W8A8 decode mat-vec (k_w8a8_matvec dot4 kernel at b=1 and at b<=4 on qkv/o; "
+                      "k_w8a8_mfvec matrix-core kernel otherwise)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

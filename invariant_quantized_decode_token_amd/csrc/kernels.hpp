@@ -24,6 +24,11 @@ hipError_t launch_quantize_block32(const uint16_t *x, int b, int K, int8_t *q, f
 hipError_t launch_w8a8_matvec(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w,
                               int b, int N, int K, uint16_t *y, int split, int32_t *part,
                               hipStream_t st);
+// The same mat-vec on the int8 matrix cores (split 1 only).  fits() tells
+// whether the shape is supported (activations must fit in LDS).
+bool w8a8_mfvec_fits(int b, int N, int K);
+hipError_t launch_w8a8_mfvec(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int b, int N,
+                             int K, uint16_t *y, hipStream_t st);
 hipError_t launch_w8a8_combine(const int32_t *part, const float *s_a, const float *s_w, int b, int N,
                                int split, uint16_t *y, hipStream_t st);
 

@@ -77,11 +77,23 @@ hipError_t launch_b(const MvArgs &a, hipStream_t st) {
     }
 }
 
+// The matrix-core kernel (w8a8_mfvec.hip) costs about the same for any
+// b <= 16, while the dot4 kernel's work grows with b: on MI355X the dot4
+// kernel wins at b = 1 and, on matrices of at most 512 tiles of 16 rows with
+// K <= 8192, at b = 2; the matrix-core kernel wins everywhere else.
+bool use_mfvec(int b, int N, int K) {
+    if (b == 1) return false;
+    if (b == 2 && (N + 15) / 16 <= 512 && K <= 8192) return false;
+    return w8a8_mfvec_fits(b, N, K);
+}
+
 }  // namespace
 
 hipError_t launch_w8a8_matvec(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w,
                               int b, int N, int K, uint16_t *y, int split, int32_t *part,
                               hipStream_t st) {
+    if (split == 1 && use_mfvec(b, N, K))
+        return launch_w8a8_mfvec(q, s_a, w, s_w, b, N, K, y, st);
     MvArgs a{};
     a.q = q;
     a.s_a = s_a;

@@ -104,6 +104,32 @@ def test_ragged_shapes_full_oracle(iqd, N, K):
         assert_bits_equal(host_bits(y), oy, f"N={N} K={K} b={b}")
 
 
+@pytest.mark.parametrize("N,K", [(4100, 1040), (8200, 2064), (4097, 272), (24592, 4096)])
+def test_matrix_core_shape_classes(iqd, N, K):
+    """Shapes on both sides of the matrix-core mat-vec's launch classes (256
+    and 512 tiles of 16 rows, a persistent grid past 256 workgroups), with N
+    not a multiple of 16 and K not a multiple of 256, at every b <= 16;
+    rows sampled against the oracle, all rows against b = 1."""
+    t = torch()
+    g = W.rng(N * 31 + K)
+    w = W.int8_weights(g, N, K)
+    s_w = W.log_uniform_scales(g, N)
+    x = W.normal_bf16(g, 16, K)
+    oq, osa = oracle.quantize_token(x)
+    q, sa = gpu_quant(iqd, x)
+    wd, swd = dev(w), dev(s_w)
+    rows = np.unique(np.concatenate([sample_rows(N, 40, N), np.arange(N - 17, N)]))
+    oy = oracle.w8a8(oq, osa, w[rows], s_w[rows])
+    y1 = t.empty((16, N), dtype=t.bfloat16, device="cuda")
+    for i in range(16):
+        iqd.w8a8_linear(q[i:i + 1], sa[i:i + 1], wd, swd, y=y1[i:i + 1])
+    ref = host_bits(y1)
+    assert_bits_equal(ref[:, rows], oy, f"N={N} K={K} b=1 vs oracle")
+    for b in range(2, 17):
+        y = iqd.w8a8_linear(q[:b], sa[:b], wd, swd)
+        assert_bits_equal(host_bits(y), ref[:b], f"N={N} K={K} b={b} vs b=1")
+
+
 def test_max_k_and_extreme_codes(iqd):
     """K = 131056 (the largest multiple of 16 under the bound) with every
     product at (-128)*(-128): acc = 2147287040, close to 2^31."""
