@@ -225,6 +225,12 @@ hipError_t launch_b(const BqArgs &base, hipStream_t st) {
 hipError_t launch_blockq8_matvec(const int8_t *q, const float *d_a, const int8_t *w,
                                  const uint16_t *d_w, int b, int N, int K, uint16_t *y, int split,
                                  float *part, hipStream_t st) {
+    // The matrix-core kernel forms the leaves of all 16 token columns of its
+    // instruction whatever b is, so its cost is flat in b, while this
+    // kernel's grows with b; measured on MI355X (4096 -> 4096 and
+    // 12288 -> 4096), the crossover is near b * K = 9 * 4096.
+    if (static_cast<int64_t>(b) * K >= 9 * 4096 && blockq8_mfvec_fits(b, N, K, split))
+        return launch_blockq8_mfvec(q, d_a, w, d_w, b, N, K, y, split, part, st);
     const int m = K / 32;
     int L = 1;
     while (L < m) L *= 2;

@@ -41,6 +41,12 @@ hipError_t launch_w8a8_mfma(const int8_t *q, const float *s_a, const int8_t *w, 
 hipError_t launch_blockq8_matvec(const int8_t *q, const float *d_a, const int8_t *w,
                                  const uint16_t *d_w, int b, int N, int K, uint16_t *y, int split,
                                  float *part, hipStream_t st);
+// The same block-quantized mat-vec on the int8 matrix cores (any split the
+// ABI accepts); fits() tells whether the shape is supported (activations
+// must fit in LDS).
+bool blockq8_mfvec_fits(int b, int N, int K, int split);
+hipError_t launch_blockq8_mfvec(const int8_t *q, const float *d_a, const int8_t *w, const uint16_t *d_w, int b,
+                                int N, int K, uint16_t *y, int split, float *part, hipStream_t st);
 hipError_t launch_blockq8_combine(const float *part, int b, int N, int split, uint16_t *y,
                                   hipStream_t st);
 

@@ -99,3 +99,41 @@ def test_blockq8_config_invariance_and_parity(iqd, li):
                 t1 = min(16, t0 + b)
                 iqd.blockq8_linear(q[t0:t1], d[t0:t1], w, dw, split_k=split, y=out[t0:t1])
             assert_bits_equal(host_bits(out), ref, f"{L.name} b={b} split={split}")
+
+
+# ----------------------------------------------------------------------------
+# the matrix-core kernel (taken from b * K >= 9 * 4096 on): ragged K and N,
+# padding-only waves, -0 padding and tree witnesses on that path
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("K", [2336, 3104, 4128, 8224])
+def test_matrix_core_path_ragged(iqd, K):
+    g = W.rng(77 * K)
+    N = 37
+    w, d_w = W.q8_0_weights(g, N, K)
+    x = W.normal_bf16(g, 16, K)
+    oq, od = oracle.quantize_block32(x)
+    od[5, 1::4] *= -1.0
+    oy = oracle.blockq8(oq, od, w, d_w)
+    q, d, wd, dwd = dev(oq), dev(od), dev(w), dev(d_w, "fp16")
+    for split in splits_for(K):
+        y = iqd.blockq8_linear(q, d, wd, dwd, split_k=split)
+        assert_bits_equal(host_bits(y), oy, f"K={K} b=16 split={split}")
+
+
+@pytest.mark.parametrize("K,b", [(4096, 9), (12288, 4)])
+def test_matrix_core_path_padding_and_witnesses(iqd, K, b):
+    q, d_a, w, d_w = W.negative_zero_operands(K, N=5, b=b)
+    oy = oracle.blockq8(q, d_a, w, d_w)
+    for split in splits_for(K):
+        y = iqd.blockq8_linear(dev(q), dev(d_a), dev(w), dev(d_w, "fp16"), split_k=split)
+        assert_bits_equal(host_bits(y), oy, f"-0 K={K} b={b} split={split}")
+    m = K // 32
+    rows = [[(0, 1)], [(16, 4)], [(32, 8)], [(0, 32)], [(128, 32)], [(256, 32)], [(0, 64)], [(96, 8), (32, 1)]]
+    rows = [r for r in rows if all(p + 3 * h < m for p, h in r)]
+    q, d_a, w, d_w = W.tree_witness_operands(K, rows, b=b)
+    oy = oracle.blockq8(q, d_a, w, d_w)
+    assert np.all(oy == 0)
+    for split in splits_for(K):
+        y = iqd.blockq8_linear(dev(q), dev(d_a), dev(w), dev(d_w, "fp16"), split_k=split)
+        assert_bits_equal(host_bits(y), oy, f"witness K={K} b={b} split={split}")
