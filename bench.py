@@ -263,10 +263,11 @@ def main():
             lg = torch.empty((b, Ll.N), dtype=torch.bfloat16, device=dev)
 
             def lh(b=b, am=am, lg=lg):
-                iqd.lm_head_argmax(ql[:b], sl[:b], wl, swl, logits=lg, argmax=am)
+                for _ in range(4):  # 622 MB of weights: far past the 256 MB Infinity Cache
+                    iqd.lm_head_argmax(ql[:b], sl[:b], wl, swl, logits=lg, argmax=am)
             g = capture(lh)
             g.replay()
-            us = time_graph(g, 10) * 1e3
+            us = time_graph(g, 10) * 1e3 / 4
             by = Ll.N * Ll.K + 4 * Ll.N
             ext.append({"op": "lm_head_argmax", "K": Ll.K, "N": Ll.N, "b": b, "us": round(us, 2),
                         "weight_GBs": round(by / (us * 1e-6) / 1e9, 1)})

@@ -153,9 +153,11 @@ int blockq8_linear(const int8_t *q, const float *d_a, const int8_t *w, const voi
  * The pages do not fix a tie rule ([P2 "Why the decoders disagreed?"] shows
  * a real bf16 tie); the lowest index wins.
  *
- *   logits_bf16  out bf16 [b, N], or NULL to skip writing the logits
+ *   logits_bf16  out bf16 [b, N], or NULL to keep the logits in the workspace
  *   argmax       out int32 [b]
- *   workspace    iqd_workspace_bytes(IQD_OP_LM_HEAD, b, N, K, 1) bytes
+ *   workspace    iqd_workspace_bytes(IQD_OP_LM_HEAD, b, N, K, 1) bytes, 16-byte
+ *                aligned: the logits when logits_bf16 is NULL, then 8 bytes
+ *                per (token, chunk of 4096 logits) of argmax scratch
  * Requires N <= 2^31 - 1.
  */
 int lm_head_argmax(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int64_t b,

@@ -221,7 +221,7 @@ def lm_head_argmax(q, s_a, w, s_w, logits=True, argmax=None, workspace=None):
     if argmax is None:
         argmax = torch.empty((b,), dtype=torch.int32, device=q.device)
     _check_tensor(argmax, "argmax", (torch.int32,), (b,))
-    need = 0 if lg is not None else workspace_bytes(IQD_OP_LM_HEAD, b, N, K, 1)
+    need = workspace_bytes(IQD_OP_LM_HEAD, b, N, K, 1)  # covers the no-logits case too
     if workspace is None:
         workspace = _workspace(need, q.device)
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0

@@ -112,8 +112,13 @@ int blockq8_split_ok(int64_t b, int64_t K, int32_t split) {
 size_t ws_w8a8(int64_t b, int64_t N, int32_t split) {
     return split > 1 ? round16(static_cast<size_t>(split) * b * N * 4) : 0;
 }
-size_t ws_lm_head(int64_t b, int64_t N, bool have_logits) {
+// [logits bf16 [b, N] when the caller passes none][argmax chunk keys u64 [b, chunks]]
+size_t ws_lm_head_logits(int64_t b, int64_t N, bool have_logits) {
     return have_logits ? 0 : round16(static_cast<size_t>(b) * N * 2);
+}
+size_t ws_lm_head(int64_t b, int64_t N, bool have_logits) {
+    return ws_lm_head_logits(b, N, have_logits) +
+           round16(static_cast<size_t>(b) * iqd::argmax_chunks(static_cast<int>(N)) * 8);
 }
 
 }  // namespace
@@ -265,6 +270,8 @@ int lm_head_argmax(const int8_t *q, const float *s_a, const int8_t *w, const flo
     clear_stale_error();
     hipStream_t hs = static_cast<hipStream_t>(stream);
     uint16_t *logits = static_cast<uint16_t *>(logits_bf16 ? logits_bf16 : workspace);
+    uint64_t *keys = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) +
+                                                  ws_lm_head_logits(b, N, logits_bf16 != nullptr));
     const int Ni = static_cast<int>(N), Ki = static_cast<int>(K);
     for (int64_t t0 = 0; t0 < b; t0 += kMatvecMaxB) {
         const int bc = static_cast<int>(b - t0 < kMatvecMaxB ? b - t0 : kMatvecMaxB);
@@ -272,7 +279,7 @@ int lm_head_argmax(const int8_t *q, const float *s_a, const int8_t *w, const flo
                                                hs);
         if (e != hipSuccess) return hip_status(e);
     }
-    return hip_status(iqd::launch_argmax_rows(logits, static_cast<int>(b), Ni, argmax, hs));
+    return hip_status(iqd::launch_argmax_rows(logits, static_cast<int>(b), Ni, argmax, keys, hs));
 }
 
 int pow2_requantize(const int8_t *w, const float *s_w, int64_t N, int64_t K, int8_t *w_out, float *s_out,

@@ -50,8 +50,10 @@ hipError_t launch_blockq8_mfvec(const int8_t *q, const float *d_a, const int8_t 
 hipError_t launch_blockq8_combine(const float *part, int b, int N, int split, uint16_t *y,
                                   hipStream_t st);
 
-// Argmax over bf16 logits [b, N]: smallest index of the row maximum.
-hipError_t launch_argmax_rows(const uint16_t *logits, int b, int N, int32_t *out, hipStream_t st);
+// Argmax over bf16 logits [b, N]: smallest index of the row maximum.  part is
+// scratch for argmax_chunks(N) 64-bit keys per row.
+int argmax_chunks(int N);
+hipError_t launch_argmax_rows(const uint16_t *logits, int b, int N, int32_t *out, uint64_t *part, hipStream_t st);
 
 hipError_t launch_pow2_requant(const int8_t *w, const float *s, int N, int K, int8_t *w_out,
                                float *s_out, hipStream_t st);

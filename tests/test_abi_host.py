@@ -37,7 +37,9 @@ def test_workspace_bytes():
     assert iqd.workspace_bytes(L.IQD_OP_W8A8, 8, 4096, 131072, 1) == 0     # rejected K
     assert iqd.workspace_bytes(L.IQD_OP_BLOCKQ8, 16, 4096, 12288, 16) == 16 * 16 * 4096 * 4
     assert iqd.workspace_bytes(L.IQD_OP_BLOCKQ8, 16, 4096, 4096, 8) == 0   # 32*8 > L=128
-    assert iqd.workspace_bytes(L.IQD_OP_LM_HEAD, 5, 151936, 4096, 1) == (5 * 151936 * 2 + 15) // 16 * 16
+    chunks = (151936 + 4095) // 4096  # argmax chunk keys: 8 bytes per (token, chunk of 4096 logits)
+    assert iqd.workspace_bytes(L.IQD_OP_LM_HEAD, 5, 151936, 4096, 1) == \
+        (5 * 151936 * 2 + 15) // 16 * 16 + (5 * chunks * 8 + 15) // 16 * 16
 
 
 A = 1 << 20  # fake, 16-byte aligned, never dereferenced
