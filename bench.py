@@ -4,17 +4,18 @@
 One step is a speculative-verify sweep over the four W8A8 decode layers of a
 Qwen3-8B-shaped transformer block (qkv 4096->6144, o 4096->4096, gate_up
 4096->24576, down 12288->4096) at every width b = 1..8: for each (b, layer)
-the bf16 activations are quantized per token (quantize_activations) and the
-int8 weights are streamed once (w8a8_linear).  The 32 (b, layer) passes use
+the bf16 activations are quantized per token and the int8 weights are
+streamed once, in one w8a8_linear_bf16 call (one kernel; the same bits as
+quantize_activations followed by w8a8_linear, whose step time is reported
+as config.separate_calls_ms_per_step).  The 32 (b, layer) passes use
 8 distinct copies of the weights (1.5 GB) so that no pass finds its weights
 in the 256 MB Infinity Cache.  Inputs are seeded synthetic data resident in
 HBM before timing; the step is replayed from a HIP graph.
 
 value = weight bytes streamed per step (int8 weights + fp32 scales) / step
-time, in GB/s.  The roofline object times the dominant kernels (the 32 W8A8
-mat-vec launches of the step: the dot4 kernel k_w8a8_matvec and the
-matrix-core kernel k_w8a8_mfvec, chosen per shape) alone with HIP events on
-the stream they run on.  The cpu_baseline
+time, in GB/s.  The roofline object times the dominant kernels, the 32 W8A8
+mat-vec launches of a step (on the step's quantized activations), alone with
+HIP events on the stream they run on.  The cpu_baseline
 object times the CPU oracle on the same step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--detail]
@@ -101,17 +102,26 @@ def main():
     def layer_bytes(L):
         return L.N * L.K + 4 * L.N
 
-    def algo_bytes(L, b):  # what one w8a8_linear call must move
+    def linear_bytes(L, b):  # what one w8a8_linear call must move: weights, scales, q, s_a in, bf16 y out
         return L.N * L.K + 4 * L.N + b * L.K + 4 * b + 2 * b * L.N
 
     step_weight_bytes = sum(layer_bytes(L) for L in layers) * len(B_LIST)
 
-    def step(quantize=True):
+    def step():
+        """The decode step: per (b, layer) one w8a8_linear_bf16 call, which
+        quantizes the bf16 activations and runs the linear in one kernel."""
         for bi, b in enumerate(B_LIST):
             c = bi % COPIES
             for li, L in enumerate(layers):
-                if quantize:
-                    iqd.quantize_activations(xs[li][:b], q=qs[li][:b], scale=sas[li][:b])
+                iqd.w8a8_linear_bf16(xs[li][:b], wsets[li][c], swsets[li], y=ys[li][:b])
+
+    def step_separate():
+        """The same step as two calls per (b, layer): quantize_activations,
+        then w8a8_linear (reported for comparison)."""
+        for bi, b in enumerate(B_LIST):
+            c = bi % COPIES
+            for li, L in enumerate(layers):
+                iqd.quantize_activations(xs[li][:b], q=qs[li][:b], scale=sas[li][:b])
                 iqd.w8a8_linear(qs[li][:b], sas[li][:b], wsets[li][c], swsets[li], y=ys[li][:b])
 
     def capture(fn):
@@ -147,16 +157,31 @@ def main():
     ms = time_graph(g_step, args.steps)
     value = step_weight_bytes / (ms * 1e-3) / 1e9
 
-    # ---- dominant kernel alone: the W8A8 mat-vec launches of the step -----------
-    g_mv = capture(lambda: step(quantize=False))
+    # ---- the same work as separate quantize + linear calls -------------------------
+    g_sep = capture(step_separate)
+    for _ in range(3):
+        g_sep.replay()
+    ms_sep = time_graph(g_sep, args.steps)
+
+    # ---- dominant kernel alone: the 32 W8A8 mat-vec launches of a step ------------
+    # (w8a8_linear on the step's quantized activations: k_w8a8_matvec at b = 1
+    # and on small matrices at b = 2, k_w8a8_mfvec otherwise)
+    for li, L in enumerate(layers):
+        iqd.quantize_activations(xs[li], q=qs[li], scale=sas[li])
+
+    def step_linear():
+        for bi, b in enumerate(B_LIST):
+            c = bi % COPIES
+            for li, L in enumerate(layers):
+                iqd.w8a8_linear(qs[li][:b], sas[li][:b], wsets[li][c], swsets[li], y=ys[li][:b])
+    g_mv = capture(step_linear)
     for _ in range(3):
         g_mv.replay()
     ms_mv = time_graph(g_mv, args.steps)
     n_launch = len(B_LIST) * len(layers)
-    mv_bytes = sum(algo_bytes(L, b) for b in B_LIST for L in layers)
+    mv_bytes = sum(linear_bytes(L, b) for b in B_LIST for L in layers)
     avg_us = ms_mv * 1e3 / n_launch
     achieved = mv_bytes / n_launch / (avg_us * 1e-6) / 1e9
-
     traffic = committed_traffic("w8a8_decode_matvec")
 
     out = {
@@ -175,16 +200,18 @@ def main():
                 "outlier channels)",
         "config": {
             "workload": "Qwen3-8B-shaped W8A8 decode linears qkv 4096->6144, o 4096->4096, gate_up "
-                        "4096->24576, down 12288->4096; quantize + linear at every b=1..8",
+                        "4096->24576, down 12288->4096; per-token quantization + linear (one "
+                        "w8a8_linear_bf16 call) at every b=1..8",
             "b": B_LIST,
             "weight_copies": COPIES,
             "weight_bytes_per_step": step_weight_bytes,
             "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
             "tokens_per_s_equiv": round(sum(B_LIST) / (ms * 1e-3), 1),
+            "separate_calls_ms_per_step": round(ms_sep, 5),
         },
         "roofline": {
-            "kernel": "W8A8 decode mat-vec (k_w8a8_matvec dot4 kernel at b=1 and at b<=4 on qkv/o; "
-                      "k_w8a8_mfvec matrix-core kernel otherwise)",
+            "kernel": "W8A8 decode mat-vec, the 32 launches of a step alone (k_w8a8_matvec dot4 at b=1 and on "
+                      "small matrices at b=2, k_w8a8_mfvec matrix cores otherwise)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -203,12 +230,20 @@ def main():
             for b in B_LIST:
                 def one(li=li, L=L, b=b):
                     for c in range(COPIES):
+                        iqd.w8a8_linear_bf16(xs[li][:b], wsets[li][c], swsets[li], y=ys[li][:b])
+
+                def lin(li=li, L=L, b=b):
+                    for c in range(COPIES):
                         iqd.w8a8_linear(qs[li][:b], sas[li][:b], wsets[li][c], swsets[li], y=ys[li][:b])
                 g = capture(one)
                 g.replay()
                 us = time_graph(g, 20) * 1e3 / COPIES
+                g2 = capture(lin)
+                g2.replay()
+                us2 = time_graph(g2, 20) * 1e3 / COPIES
                 det.append({"layer": L.name, "b": b, "us": round(us, 3),
-                            "weight_GBs": round(layer_bytes(L) / (us * 1e-6) / 1e9, 1)})
+                            "weight_GBs": round(layer_bytes(L) / (us * 1e-6) / 1e9, 1),
+                            "linear_only_us": round(us2, 3)})
         out["detail"] = det
 
     if not args.no_prefill:

@@ -67,7 +67,7 @@ typedef enum {
 } iqd_status;
 
 /* Operation codes for iqd_workspace_bytes. */
-enum { IQD_OP_W8A8 = 1, IQD_OP_BLOCKQ8 = 2, IQD_OP_LM_HEAD = 3 };
+enum { IQD_OP_W8A8 = 1, IQD_OP_BLOCKQ8 = 2, IQD_OP_LM_HEAD = 3, IQD_OP_W8A8_BF16 = 4 };
 
 #define IQD_K_MAX 131071
 #define IQD_SPLIT_K_MAX 64
@@ -109,14 +109,41 @@ int quantize_activations(const void *x_bf16, int64_t b, int64_t K, int32_t group
  *              kernel adds (exactly) before the epilogue.  Needs workspace.
  *   workspace  device scratch of iqd_workspace_bytes(IQD_OP_W8A8, ...) bytes
  *              (NULL allowed when that is 0).
- * b <= 16 streams the weights once through packed int8 dot products; larger
- * b uses the int8 matrix-core path.  Both give identical bits.
+ * b <= 16 streams the weights once (packed int8 dot products at b = 1 and
+ * on small matrices at b = 2, the int8 matrix cores otherwise); larger b uses
+ * the tiled matrix-core path.  All give identical bits.
  * Errors: IQD_ERR_INVALID, IQD_ERR_ALIGN, IQD_ERR_RANGE, IQD_ERR_UNSUPPORTED
  * (bad split_k), IQD_ERR_WORKSPACE, IQD_ERR_HIP.
  */
 int w8a8_linear(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int64_t b,
                 int64_t N, int64_t K, void *y_bf16, int32_t split_k, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/*
+ * w8a8_linear_bf16 - quantize_activations (per token) and w8a8_linear in one
+ * call, from bf16 activations.
+ *
+ * The results are those of quantize_activations(x, group 0) followed by
+ * w8a8_linear(split_k 1), bit for bit.  For one token (K <= 8192) one kernel
+ * does both: every workgroup quantizes the activations it multiplies (the
+ * reciprocal of the scale first, the correctly rounded division wherever the
+ * quotient lies within 2^-14 of a rounding boundary), which removes the
+ * separate quantization launch.  Wider passes run the two kernels.
+ *
+ *   x_bf16   in  bf16 [b, K]                (16-byte aligned)
+ *   w, s_w   as w8a8_linear
+ *   y_bf16   out bf16 [b, N]
+ *   q_out    out int8 [b, K], or NULL       (16-byte aligned)
+ *   s_a_out  out fp32 [b], or NULL
+ *   workspace  iqd_workspace_bytes(IQD_OP_W8A8_BF16, b, N, K, 1) bytes,
+ *              16-byte aligned; used (for q and s_a) only when a shape takes
+ *              the separate quantize + linear path and q_out or s_a_out is
+ *              NULL; NULL allowed when both outputs are given.
+ * Errors: as w8a8_linear.
+ */
+int w8a8_linear_bf16(const void *x_bf16, const int8_t *w, const float *s_w, int64_t b, int64_t N, int64_t K,
+                     void *y_bf16, int8_t *q_out, float *s_a_out, void *workspace, size_t workspace_bytes,
+                     void *stream);
 
 /*
  * blockq8_linear - q8_0-style block-quantized linear.

@@ -26,6 +26,7 @@ IQD_ERR_HIP = -6
 IQD_OP_W8A8 = 1
 IQD_OP_BLOCKQ8 = 2
 IQD_OP_LM_HEAD = 3
+IQD_OP_W8A8_BF16 = 4
 
 IQD_K_MAX = 131071
 IQD_SPLIT_K_MAX = 64
@@ -50,6 +51,7 @@ SZ = ctypes.c_size_t
 SIGNATURES = {
     "quantize_activations": (ctypes.c_int, [P, I64, I64, I32, P, P, P]),
     "w8a8_linear": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]),
+    "w8a8_linear_bf16": (ctypes.c_int, [P, P, P, I64, I64, I64, P, P, P, P, SZ, P]),
     "blockq8_linear": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]),
     "lm_head_argmax": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, P, SZ, P]),
     "pow2_requantize": (ctypes.c_int, [P, P, I64, I64, P, P, P]),
@@ -200,6 +202,33 @@ def blockq8_linear(q, d_a, w, d_w, split_k: int = 1, y=None, workspace=None):
     st = load().blockq8_linear(_ptr(q), _ptr(d_a), _ptr(w), _ptr(d_w), b, N, K, _ptr(y), split_k, _ptr(workspace),
                                wsb, _stream_ptr())
     _raise(st, "blockq8_linear")
+    return y
+
+
+def w8a8_linear_bf16(x, w, s_w, y=None, q_out=None, s_a_out=None, workspace=None):
+    """x bf16 [b, K], w int8 [N, K], s_w fp32 [N] -> y bf16 [b, N]; quantize_activations
+    and w8a8_linear in one call (q_out int8 [b, K] / s_a_out fp32 [b] optionally receive the
+    quantized activations)."""
+    torch = _torch()
+    _check_tensor(x, "x", (torch.bfloat16,))
+    b, K = x.shape
+    N = w.shape[0]
+    _check_tensor(w, "w", (torch.int8,), (N, K))
+    _check_tensor(s_w, "s_w", (torch.float32,), (N,))
+    if y is None:
+        y = torch.empty((b, N), dtype=torch.bfloat16, device=x.device)
+    _check_tensor(y, "y", (torch.bfloat16,), (b, N))
+    if q_out is not None:
+        _check_tensor(q_out, "q_out", (torch.int8,), (b, K))
+    if s_a_out is not None:
+        _check_tensor(s_a_out, "s_a_out", (torch.float32,), (b,))
+    need = 0 if (q_out is not None and s_a_out is not None) else workspace_bytes(IQD_OP_W8A8_BF16, b, N, K, 1)
+    if workspace is None:
+        workspace = _workspace(need, x.device)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().w8a8_linear_bf16(_ptr(x), _ptr(w), _ptr(s_w), b, N, K, _ptr(y), _ptr(q_out), _ptr(s_a_out),
+                                 _ptr(workspace), wsb, _stream_ptr())
+    _raise(st, "w8a8_linear_bf16")
     return y
 
 

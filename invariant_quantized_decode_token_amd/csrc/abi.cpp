@@ -112,6 +112,9 @@ int blockq8_split_ok(int64_t b, int64_t K, int32_t split) {
 size_t ws_w8a8(int64_t b, int64_t N, int32_t split) {
     return split > 1 ? round16(static_cast<size_t>(split) * b * N * 4) : 0;
 }
+// [q int8 [b, K]][s_a fp32 [b]] for the separate quantize + linear path
+size_t ws_w8a8_bf16(int64_t b, int64_t K) { return round16(static_cast<size_t>(b) * K) + round16(static_cast<size_t>(b) * 4); }
+
 // [logits bf16 [b, N] when the caller passes none][argmax chunk keys u64 [b, chunks]]
 size_t ws_lm_head_logits(int64_t b, int64_t N, bool have_logits) {
     return have_logits ? 0 : round16(static_cast<size_t>(b) * N * 2);
@@ -150,6 +153,8 @@ size_t iqd_workspace_bytes(int op, int64_t b, int64_t N, int64_t K, int32_t spli
             return split_k > 1 ? round16(static_cast<size_t>(split_k) * b * N * 4) : 0;
         case IQD_OP_LM_HEAD:
             return ws_lm_head(b, N, false);
+        case IQD_OP_W8A8_BF16:
+            return ws_w8a8_bf16(b, K);
         default:
             return 0;
     }
@@ -202,6 +207,41 @@ int w8a8_linear(const int8_t *q, const float *s_a, const int8_t *w, const float 
     hipError_t e = iqd::launch_w8a8_matvec(q, s_a, w, s_w, bi, Ni, Ki, nullptr, split_k, part, hs);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(iqd::launch_w8a8_combine(part, s_a, s_w, bi, Ni, split_k, y, hs));
+}
+
+int w8a8_linear_bf16(const void *x_bf16, const int8_t *w, const float *s_w, int64_t b, int64_t N, int64_t K,
+                     void *y_bf16, int8_t *q_out, float *s_a_out, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    if (!x_bf16 || !w || !s_w || !y_bf16) return IQD_ERR_INVALID;
+    int st = check_shape(b, N, K);
+    if (st != IQD_OK) return st;
+    if (!aligned(x_bf16, 16) || !aligned(w, 16) || !aligned(s_w, 4) || !aligned(y_bf16, 2) ||
+        (q_out && !aligned(q_out, 16)) || (s_a_out && !aligned(s_a_out, 4)))
+        return IQD_ERR_ALIGN;
+    const bool fused = b <= kMatvecMaxB && iqd::w8a8_mfvec_fused_ok(static_cast<int>(b), static_cast<int>(N),
+                                                                   static_cast<int>(K));
+    const size_t ws = (!fused && (!q_out || !s_a_out)) ? ws_w8a8_bf16(b, K) : 0;
+    if (ws > 0) {
+        if (!workspace || workspace_bytes < ws) return IQD_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return IQD_ERR_ALIGN;
+    }
+    const size_t qbytes = static_cast<size_t>(b) * K;
+    if (any_overlap({{y_bf16, static_cast<size_t>(b) * N * 2}, {q_out, q_out ? qbytes : 0},
+                     {s_a_out, s_a_out ? static_cast<size_t>(b) * 4 : 0}, {ws ? workspace : nullptr, ws}},
+                    {{x_bf16, qbytes * 2}, {w, static_cast<size_t>(N) * K}, {s_w, static_cast<size_t>(N) * 4}}))
+        return IQD_ERR_INVALID;
+    clear_stale_error();
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
+    uint16_t *y = static_cast<uint16_t *>(y_bf16);
+    const int bi = static_cast<int>(b), Ni = static_cast<int>(N), Ki = static_cast<int>(K);
+    if (fused) return hip_status(iqd::launch_w8a8_mfvec_fused(x, w, s_w, bi, Ni, Ki, y, q_out, s_a_out, hs));
+    int8_t *q = q_out ? q_out : static_cast<int8_t *>(workspace);
+    float *s_a = s_a_out ? s_a_out : reinterpret_cast<float *>(static_cast<char *>(workspace) + round16(qbytes));
+    hipError_t e = iqd::launch_quantize_token(x, bi, Ki, q, s_a, hs);
+    if (e != hipSuccess) return hip_status(e);
+    if (b > kMatvecMaxB) return hip_status(iqd::launch_w8a8_mfma(q, s_a, w, s_w, bi, Ni, Ki, y, hs));
+    return hip_status(iqd::launch_w8a8_matvec(q, s_a, w, s_w, bi, Ni, Ki, y, 1, nullptr, hs));
 }
 
 int blockq8_linear(const int8_t *q, const float *d_a, const int8_t *w, const void *d_w_fp16, int64_t b, int64_t N,

@@ -50,8 +50,11 @@ constexpr int kOob = 0x7FFFFFF0;            // buffer offset that reads zeros (l
 constexpr int kMaxLds = 160 * 1024;
 
 struct MfvArgs {
-    const int8_t *q;
-    const float *s_a;
+    const int8_t *q;     // int8 activations [b, K] (or, fused, nothing)
+    const float *s_a;    // their per-token scales [b]
+    const uint16_t *x;   // fused: bf16 activations [b, K], quantized by every workgroup
+    int8_t *q_out;       // fused, optional: workgroup 0 writes the quantized activations here
+    float *s_out;        // fused, optional: and their scales here
     const int8_t *w;
     const float *s_w;
     int b, N, K;
@@ -59,6 +62,63 @@ struct MfvArgs {
     int ntiles;  // ceil(N / 16)
     int nch;     // chunks per tile per wave
 };
+
+// Per-token quantization of 8 bf16 values (one 16-byte vector), the same
+// result as the quantize kernel: q = clamp(rint_half_even(fl(x / s)), -127,
+// 127), 0 when s == 0.  The quotient is formed as y = fl(x * fl(1 / s)) first:
+// |y - fl(x / s)| <= |x / s| (3 u + u^2) < 2.3e-5 (u = 2^-24, |x / s| <= 127
+// (1 + u)), so rint(y) == rint(fl(x / s)) unless y lies within 2^-14 of a
+// half-integer.  A vector with such a value (or any vector when 1 / s
+// overflows) is redone with the correctly rounded division.  |x / s| never
+// exceeds 127 (1 + u) for finite x, so the clamp only matters for the slow
+// path's non-finite inputs.
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t pack4(int32_t a, int32_t b, int32_t c, int32_t d) {
+    return (static_cast<uint32_t>(a) & 0xFFu) | ((static_cast<uint32_t>(b) & 0xFFu) << 8) |
+           ((static_cast<uint32_t>(c) & 0xFFu) << 16) | (static_cast<uint32_t>(d) << 24);
+}
+
+__device__ __forceinline__ uint2 quant8(const v4i &v, float s, float rcp, bool fast_ok) {
+    if (s == 0.0f) return make_uint2(0u, 0u);
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        e[2 * i] = bf16_lo(static_cast<uint32_t>(v[i]));
+        e[2 * i + 1] = bf16_hi(static_cast<uint32_t>(v[i]));
+    }
+    int32_t q[8];
+    bool near = !fast_ok;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float y = e[i] * rcp;
+        near |= __builtin_fabsf(__builtin_amdgcn_fractf(y) - 0.5f) <= 0x1p-14f;
+        q[i] = static_cast<int32_t>(__builtin_rintf(y));
+    }
+    if (__builtin_expect(near, 0)) {  // one branch per vector
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = static_cast<int32_t>(fminf(fmaxf(__builtin_rintf(e[i] / s), -127.0f), 127.0f));
+    }
+    return make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+}
+
+__device__ __forceinline__ float amax8(const v4i &v) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m = fmaxf(m, __builtin_fabsf(bf16_lo(static_cast<uint32_t>(v[i]))));
+        m = fmaxf(m, __builtin_fabsf(bf16_hi(static_cast<uint32_t>(v[i]))));
+    }
+    return m;
+}
+
+// Maximum over the lanes of a wave (exact: max does not round).
+__device__ __forceinline__ float wave_max(float m) {
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) m = fmaxf(m, shfl_xor(m, mask));
+    return m;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
@@ -72,7 +132,7 @@ struct TChunk {
 
 __host__ __device__ constexpr int act_stride(int K) { return (K + kUnit - 1) / kUnit * kUnit + 16; }
 
-template <int NW, int KS, int U, int D, int XB, bool WFIRST>
+template <int NW, int KS, int U, int D, int XB, bool WFIRST, bool FUSE>
 __global__ __launch_bounds__(NW * kWave) void k_w8a8_mfvec(MfvArgs a) {
     constexpr int NT = NW / KS;  // tile slots per workgroup
     static_assert(NW % KS == 0 && D >= 2, "tile slots and ring");
@@ -141,42 +201,130 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_mfvec(MfvArgs a) {
     // launcher sizes XB to cover all b x K bytes when it can), and are
     // written to LDS while the later weight chunks are still in flight.
     constexpr int NTH = NW * kWave;
-    const int kv = K / 16;
-    const int nv = a.b * kv;
     const int tid = static_cast<int>(threadIdx.x);
-    v4i xa[XB];
     TChunk<U> ring[D];  // chunk c lives in ring[c % D]
-    if constexpr (WFIRST) ring[0] = load_chunk(0, true);
-#pragma unroll
-    for (int j = 0; j < XB; ++j) {
-        const int v = j * NTH + tid;
-        xa[j] = __builtin_amdgcn_raw_buffer_load_b128(qr, v < nv ? 16 * v : kOob, 0, 0);
-    }
-#pragma unroll
-    for (int i = WFIRST ? 1 : 0; i < D - 1; ++i) ring[i] = load_chunk(i, true);
-    // Lanes past the end store to their wave's transpose tile (rewritten
-    // before it is read), so that the store, and the load feeding it, stay
-    // unconditional and in issue order.
-    auto put = [&](int base) __attribute__((always_inline)) {
+    v4i xa[XB];
+    float sa;
+    if constexpr (!FUSE) {
+        const int kv = K / 16;
+        const int nv = a.b * kv;
+        if constexpr (WFIRST) ring[0] = load_chunk(0, true);
 #pragma unroll
         for (int j = 0; j < XB; ++j) {
-            const int v = base + j * NTH + tid;
-            const int t = v < nv ? v / kv : 0;
-            int8_t *dst = v < nv ? xs + t * KP + 16 * (v - t * kv) : tt + 16 * lane;
-            *reinterpret_cast<v4i *>(dst) = xa[j];
-        }
-    };
-    // The token scale is needed only by the epilogue: loaded behind the
-    // prologue so that no prologue wait depends on it.
-    const float sa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sar, r * 4, 0, 0));
-    put(0);
-    for (int base = XB * NTH; base < nv; base += XB * NTH) {  // only when b x K exceeds one batch
-#pragma unroll
-        for (int j = 0; j < XB; ++j) {
-            const int v = base + j * NTH + tid;
+            const int v = j * NTH + tid;
             xa[j] = __builtin_amdgcn_raw_buffer_load_b128(qr, v < nv ? 16 * v : kOob, 0, 0);
         }
-        put(base);
+#pragma unroll
+        for (int i = WFIRST ? 1 : 0; i < D - 1; ++i) ring[i] = load_chunk(i, true);
+        // Lanes past the end store to their wave's transpose tile (rewritten
+        // before it is read), so that the store, and the load feeding it,
+        // stay unconditional and in issue order.
+        auto put = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < XB; ++j) {
+                const int v = base + j * NTH + tid;
+                const int t = v < nv ? v / kv : 0;
+                int8_t *dst = v < nv ? xs + t * KP + 16 * (v - t * kv) : tt + 16 * lane;
+                *reinterpret_cast<v4i *>(dst) = xa[j];
+            }
+        };
+        // The token scale is needed only by the epilogue: loaded behind the
+        // prologue so that no prologue wait depends on it.
+        sa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sar, r * 4, 0, 0));
+        put(0);
+        for (int base = XB * NTH; base < nv; base += XB * NTH) {  // only when b x K exceeds one batch
+#pragma unroll
+            for (int j = 0; j < XB; ++j) {
+                const int v = base + j * NTH + tid;
+                xa[j] = __builtin_amdgcn_raw_buffer_load_b128(qr, v < nv ? 16 * v : kOob, 0, 0);
+            }
+            put(base);
+        }
+    } else {
+        // Fused quantization: every workgroup reads the bf16 activations
+        // (16-byte vectors of 8 values), forms the per-token absmax through
+        // LDS, and writes the int8 codes of all b tokens into its staging
+        // area; workgroup 0 also writes them (and the scales) out if asked.
+        __shared__ uint32_t amx[16];
+        __shared__ float ssc[16], src[16];
+        const int kvx = K / 8;
+        const int nvx = a.b * kvx;
+        const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, a.b * K * 2);
+        auto load_x = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < XB; ++j) {
+                const int v = base + j * NTH + tid;
+                xa[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, v < nvx ? 16 * v : kOob, 0, 0);
+            }
+        };
+        if constexpr (WFIRST) ring[0] = load_chunk(0, true);
+        load_x(0);
+#pragma unroll
+        for (int i = WFIRST ? 1 : 0; i < D - 1; ++i) ring[i] = load_chunk(i, true);
+        if (tid < 16) amx[tid] = 0u;
+        __syncthreads();
+        // The 64 consecutive vectors of a wave instruction span at most two
+        // tokens when a token row holds at least 64 of them: one wave maximum
+        // per token, one LDS atomic per wave.  Shorter rows: one atomic per
+        // lane.  (|x| >= 0, so float bits order as the values.)
+        auto fold_max = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < XB; ++j) {
+                const int v = base + j * NTH + tid;
+                const float m = v < nvx ? amax8(xa[j]) : 0.0f;
+                if (kvx >= kWave) {
+                    const int vw = __builtin_amdgcn_readfirstlane(v);  // lane 0's vector
+                    const int t0 = vw / kvx;
+                    const int t1 = min(t0 + 1, a.b - 1);
+                    const bool first = v / kvx == t0;
+                    const float m0 = wave_max(first ? m : 0.0f);
+                    const float m1 = wave_max(first ? 0.0f : m);
+                    if (lane == 0 && vw < nvx) {
+                        atomicMax(&amx[t0], __float_as_uint(m0));
+                        if (t1 != t0) atomicMax(&amx[t1], __float_as_uint(m1));
+                    }
+                } else if (v < nvx) {
+                    atomicMax(&amx[v / kvx], __float_as_uint(m));
+                }
+            }
+        };
+        fold_max(0);
+        const bool multi = nvx > XB * NTH;  // rare: b x K exceeds one batch, x is read twice
+        for (int base = XB * NTH; base < nvx; base += XB * NTH) {
+            load_x(base);
+            fold_max(base);
+        }
+        __syncthreads();
+        if (tid < a.b) {
+            const float sc = __uint_as_float(amx[tid]) / 127.0f;  // the quantizer's scale, IEEE division
+            ssc[tid] = sc;
+            src[tid] = 1.0f / sc;
+        }
+        __syncthreads();
+        const bool out = bx == 0 && a.q_out != nullptr;
+        auto put_q = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < XB; ++j) {
+                const int v = base + j * NTH + tid;
+                if (v < nvx) {
+                    const int t = v / kvx;
+                    const float rc = src[t];
+                    const uint2 q8 = quant8(xa[j], ssc[t], rc, __builtin_isfinite(rc));
+                    *reinterpret_cast<uint2 *>(xs + t * KP + 8 * (v - t * kvx)) = q8;
+                    if (out) *reinterpret_cast<uint2 *>(a.q_out + 8 * static_cast<int64_t>(v)) = q8;
+                }
+            }
+        };
+        if (multi) {
+            for (int base = 0; base < nvx; base += XB * NTH) {
+                load_x(base);
+                put_q(base);
+            }
+        } else {
+            put_q(0);
+        }
+        if (bx == 0 && a.s_out != nullptr && tid < a.b) a.s_out[tid] = ssc[tid];
+        sa = ssc[min(r, a.b - 1)];
     }
     __syncthreads();
     const int kmax = KP - 16 - 64;  // last in-row start of a 64-byte step (past K the weights are 0)
@@ -227,14 +375,14 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_mfvec(MfvArgs a) {
 
 template <int NW, int KS>
 constexpr int lds_bytes_static() {
-    return (KS > 1 ? 2 * NW : 1) * kWave * 16;
+    return (KS > 1 ? 2 * NW : 1) * kWave * 16 + 256;  // + the fused path's per-token scale slots
 }
 
-template <int NW, int KS, int U, int D, int XB, bool WFIRST>
+template <int NW, int KS, int U, int D, int XB, bool WFIRST, bool FUSE>
 hipError_t launch_x(const MfvArgs &a, int grid, int smem, hipStream_t st) {
     constexpr int NT = NW / KS;
     const int ngroups = (a.ntiles + NT - 1) / NT;
-    const void *fn = reinterpret_cast<const void *>(&k_w8a8_mfvec<NW, KS, U, D, XB, WFIRST>);
+    const void *fn = reinterpret_cast<const void *>(&k_w8a8_mfvec<NW, KS, U, D, XB, WFIRST, FUSE>);
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     if (grid <= 0) {  // one round of resident workgroups: past that, persistent ones (activations staged once each)
@@ -248,28 +396,36 @@ hipError_t launch_x(const MfvArgs &a, int grid, int smem, hipStream_t st) {
         grid = (per_cu < 1 ? 1 : per_cu) * device_info().cus;
     }
     if (grid > ngroups) grid = ngroups;
-    hipLaunchKernelGGL((k_w8a8_mfvec<NW, KS, U, D, XB, WFIRST>), dim3(grid), dim3(NW * kWave), smem, st, a);
+    hipLaunchKernelGGL((k_w8a8_mfvec<NW, KS, U, D, XB, WFIRST, FUSE>), dim3(grid), dim3(NW * kWave), smem, st, a);
     return hipGetLastError();
 }
 
-// Activation vectors per thread: the smallest instantiated count that covers
-// all of b x K in one batch (16 and a loop beyond that).
-template <int NW, int KS, int U, int D, bool WFIRST>
+// Staged 16-byte vectors per thread (int8 codes, or bf16 values when fused):
+// the smallest instantiated count that covers all of b x K in one batch (16
+// and a loop beyond that).
+template <int NW, int KS, int U, int D, bool WFIRST, bool FUSE>
 hipError_t launch_d(const MfvArgs &a, int grid, int smem, hipStream_t st) {
-    const int per_thread = (a.b * (a.K / 16) + NW * kWave - 1) / (NW * kWave);
-    if (per_thread <= 1) return launch_x<NW, KS, U, D, 1, WFIRST>(a, grid, smem, st);
-    if (per_thread <= 2) return launch_x<NW, KS, U, D, 2, WFIRST>(a, grid, smem, st);
-    if (per_thread <= 3) return launch_x<NW, KS, U, D, 3, WFIRST>(a, grid, smem, st);
-    if (per_thread <= 4) return launch_x<NW, KS, U, D, 4, WFIRST>(a, grid, smem, st);
-    if (per_thread <= 6) return launch_x<NW, KS, U, D, 6, WFIRST>(a, grid, smem, st);
-    if (per_thread <= 8) return launch_x<NW, KS, U, D, 8, WFIRST>(a, grid, smem, st);
-    if (per_thread <= 12) return launch_x<NW, KS, U, D, 12, WFIRST>(a, grid, smem, st);
-    return launch_x<NW, KS, U, D, 16, WFIRST>(a, grid, smem, st);
+    const int vec_bytes = FUSE ? 8 : 16;  // K elements per 16-byte vector
+    const int per_thread = (a.b * (a.K / vec_bytes) + NW * kWave - 1) / (NW * kWave);
+    if constexpr (FUSE) {  // taken for one token and K <= 8192 only
+        if (per_thread <= 1) return launch_x<NW, KS, U, D, 1, WFIRST, FUSE>(a, grid, smem, st);
+        if (per_thread <= 2) return launch_x<NW, KS, U, D, 2, WFIRST, FUSE>(a, grid, smem, st);
+        if (per_thread <= 4) return launch_x<NW, KS, U, D, 4, WFIRST, FUSE>(a, grid, smem, st);
+        return hipErrorInvalidValue;
+    }
+    if (per_thread <= 1) return launch_x<NW, KS, U, D, 1, WFIRST, FUSE>(a, grid, smem, st);
+    if (per_thread <= 2) return launch_x<NW, KS, U, D, 2, WFIRST, FUSE>(a, grid, smem, st);
+    if (per_thread <= 3) return launch_x<NW, KS, U, D, 3, WFIRST, FUSE>(a, grid, smem, st);
+    if (per_thread <= 4) return launch_x<NW, KS, U, D, 4, WFIRST, FUSE>(a, grid, smem, st);
+    if (per_thread <= 6) return launch_x<NW, KS, U, D, 6, WFIRST, FUSE>(a, grid, smem, st);
+    if (per_thread <= 8) return launch_x<NW, KS, U, D, 8, WFIRST, FUSE>(a, grid, smem, st);
+    if (per_thread <= 12) return launch_x<NW, KS, U, D, 12, WFIRST, FUSE>(a, grid, smem, st);
+    return launch_x<NW, KS, U, D, 16, WFIRST, FUSE>(a, grid, smem, st);
 }
 
 // The prologue loads D - 1 chunks of the first tile, so D - 1 may not exceed
 // the chunks of one tile; shorter K falls back to a ring of two.
-template <int NW, int KS, int U, int D, bool WFIRST>
+template <int NW, int KS, int U, int D, bool WFIRST, bool FUSE>
 hipError_t launch_cfg(MfvArgs a, int grid, hipStream_t st) {
     a.ntiles = (a.N + kTileRows - 1) / kTileRows;
     const int nku = (a.K + kUnit - 1) / kUnit;
@@ -277,9 +433,9 @@ hipError_t launch_cfg(MfvArgs a, int grid, hipStream_t st) {
     const int smem = NW * kTBytes + a.b * act_stride(a.K);
     if (smem + lds_bytes_static<NW, KS>() > kMaxLds) return hipErrorInvalidValue;
     if constexpr (D > 2) {
-        if (a.nch < D - 1) return launch_d<NW, KS, U, 2, WFIRST>(a, grid, smem, st);
+        if (a.nch < D - 1) return launch_d<NW, KS, U, 2, WFIRST, FUSE>(a, grid, smem, st);
     }
-    return launch_d<NW, KS, U, D, WFIRST>(a, grid, smem, st);
+    return launch_d<NW, KS, U, D, WFIRST, FUSE>(a, grid, smem, st);
 }
 
 // Launch shapes from a sweep on MI355X over the Qwen3-8B decode layers at
@@ -303,20 +459,21 @@ Pick pick(int b, int N, int K) {
     return b > 12 ? Pick{8, 4, 5} : Pick{4, 2, 4};
 }
 
+template <bool FUSE>
 hipError_t launch_pick(const Pick &p, const MfvArgs &a, hipStream_t st) {
     switch (p.id) {
-        case 0: return launch_cfg<8, 8, 1, 2, false>(a, 0, st);
-        case 1: return launch_cfg<8, 8, 2, 2, false>(a, 0, st);
-        case 2: return launch_cfg<4, 4, 2, 2, true>(a, 0, st);
-        case 3: return launch_cfg<8, 4, 2, 3, false>(a, device_info().cus, st);
-        case 4: return launch_cfg<4, 2, 2, 2, true>(a, 0, st);
-        case 5: return launch_cfg<8, 4, 2, 3, true>(a, 0, st);
+        case 0: return launch_cfg<8, 8, 1, 2, false, FUSE>(a, 0, st);
+        case 1: return launch_cfg<8, 8, 2, 2, false, FUSE>(a, 0, st);
+        case 2: return launch_cfg<4, 4, 2, 2, true, FUSE>(a, 0, st);
+        case 3: return launch_cfg<8, 4, 2, 3, false, FUSE>(a, device_info().cus, st);
+        case 4: return launch_cfg<4, 2, 2, 2, true, FUSE>(a, 0, st);
+        case 5: return launch_cfg<8, 4, 2, 3, true, FUSE>(a, 0, st);
     }
     return hipErrorInvalidValue;
 }
 
 int lds_need(const Pick &p, int b, int K) {
-    return p.nw * kTBytes + b * act_stride(K) + (p.ks > 1 ? 2 * p.nw : 1) * kWave * 16;
+    return p.nw * kTBytes + b * act_stride(K) + (p.ks > 1 ? 2 * p.nw : 1) * kWave * 16 + 256;
 }
 
 }  // namespace
@@ -341,7 +498,29 @@ hipError_t launch_w8a8_mfvec(const int8_t *q, const float *s_a, const int8_t *w,
     a.N = N;
     a.K = K;
     a.y = y;
-    return launch_pick(pick(b, N, K), a, st);
+    return launch_pick<false>(pick(b, N, K), a, st);
+}
+
+// Every workgroup repeats the quantization of all b x K activations, so the
+// fused kernel pays only for one token: measured on MI355X against the
+// separate quantize kernel + mat-vec, it wins at b = 1 for K = 4096 and
+// loses from b = 2 on (at b = 8 it is 2-3x slower on the Qwen3-8B layers).
+bool w8a8_mfvec_fused_ok(int b, int N, int K) { return b == 1 && K <= 8192 && w8a8_mfvec_fits(b, N, K); }
+
+hipError_t launch_w8a8_mfvec_fused(const uint16_t *x, const int8_t *w, const float *s_w, int b, int N, int K,
+                                   uint16_t *y, int8_t *q_out, float *s_out, hipStream_t st) {
+    if (!w8a8_mfvec_fused_ok(b, N, K)) return hipErrorInvalidValue;
+    MfvArgs a{};
+    a.x = x;
+    a.q_out = q_out;
+    a.s_out = s_out;
+    a.w = w;
+    a.s_w = s_w;
+    a.b = b;
+    a.N = N;
+    a.K = K;
+    a.y = y;
+    return launch_pick<true>(pick(b, N, K), a, st);
 }
 
 }  // namespace iqd

@@ -17,7 +17,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = iqd.header_functions()
-    assert set(names) == {"quantize_activations", "w8a8_linear", "blockq8_linear", "lm_head_argmax",
+    assert set(names) == {"quantize_activations", "w8a8_linear", "w8a8_linear_bf16", "blockq8_linear", "lm_head_argmax",
                           "pow2_requantize", "iqd_workspace_bytes", "iqd_status_str", "iqd_last_hip_error"}
     for n in names:
         assert hasattr(lib, n), n
@@ -117,3 +117,17 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros((2, 64), dtype=torch.int8)
     with pytest.raises(ValueError, match="GPU"):
         iqd.w8a8_linear(q, torch.zeros(2), torch.zeros((8, 64), dtype=torch.int8), torch.zeros(8))
+
+
+def test_w8a8_bf16_validation(lib):
+    def call(x=A, w=2 * A, sw=3 * A, b=4, N=64, K=1024, y=4 * A, q=5 * A, s=6 * A, ws=0, wsb=0):
+        return lib.w8a8_linear_bf16(ptr(x), ptr(w), ptr(sw), b, N, K, ptr(y), ptr(q), ptr(s), ptr(ws), wsb, None)
+    assert call(x=0) == L.IQD_ERR_INVALID
+    assert call(K=1000) == L.IQD_ERR_INVALID                  # K % 16
+    assert call(K=131072) == L.IQD_ERR_RANGE
+    assert call(x=A + 8) == L.IQD_ERR_ALIGN                   # x needs 16 bytes
+    assert call(q=5 * A + 4) == L.IQD_ERR_ALIGN
+    assert call(y=A + 64) == L.IQD_ERR_INVALID                # y overlaps x
+    assert call(b=40, q=0) == L.IQD_ERR_WORKSPACE             # b > 16: separate quantization needs q space
+    ws = iqd.workspace_bytes(L.IQD_OP_W8A8_BF16, 40, 64, 1024, 1)
+    assert ws == 40 * 1024 + (40 * 4 + 15) // 16 * 16

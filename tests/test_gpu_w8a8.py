@@ -218,3 +218,87 @@ def test_qwen3_8b_layer_invariance_and_parity(iqd, li):
     assert_bits_equal(host_bits(y512), ref, f"{L.name} b=512 vs b=1")
     y512b = iqd.w8a8_linear(q, sa, w, sw)
     assert_bits_equal(host_bits(y512b), ref, f"{L.name} b=512 second run")
+
+
+# ----------------------------------------------------------------------------
+# w8a8_linear_bf16: quantization fused into the mat-vec (one kernel for b <= 16)
+# ----------------------------------------------------------------------------
+
+def _f32_bits_to_bf16(values):
+    """Exact bf16 bit patterns of values that bf16 represents exactly."""
+    a = np.asarray(values, np.float32)
+    bits = W.f32_to_bf16_bits(a)
+    assert np.array_equal(W.bf16_bits_to_f32(bits), a), "not exactly representable in bf16"
+    return bits
+
+
+def _edge_rows(K):
+    """Token rows aimed at the fused quantizer's two paths: exact ties of
+    x / s (the correctly rounded division decides), scales whose reciprocal
+    overflows (subnormal s), a zero row (s = 0), values near the bf16 top."""
+    rows = np.zeros((8, K), np.uint16)
+    # 1: s = 1 exactly (amax 127); ties k + 1/2 both signs
+    r = np.zeros(K, np.float32)
+    r[0] = 127.0
+    ties = np.array([0.5, 1.5, 2.5, 3.5, 62.5, 63.5, 125.5, 126.5], np.float32)
+    r[1:1 + 16] = np.concatenate([ties, -ties])
+    rows[1] = _f32_bits_to_bf16(r)
+    # 2: s = 2^-3 exactly (amax 15.875); ties on that grid
+    r = np.zeros(K, np.float32)
+    r[5] = -15.875
+    r[9:9 + 8] = (np.array([0.5, 1.5, 2.5, 7.5, 100.5, 101.5, -3.5, -4.5], np.float32) * 0.125)
+    rows[2] = _f32_bits_to_bf16(r)
+    # 3: amax = 2^-126: s is subnormal and 1 / s overflows
+    r = np.zeros(K, np.float32)
+    r[0] = 2.0 ** -126
+    r[1:6] = [2.0 ** -127, -2.0 ** -126, 2.0 ** -130, 3 * 2.0 ** -129, -2.0 ** -133]
+    rows[3] = _f32_bits_to_bf16(r)
+    # 4: amax the smallest subnormal bf16
+    rows[4, 7] = 0x0001
+    rows[4, 8] = 0x8001
+    # 5: near the top of bf16
+    r = np.zeros(K, np.float32)
+    r[0] = 3.0e38
+    r[1:4] = [-1.0e38, 2.5e37, 1.0]
+    rows[5, :] = W.f32_to_bf16_bits(r)
+    # 6, 7: N(0, 1) with 1 % outliers x 20
+    g = W.rng(K + 17)
+    rows[6:8] = W.normal_bf16(g, 2, K)
+    return rows  # row 0 stays all zero
+
+
+@pytest.mark.parametrize("N,K", [(256, 512), (130, 4112), (4100, 1040), (8200, 2064), (300, 12304), (6144, 4096)])
+def test_fused_bf16_matches_quantize_then_linear(iqd, N, K):
+    t = torch()
+    g = W.rng(N * 13 + K)
+    w = W.int8_weights(g, N, K)
+    s_w = W.log_uniform_scales(g, N)
+    x = np.concatenate([_edge_rows(K), W.normal_bf16(g, 32, K)])  # 40 token rows
+    oq, osa = oracle.quantize_token(x)
+    rows = np.unique(np.concatenate([sample_rows(N, 40, K), np.arange(max(0, N - 17), N)]))
+    oy = oracle.w8a8(oq, osa, w[rows], s_w[rows])
+    xd, wd, swd = dev(x), dev(w), dev(s_w)
+    for b in list(range(1, 17)) + [17, 40]:
+        for t0 in (0, 40 - b) if b < 40 else (0,):
+            q_out = t.empty((b, K), dtype=t.int8, device="cuda")
+            s_out = t.empty((b,), dtype=t.float32, device="cuda")
+            y = iqd.w8a8_linear_bf16(xd[t0:t0 + b], wd, swd, q_out=q_out, s_a_out=s_out)
+            assert_bits_equal(host_bits(y)[:, rows], oy[t0:t0 + b], f"N={N} K={K} b={b} t0={t0} y")
+            assert_bits_equal(host(q_out), oq[t0:t0 + b], f"N={N} K={K} b={b} t0={t0} q")
+            assert_bits_equal(host(s_out).view(np.uint32), osa[t0:t0 + b].view(np.uint32), f"N={N} K={K} b={b} s")
+        # without the optional outputs (the fallback path then uses the workspace)
+        y2 = iqd.w8a8_linear_bf16(xd[:b], wd, swd)
+        assert_bits_equal(host_bits(y2)[:, rows], oy[:b], f"N={N} K={K} b={b} no outputs")
+
+
+def test_fused_bf16_qwen3_8b_layers_equal_unfused(iqd):
+    """Every Qwen3-8B decode layer at b = 1..8: the fused call equals
+    quantize_activations + w8a8_linear on all outputs."""
+    for li in range(4):
+        L = W.qwen3_8b_layer(li, tokens=8)
+        xd, wd, swd = dev(L.x), dev(L.w), dev(L.s_w)
+        q, sa = iqd.quantize_activations(xd)
+        for b in range(1, 9):
+            ref = iqd.w8a8_linear(q[:b], sa[:b], wd, swd)
+            y = iqd.w8a8_linear_bf16(xd[:b], wd, swd)
+            assert_bits_equal(host_bits(y), host_bits(ref), f"{L.name} b={b}")
