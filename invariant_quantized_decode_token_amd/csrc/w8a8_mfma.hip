@@ -18,10 +18,13 @@
 // v_mfma_i32_16x16x64_i8 accumulators.  K advances BK bytes per stage; both
 // operand tiles are staged in LDS (rows padded by 16 bytes, so that the 16
 // rows a fragment read touches fall on distinct banks), double-buffered per
-// group, with two stages of global loads in flight ahead of the stage being
-// multiplied.  The groups' partial tiles are added through LDS at the end
-// (exact int32).  At b = 512 the kernel is bound by load latency: more K
-// groups keep more bytes in flight per CU.
+// group, and a ring of R register sets keeps the global loads of R - 1
+// stages in flight.  The groups' partial tiles are added through LDS at the
+// end (exact int32), and the bf16 tile leaves through LDS as 16-byte stores.
+// Measured on MI355X (per-stage timestamps and kernels with parts removed):
+// a stage costs its barrier, its global loads, its LDS traffic and its
+// matrix-core work nearly one after the other, so overlap comes from a
+// second workgroup on the CU rather than from a deeper ring.
 // Tiles are mapped to workgroups XCD by XCD so that the M tiles sharing a
 // weight tile run on one XCD and reuse it from its L2.
 // Operand layout of the instruction (checked on MI355X): lane l holds 16
@@ -47,7 +50,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t
 template <int BK>
 constexpr int row_pad() { return BK + 16; }
 
-template <int BM, int BK, int KG>
+// Row stride (elements) of the bf16 output tile staged in LDS: 16-byte
+// aligned rows, and rows four apart fall 16 banks apart for the 2-byte
+// writes of the epilogue.
+constexpr int out_stride() { return kBN + 8; }
+
+template <int BM, int BK, int KG, int R>
 __global__ __launch_bounds__(KG * kGroupThreads) void k_w8a8_mfma(const int8_t *__restrict__ q,
                                                                   const float *__restrict__ s_a,
                                                                   const int8_t *__restrict__ w,
@@ -98,26 +106,33 @@ __global__ __launch_bounds__(KG * kGroupThreads) void k_w8a8_mfma(const int8_t *
     // is redirected out of range, so it reads zeros.
     const __amdgpu_buffer_rsrc_t ra = rsrc(q, static_cast<int64_t>(M) * K);
     const __amdgpu_buffer_rsrc_t rb = rsrc(w, static_cast<int64_t>(N) * K);
+    // Piece p of a thread is an activation piece for p < A_PIECES / 256 and a
+    // weight piece after that, the same for every lane: no lane-dependent
+    // branch surrounds a load (such branches make the compiler wait for all
+    // loads in flight before the next LDS store).
+    static_assert(A_PIECES % kGroupThreads == 0, "whole activation pieces per thread");
     auto gload = [&](int st, v4i(&regs)[PIECES]) __attribute__((always_inline)) {
 #pragma unroll
         for (int p = 0; p < PIECES; ++p) {
-            const int id = tid + p * kGroupThreads;
-            const bool is_a = id < A_PIECES;
-            const int j = is_a ? id : id - A_PIECES;
+            constexpr int AP = A_PIECES / kGroupThreads;
+            const bool is_a = p < AP;
+            const int j = tid + (is_a ? p : p - AP) * kGroupThreads;
             const int k = (st * KG + kg) * kBK + (j % CPR) * 16;
             const int row = (is_a ? m0 : n0) + j / CPR;
-            int off = row * K + k;
-            if (k >= K || row >= (is_a ? M : N)) off = 0x7FFFFFF0;
-            regs[p] = is_a ? __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0)
-                           : __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 2);
+            const bool in = k < K && row < (is_a ? M : N);
+            const int off = in ? row * K + k : 0x7FFFFFF0;
+            if (is_a)
+                regs[p] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+            else
+                regs[p] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 2);
         }
     };
     auto lstore = [&](int buf, const v4i(&regs)[PIECES]) __attribute__((always_inline)) {
 #pragma unroll
         for (int p = 0; p < PIECES; ++p) {
-            const int id = tid + p * kGroupThreads;
-            const bool is_a = id < A_PIECES;
-            const int j = is_a ? id : id - A_PIECES;
+            constexpr int AP = A_PIECES / kGroupThreads;
+            const bool is_a = p < AP;
+            const int j = tid + (is_a ? p : p - AP) * kGroupThreads;
             const int row = (is_a ? 0 : BM) + j / CPR;
             *reinterpret_cast<v4i *>(&lds[buf * STAGE + row * kRowPad + (j % CPR) * 16]) = regs[p];
         }
@@ -129,44 +144,64 @@ __global__ __launch_bounds__(KG * kGroupThreads) void k_w8a8_mfma(const int8_t *
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-    // Two stages of global loads in flight ahead of the one being computed.
-    v4i r0[PIECES], r1[PIECES];
-    gload(0, r0);
-    if (nst > 1) gload(1, r1);
-    lstore(0, r0);
+    // A ring of R register sets holds the global loads of the next R - 1
+    // stages while one stage is multiplied out of LDS.  Loads of stages past
+    // K read zeros (their buffer offsets are out of range), so no branch
+    // guards a load.
+    v4i ring[R][PIECES];
+#pragma unroll
+    for (int d = 0; d < R; ++d) gload(d, ring[d]);
+    lstore(0, ring[0]);
     __syncthreads();
     const int fr = lane & 15;         // fragment row (A) / column (B)
     const int fk = (lane >> 4) * 16;  // K byte offset of this lane's 16 bytes within 64
-    auto stage = [&](int st, v4i(&next)[PIECES], v4i(&cur_in)[PIECES]) __attribute__((always_inline)) {
-        const int buf = st & 1;
-        if (st + 1 < nst) lstore(buf ^ 1, cur_in);          // stage st+1, loaded one stage ago
-        if (st + 2 < nst) gload(st + 2, next);               // stage st+2 into the registers just freed
-        const int8_t *base = lds + buf * STAGE;
+    for (int st0 = 0; st0 < nst; st0 += R) {
 #pragma unroll
-        for (int kk = 0; kk < kBK / 64; ++kk) {
-            v4i af[FM], bfr[FN];
+        for (int d = 0; d < R; ++d) {
+            const int st = st0 + d;
+            if (st >= nst) break;  // uniform: the last round may be short
+            lstore((st + 1) & 1, ring[(d + 1) % R]);  // stage st + 1, loaded R - 1 stages ago
+            gload(st + R, ring[d]);                  // stage st + R into the set stage st used
+            const int8_t *base = lds + (st & 1) * STAGE;
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const v4i *>(base + (wm * WM + i * 16 + fr) * kRowPad + kk * 64 + fk);
+            for (int kk = 0; kk < kBK / 64; ++kk) {
+                v4i af[FM], bfr[FN];
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                bfr[j] = *reinterpret_cast<const v4i *>(base + (BM + wn * 64 + j * 16 + fr) * kRowPad + kk * 64 + fk);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
+                for (int i = 0; i < FM; ++i)
+                    af[i] = *reinterpret_cast<const v4i *>(base + (wm * WM + i * 16 + fr) * kRowPad + kk * 64 + fk);
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    bfr[j] = *reinterpret_cast<const v4i *>(base + (BM + wn * 64 + j * 16 + fr) * kRowPad + kk * 64 + fk);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            }
+            __syncthreads();
         }
-        __syncthreads();
-    };
-    // r0 is free after stage 0's store; stage st stores st+1 from the other set.
-    for (int st = 0; st < nst; st += 2) {
-        stage(st, r0, r1);
-        if (st + 1 < nst) stage(st + 1, r1, r0);
     }
 
+    // Scales of the tile, loaded before the first store: one counter tracks
+    // both loads and stores, so a load issued after stores would wait for
+    // them to complete.  Lane l, register r of fragment (i, j) is token
+    // m0 + wm*WM + 16 i + 4 (l / 16) + r and weight row n0 + 64 wn + 16 j + l % 16.
+    float sw[FN], sa[FM][4];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int n = n0 + wn * 64 + j * 16 + fr;
+        sw[j] = n < N ? s_w[n] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = m0 + wm * WM + i * 16 + (lane >> 4) * 4 + r;
+            sa[i][r] = m < M ? s_a[m] : 0.0f;
+        }
+
     // The other K groups hand their partial tiles to group 0 through LDS
-    // (their stage buffers are free after the loop's last barrier).
+    // (the stage buffers are free after the loop's last barrier).
     if constexpr (KG > 1) {
         v4i *xch = reinterpret_cast<v4i *>(lds_all);  // [KG - 1][4 waves][FM * FN][64 lanes]
         if (kg > 0) {
@@ -177,48 +212,66 @@ __global__ __launch_bounds__(KG * kGroupThreads) void k_w8a8_mfma(const int8_t *
                     xch[(((kg - 1) * 4 + wave) * FM * FN + i * FN + j) * kWave + lane] = acc[i][j];
         }
         __syncthreads();
-        if (kg > 0) return;
+        if (kg == 0) {
 #pragma unroll
-        for (int g = 1; g < KG; ++g)
+            for (int g = 1; g < KG; ++g)
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] += xch[(((g - 1) * 4 + wave) * FM * FN + i * FN + j) * kWave + lane];
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] += xch[(((g - 1) * 4 + wave) * FM * FN + i * FN + j) * kWave + lane];
+        }
+        __syncthreads();  // the exchange is read before the output tile reuses its space
     }
 
-    // Epilogue: lane l, register r of fragment (i, j) is token
-    // m0 + wm*WM + 16 i + 4 (l / 16) + r and weight row n0 + 64 wn + 16 j + l % 16.
+    // Epilogue into a bf16 tile in LDS, then stores of 16 contiguous bytes
+    // (8 outputs of one token) by every thread of the workgroup.
+    constexpr int OTS = out_stride();
+    uint16_t *ot = reinterpret_cast<uint16_t *>(lds_all);  // [BM][OTS]
+    if (kg == 0) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int n = n0 + wn * 64 + j * 16 + fr;
-        if (n >= N) continue;
-        const float sw = s_w[n];
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + wm * WM + i * 16 + (lane >> 4) * 4 + r;
-                if (m < M) y[static_cast<int64_t>(m) * N + n] = w8a8_epilogue(acc[i][j][r], s_a[m], sw);
-            }
+                for (int r = 0; r < 4; ++r)
+                    ot[(wm * WM + i * 16 + (lane >> 4) * 4 + r) * OTS + wn * 64 + j * 16 + fr] =
+                        w8a8_epilogue(acc[i][j][r], sa[i][r], sw[j]);
+    }
+    __syncthreads();
+    constexpr int PPR = kBN / 8;  // 16-byte pieces per tile row
+    for (int p = static_cast<int>(threadIdx.x); p < BM * PPR; p += KG * kGroupThreads) {
+        const int row = p / PPR, c = (p % PPR) * 8;
+        const int m = m0 + row, n = n0 + c;
+        if (m >= M || n >= N) continue;
+        const v4i v = *reinterpret_cast<const v4i *>(&ot[row * OTS + c]);
+        uint16_t *dst = y + static_cast<int64_t>(m) * N + n;
+        if ((N & 7) == 0) {  // n + 8 <= N and the row start is 16-byte aligned
+            *reinterpret_cast<v4i *>(dst) = v;
+        } else {
+            uint16_t e[8];
+            __builtin_memcpy(e, &v, sizeof(e));
+            for (int t = 0; t < 8 && n + t < N; ++t) dst[t] = e[t];
         }
     }
 }
 
-template <int BM, int BK, int KG>
+template <int BM, int BK, int KG, int R>
 hipError_t launch_tiles(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int b, int N, int K,
                         uint16_t *y, hipStream_t st) {
     constexpr int WM = BM / 2, FM = WM / 16, FN = 4;
     const size_t stages = static_cast<size_t>(KG) * 2 * (BM + kBN) * row_pad<BK>();
     const size_t xch = static_cast<size_t>(KG - 1) * 4 * FM * FN * kWave * 16;
-    const size_t smem = stages > xch ? stages : xch;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w8a8_mfma<BM, BK, KG>),
+    const size_t otile = static_cast<size_t>(BM) * out_stride() * 2;
+    size_t smem = stages > xch ? stages : xch;
+    if (otile > smem) smem = otile;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w8a8_mfma<BM, BK, KG, R>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     if (e != hipSuccess) return e;
     const int mt = (b + BM - 1) / BM;
     const int nt = (N + kBN - 1) / kBN;
     const int nt_pad = (nt + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((k_w8a8_mfma<BM, BK, KG>), dim3(mt * nt_pad), dim3(KG * kGroupThreads), smem, st, q, s_a, w,
+    hipLaunchKernelGGL((k_w8a8_mfma<BM, BK, KG, R>), dim3(mt * nt_pad), dim3(KG * kGroupThreads), smem, st, q, s_a, w,
                        s_w, b, N, K, y);
     return hipGetLastError();
 }
@@ -238,16 +291,15 @@ hipError_t launch_w8a8_mfma(const int8_t *q, const float *s_a, const int8_t *w, 
         }
         return hipSuccess;
     }
-    // Two K groups per workgroup (8 waves) keep twice the loads in flight
-    // per CU; the tile shape follows the tile count (measured at b = 512 on
-    // the Qwen3-8B layers, against 1 or 4 groups, 32- to 128-token tiles and
-    // 64- or 128-byte stages): up to one 64 x 128 tile per CU, 128-byte
-    // stages; up to two, 64-byte stages; past that, 128 x 128 tiles.
+    // Tile choice, measured at b = 512 on the Qwen3-8B layers against 32- to
+    // 128-token tiles, 64- or 128-byte stages, 1, 2 or 4 K groups and ring
+    // depths 2 to 8: while the 64 x 128 tiles fit one per CU, two K groups
+    // (8 waves) share each tile; past that, 128 x 128 tiles with one K
+    // group, two workgroups per CU, whose barriers do not wait for each other.
     const int64_t tiles = static_cast<int64_t>((b + 63) / 64) * ((N + kBN - 1) / kBN);
     const int cus = device_info().cus;
-    if (tiles <= cus) return launch_tiles<64, 128, 2>(q, s_a, w, s_w, b, N, K, y, st);
-    if (tiles <= 2 * cus) return launch_tiles<64, 64, 2>(q, s_a, w, s_w, b, N, K, y, st);
-    return launch_tiles<128, 64, 2>(q, s_a, w, s_w, b, N, K, y, st);
+    if (tiles <= cus) return launch_tiles<64, 128, 2, 4>(q, s_a, w, s_w, b, N, K, y, st);
+    return launch_tiles<128, 128, 1, 3>(q, s_a, w, s_w, b, N, K, y, st);
 }
 
 }  // namespace iqd
