@@ -24,6 +24,11 @@
 // stack (the same tree, built left to right), the waves of a workgroup own
 // aligned sub-ranges of chunks and fold them in tree order, and API splits
 // own aligned subtrees folded by k_blockq8_combine.
+// A wave takes RS rows at once, so that each activation load serves RS
+// weight rows, and issues the loads of U chunks before it uses any; loads of
+// blocks past m read zeros from out-of-range buffer offsets, so no branch
+// surrounds a load (such branches make the compiler wait for every load in
+// flight).
 // Leaves of blocks in [m, L) are +0 (the canonical padding).  When L < 32
 // the chunk has lanes beyond the tree; their leaves are -0, the exact
 // identity of binary32 addition, so they do not disturb the root.
@@ -36,6 +41,12 @@ namespace {
 constexpr int kBqWaves = 4;
 constexpr int kBqThreads = kBqWaves * kWave;
 constexpr int kMaxLevels = 8;  // chunk-slot tree depth: K <= 131071 -> at most 128 slots
+constexpr int kBqOob = 0x7FFFFFF0;  // a buffer offset past every range: the load returns zeros
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int64_t bytes) {
+    const int nr = bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : static_cast<int>(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, nr, 0x00020000);
+}
 
 struct BqArgs {
     const int8_t *q;
@@ -77,11 +88,11 @@ struct AddF {
     __device__ float operator()(float a, float b) const { return a + b; }
 };
 
-template <int B, int RS>
+template <int B, int RS, int U>
 __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
     __shared__ float red[kBqWaves][kWave];
     const int lane = lane_id();
-    const int wave = static_cast<int>(threadIdx.x) / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int s = blockIdx.y;
     const int K = a.K, N = a.N, m = a.m, L = a.L;
     const int ks = a.ks;
@@ -97,69 +108,96 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
     constexpr int NP = pow2_ceil(NV);
     constexpr int NPH = NP >= 2 ? NP / 2 : 1;
 
+    // Activations and their scales: one buffer for all tokens (b * K < 2^31).
+    const __amdgpu_buffer_rsrc_t qr = buf_rsrc(a.q, static_cast<int64_t>(B) * K);
+    const __amdgpu_buffer_rsrc_t dar = buf_rsrc(a.d_a, static_cast<int64_t>(B) * m * 4);
+
     for (int step = blockIdx.x; step < a.nsteps; step += gridDim.x) {
         const int row0 = (step * rgs + rg) * RS;
-        int rows[RS];
+        // Weights and block scales of the RS rows from buffers based at the
+        // first row (offsets stay below 2 * K whatever N is); rows past N
+        // re-read the last row and their results are dropped.
+        const int rfirst = min(row0, N - 1);
+        const int rlast = min(row0 + RS - 1, N - 1);
+        const int nrows = rlast - rfirst + 1;
+        const __amdgpu_buffer_rsrc_t wr = buf_rsrc(a.w + static_cast<int64_t>(rfirst) * K, static_cast<int64_t>(nrows) * K);
+        const __amdgpu_buffer_rsrc_t dwr =
+            buf_rsrc(a.d_w + static_cast<int64_t>(rfirst) * m, static_cast<int64_t>(nrows) * m * 2);
+        int roff[RS];
 #pragma unroll
-        for (int r = 0; r < RS; ++r) rows[r] = min(row0 + r, N - 1);
+        for (int r = 0; r < RS; ++r) roff[r] = min(row0 + r, N - 1) - rfirst;
         float stk[kMaxLevels];
 #pragma unroll
         for (int l = 0; l < kMaxLevels; ++l) stk[l] = 0.0f;
         float root = 0.0f;
-        for (int i = 0; i < nsw; ++i) {
-            const int slot = slot0 + i;
-            const int j = slot * 32 + (lane >> 1);  // this lane's block
-            float cr;
-            if (slot * 32 < m) {
-                const bool live = j < m;
-                const int64_t kb = static_cast<int64_t>(j) * 32 + 16 * half;
-                int32_t isum[NP];
+        for (int i0 = 0; i0 < nsw; i0 += U) {
+            // All loads of U slots go out before any is used, and no branch
+            // surrounds them: blocks past m (or slots past the wave's range)
+            // read zeros from out-of-range offsets.
+            v4i wv[U][RS], av[U][B];
+            uint32_t dwb[U][RS];
+            float dav[U][B];
 #pragma unroll
-                for (int v = 0; v < NP; ++v) isum[v] = 0;
-                v4i wv[RS];
+            for (int u = 0; u < U; ++u) {
+                const int j = (slot0 + i0 + u) * 32 + (lane >> 1);  // this lane's block
+                const bool live = i0 + u < nsw && j < m;
+                const int kb = j * 32 + 16 * half;
 #pragma unroll
-                for (int r = 0; r < RS; ++r)
-                    wv[r] = live ? load_stream16(a.w + static_cast<int64_t>(rows[r]) * K + kb)
-                                 : zero16();
-                float dwv[RS];
-#pragma unroll
-                for (int r = 0; r < RS; ++r)
-                    dwv[r] = live ? fp16_to_f32(a.d_w[static_cast<int64_t>(rows[r]) * m + j]) : 0.0f;
-                float dav[B];
+                for (int r = 0; r < RS; ++r) {
+                    wv[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wr, live ? roff[r] * K + kb : kBqOob, 0, 2);
+                    dwb[u][r] = __builtin_amdgcn_raw_buffer_load_b16(dwr, live ? 2 * (roff[r] * m + j) : kBqOob, 0, 0);
+                }
 #pragma unroll
                 for (int t = 0; t < B; ++t) {
-                    const v4i av = live ? load16(a.q + static_cast<int64_t>(t) * K + kb) : zero16();
-                    dav[t] = live ? a.d_a[static_cast<int64_t>(t) * m + j] : 0.0f;
-#pragma unroll
-                    for (int r = 0; r < RS; ++r) isum[r * B + t] = dot16(wv[r], av, isum[r * B + t]);
+                    av[u][t] = __builtin_amdgcn_raw_buffer_load_b128(qr, live ? t * K + kb : kBqOob, 0, 0);
+                    dav[u][t] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(dar, live ? 4 * (t * m + j) : kBqOob, 0, 0));
                 }
-                // tree level 0 -> block sums: integer reduce-scatter over the lane pair
-                float leaf[NPH];
-                if constexpr (NP >= 2) {
-                    rs_step<1, NP>(isum, lane, AddI());
-#pragma unroll
-                    for (int v = 0; v < NPH; ++v) {
-                        const int vlo = v, vhi = v + NPH;
-                        const float da_lo = vlo < NV ? dav[vlo % B] : 0.0f;
-                        const float dw_lo = vlo < NV ? dwv[vlo / B] : 0.0f;
-                        const float da_hi = vhi < NV ? dav[vhi % B] : 0.0f;
-                        const float dw_hi = vhi < NV ? dwv[vhi / B] : 0.0f;
-                        const float da = sel(half != 0, da_hi, da_lo);
-                        const float dw = sel(half != 0, dw_hi, dw_lo);
-                        const float p = (static_cast<float>(isum[v]) * da) * dw;
-                        leaf[v] = live ? p : (j < L ? 0.0f : -0.0f);
-                    }
-                } else {
-                    const int32_t tot = isum[0] + xor_lane<1>(isum[0]);
-                    const float p = (static_cast<float>(tot) * dav[0]) * dwv[0];
-                    leaf[0] = live ? p : (j < L ? 0.0f : -0.0f);
-                }
-                // tree levels 1..5 inside the chunk: lane masks 2..32
-                cr = rs_chain<2, NPH>(leaf, lane, AddF());
-            } else {
-                cr = 0.0f;  // a slot made only of padding leaves
             }
-            root = carry_insert(stk, i, cr);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int slot = slot0 + i0 + u;
+                if (i0 + u >= nsw) break;  // uniform: past the wave's slots
+                const int j = slot * 32 + (lane >> 1);
+                const bool live = j < m;  // blocks in [m, L) are +0 leaves, beyond L -0 (a slot of padding gives +0)
+                float cr = 0.0f;          // a slot made only of padding leaves
+                if (slot * 32 < m) {      // uniform
+                    int32_t isum[NP];
+#pragma unroll
+                    for (int v = 0; v < NP; ++v) isum[v] = 0;
+#pragma unroll
+                    for (int t = 0; t < B; ++t)
+#pragma unroll
+                        for (int r = 0; r < RS; ++r) isum[r * B + t] = dot16(wv[u][r], av[u][t], isum[r * B + t]);
+                    float dwv[RS];
+#pragma unroll
+                    for (int r = 0; r < RS; ++r) dwv[r] = fp16_to_f32(static_cast<uint16_t>(dwb[u][r]));
+                    // tree level 0 -> block sums: integer reduce-scatter over the lane pair
+                    float leaf[NPH];
+                    if constexpr (NP >= 2) {
+                        rs_step<1, NP>(isum, lane, AddI());
+#pragma unroll
+                        for (int v = 0; v < NPH; ++v) {
+                            const int vlo = v, vhi = v + NPH;
+                            const float da_lo = vlo < NV ? dav[u][vlo % B] : 0.0f;
+                            const float dw_lo = vlo < NV ? dwv[vlo / B] : 0.0f;
+                            const float da_hi = vhi < NV ? dav[u][vhi % B] : 0.0f;
+                            const float dw_hi = vhi < NV ? dwv[vhi / B] : 0.0f;
+                            const float da = sel(half != 0, da_hi, da_lo);
+                            const float dw = sel(half != 0, dw_hi, dw_lo);
+                            const float p = (static_cast<float>(isum[v]) * da) * dw;
+                            leaf[v] = live ? p : (j < L ? 0.0f : -0.0f);
+                        }
+                    } else {
+                        const int32_t tot = isum[0] + xor_lane<1>(isum[0]);
+                        const float p = (static_cast<float>(tot) * dav[u][0]) * dwv[0];
+                        leaf[0] = live ? p : (j < L ? 0.0f : -0.0f);
+                    }
+                    // tree levels 1..5 inside the chunk: lane masks 2..32
+                    cr = rs_chain<2, NPH>(leaf, lane, AddF());
+                }
+                root = carry_insert(stk, i0 + u, cr);
+            }
         }
         if (ks > 1) {
             red[wave][lane] = root;
@@ -202,9 +240,18 @@ __global__ __launch_bounds__(256) void k_blockq8_combine(const float *__restrict
     y[i] = bf16_rne(root);
 }
 
+template <int B, int RS, int U>
+hipError_t launch_rs(const BqArgs &a, int grid, hipStream_t st) {
+    hipLaunchKernelGGL((k_blockq8_matvec<B, RS, U>), dim3(grid, a.split), dim3(kBqThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+// Four rows per wave: each activation load serves four weight rows (measured
+// on MI355X at 4096 -> 4096 and 12288 -> 4096 against 1, 2 and 8 rows).  At
+// b = 1 a wave with at least four slots keeps two slots of loads in flight.
 template <int B>
 hipError_t launch_b(const BqArgs &base, hipStream_t st) {
-    constexpr int RS = B <= 8 ? 2 : 1;
+    constexpr int RS = 4;
     BqArgs a = base;
     const int row_groups = (a.N + RS - 1) / RS;
     const int target = device_info().cus * 16;
@@ -216,8 +263,10 @@ hipError_t launch_b(const BqArgs &base, hipStream_t st) {
     a.nsteps = (a.N + rows_per_step - 1) / rows_per_step;
     int grid = device_info().cus * 8;
     if (grid > a.nsteps) grid = a.nsteps;
-    hipLaunchKernelGGL((k_blockq8_matvec<B, RS>), dim3(grid, a.split), dim3(kBqThreads), 0, st, a);
-    return hipGetLastError();
+    if constexpr (B == 1) {
+        if (nss / ks >= 4) return launch_rs<B, RS, 2>(a, grid, st);
+    }
+    return launch_rs<B, RS, 1>(a, grid, st);
 }
 
 }  // namespace
@@ -226,10 +275,10 @@ hipError_t launch_blockq8_matvec(const int8_t *q, const float *d_a, const int8_t
                                  const uint16_t *d_w, int b, int N, int K, uint16_t *y, int split,
                                  float *part, hipStream_t st) {
     // The matrix-core kernel forms the leaves of all 16 token columns of its
-    // instruction whatever b is, so its cost is flat in b, while this
-    // kernel's grows with b; measured on MI355X (4096 -> 4096 and
-    // 12288 -> 4096), the crossover is near b * K = 9 * 4096.
-    if (static_cast<int64_t>(b) * K >= 9 * 4096 && blockq8_mfvec_fits(b, N, K, split))
+    // instruction whatever b is, so its cost is flat in b; measured on MI355X
+    // (4096 -> 4096 and 12288 -> 4096) it is ahead of this kernel only from
+    // b = 9 on, where its activations fit in LDS.
+    if (b >= 9 && blockq8_mfvec_fits(b, N, K, split))
         return launch_blockq8_mfvec(q, d_a, w, d_w, b, N, K, y, split, part, st);
     const int m = K / 32;
     int L = 1;

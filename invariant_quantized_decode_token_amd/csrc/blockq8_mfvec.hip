@@ -146,28 +146,32 @@ __global__ __launch_bounds__(NW * kWave) void k_blockq8_mfvec(Bq8Args a) {
         const int ui = unit_of(c, u);
         return ui < units && blk0 + ui * kUnitBlocks < m;
     };
+    // No branch surrounds a load (such branches make the compiler wait for
+    // every load in flight before the data are used): a dead unit, or a chunk
+    // past the wave's last one (its tile lies past the last row), reads zeros
+    // from out-of-range buffer offsets and is never used.
     auto load_chunk = [&](int c) __attribute__((always_inline)) {
         QChunk<U> ch;
         const int tile = tile_of(c);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (unit_live(c, u)) {  // uniform: dead units load nothing
-                const int ublk = blk0 + unit_of(c, u) * kUnitBlocks;
-                const int k = 32 * ublk + lcol;
+            const bool live = unit_live(c, u);  // uniform
+            const int ublk = blk0 + unit_of(c, u) * kUnitBlocks;
+            const int k = 32 * ublk + lcol;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = tile * kTileRows + 4 * i + lrow;
-                    const unsigned lin = static_cast<unsigned>(row) * static_cast<unsigned>(K) + static_cast<unsigned>(k);
-                    const int off = (row < N && k < K) ? static_cast<int>(lin) : kOob;
-                    ch.w[u][i] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2);  // nt: read once
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int row = tile * kTileRows + 4 * i + lrow;
+                const unsigned lin = static_cast<unsigned>(row) * static_cast<unsigned>(K) + static_cast<unsigned>(k);
+                const int off = (live && row < N && k < K) ? static_cast<int>(lin) : kOob;
+                ch.w[u][i] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2);  // nt: read once
+            }
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int v = 64 * h + lane;
-                    const int row = tile * kTileRows + (v >> 3), blk = ublk + (v & 7);
-                    const int off = (row < N && blk < m) ? 2 * (row * m + blk) : kOob;
-                    ch.dw[u][h] = __builtin_amdgcn_raw_buffer_load_b16(dwr, off, 0, 0);
-                }
+            for (int h = 0; h < 2; ++h) {
+                const int v = 64 * h + lane;
+                const int row = tile * kTileRows + (v >> 3), blk = ublk + (v & 7);
+                const unsigned dl = 2u * (static_cast<unsigned>(row) * static_cast<unsigned>(m) + static_cast<unsigned>(blk));
+                const int off = (live && row < N && blk < m) ? static_cast<int>(dl) : kOob;
+                ch.dw[u][h] = __builtin_amdgcn_raw_buffer_load_b16(dwr, off, 0, 0);
             }
         }
         return ch;
@@ -190,8 +194,7 @@ __global__ __launch_bounds__(NW * kWave) void k_blockq8_mfvec(Bq8Args a) {
     }
     QChunk<U> ring[D];
 #pragma unroll
-    for (int i = 0; i < D - 1; ++i)
-        if (i < total) ring[i] = load_chunk(i);
+    for (int i = 0; i < D - 1; ++i) ring[i] = load_chunk(i);
     auto put = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < XB; ++j) {
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(NW * kWave) void k_blockq8_mfvec(Bq8Args a) {
         for (int i = 0; i < D; ++i) {
             const int c = c0 + i;
             if (c >= total) break;
-            if (c + D - 1 < total) ring[(i + D - 1) % D] = load_chunk(c + D - 1);
+            ring[(i + D - 1) % D] = load_chunk(c + D - 1);  // past the end: zeros, unused
             // The U units of a chunk are an aligned subtree (U divides the
             // slice, or the slice is one unit): their roots fold pairwise and
             // the chunk root goes into the carry stack.

@@ -102,7 +102,7 @@ def test_blockq8_config_invariance_and_parity(iqd, li):
 
 
 # ----------------------------------------------------------------------------
-# the matrix-core kernel (taken from b * K >= 9 * 4096 on): ragged K and N,
+# the matrix-core kernel (taken from b = 9 on where its LDS fits): ragged K and N,
 # padding-only waves, -0 padding and tree witnesses on that path
 # ----------------------------------------------------------------------------
 
@@ -121,7 +121,9 @@ def test_matrix_core_path_ragged(iqd, K):
         assert_bits_equal(host_bits(y), oy, f"K={K} b=16 split={split}")
 
 
-@pytest.mark.parametrize("K,b", [(4096, 9), (12288, 4)])
+# (4096, 9) and (6176, 9) take the matrix-core kernel (b >= 9, activations in
+# LDS; 6176 pads 193 blocks to a 256-leaf tree), (12288, 4) the lane-pair one.
+@pytest.mark.parametrize("K,b", [(4096, 9), (6176, 9), (12288, 4)])
 def test_matrix_core_path_padding_and_witnesses(iqd, K, b):
     q, d_a, w, d_w = W.negative_zero_operands(K, N=5, b=b)
     oy = oracle.blockq8(q, d_a, w, d_w)
