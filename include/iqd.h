@@ -124,11 +124,12 @@ int w8a8_linear(const int8_t *q, const float *s_a, const int8_t *w, const float 
  * call, from bf16 activations.
  *
  * The results are those of quantize_activations(x, group 0) followed by
- * w8a8_linear(split_k 1), bit for bit.  For one token (K <= 8192) one kernel
- * does both: every workgroup quantizes the activations it multiplies (the
- * reciprocal of the scale first, the correctly rounded division wherever the
- * quotient lies within 2^-14 of a rounding boundary), which removes the
- * separate quantization launch.  Wider passes run the two kernels.
+ * w8a8_linear(split_k 1), bit for bit.  For a few tokens (up to 2 or 4,
+ * depending on N and K) one kernel does both: every workgroup quantizes the
+ * activations it multiplies (the reciprocal of the scale first, the
+ * correctly rounded division wherever the quotient lies within 2^-14 of a
+ * rounding boundary) while its first weights are in flight, which removes
+ * the separate quantization launch.  Wider passes run the two kernels.
  *
  *   x_bf16   in  bf16 [b, K]                (16-byte aligned)
  *   w, s_w   as w8a8_linear

@@ -31,7 +31,7 @@ hipError_t launch_w8a8_mfvec(const int8_t *q, const float *s_a, const int8_t *w,
                              int K, uint16_t *y, hipStream_t st);
 // Quantization fused in: bf16 activations x [b, K] in; q_out [b, K] and
 // s_out [b] (both optional) receive the quantized activations.  Supported
-// where fused_ok() says so (one token, K <= 8192).
+// where fused_ok() says so (a few tokens: up to 2 or 4 by shape).
 bool w8a8_mfvec_fused_ok(int b, int N, int K);
 hipError_t launch_w8a8_mfvec_fused(const uint16_t *x, const int8_t *w, const float *s_w, int b, int N, int K,
                                    uint16_t *y, int8_t *q_out, float *s_out, hipStream_t st);

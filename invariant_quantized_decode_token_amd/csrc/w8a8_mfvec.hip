@@ -245,11 +245,24 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_mfvec(MfvArgs a) {
         // (16-byte vectors of 8 values), forms the per-token absmax through
         // LDS, and writes the int8 codes of all b tokens into its staging
         // area; workgroup 0 also writes them (and the scales) out if asked.
+        // The activations go out ahead of the weight prologue, so that the
+        // quantization runs while the first weight chunks are in flight.
         __shared__ uint32_t amx[16];
         __shared__ float ssc[16], src[16];
-        const int kvx = K / 8;
+        const int kvx = K / 8;  // vectors per token row
         const int nvx = a.b * kvx;
         const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, a.b * K * 2);
+        // Vector base + j * NTH + tid lies in token row t at position p; both
+        // advance by a constant per j, so one division per thread and batch
+        // serves every vector.
+        const int step_t = NTH / kvx, step_p = NTH - step_t * kvx;
+        auto advance = [&](int &t, int &p) __attribute__((always_inline)) {
+            p += step_p;
+            t += step_t;
+            const bool wrap = p >= kvx;
+            p = wrap ? p - kvx : p;
+            t = wrap ? t + 1 : t;
+        };
         auto load_x = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < XB; ++j) {
@@ -257,35 +270,49 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_mfvec(MfvArgs a) {
                 xa[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, v < nvx ? 16 * v : kOob, 0, 0);
             }
         };
-        if constexpr (WFIRST) ring[0] = load_chunk(0, true);
         load_x(0);
 #pragma unroll
-        for (int i = WFIRST ? 1 : 0; i < D - 1; ++i) ring[i] = load_chunk(i, true);
+        for (int i = 0; i < D - 1; ++i) ring[i] = load_chunk(i, true);
         if (tid < 16) amx[tid] = 0u;
         __syncthreads();
-        // The 64 consecutive vectors of a wave instruction span at most two
-        // tokens when a token row holds at least 64 of them: one wave maximum
-        // per token, one LDS atomic per wave.  Shorter rows: one atomic per
-        // lane.  (|x| >= 0, so float bits order as the values.)
+        // When a token row is a whole number of 64-vector spans, the 64 vectors
+        // of a wave instruction share one token: one maximum per vector over
+        // the wave (lane exchanges, the XB reductions interleaved), one LDS
+        // atomic per wave.  Other rows: one atomic per lane.  (|x| >= 0, so
+        // float bits order as the values.)
         auto fold_max = [&](int base) __attribute__((always_inline)) {
+            const int v0 = base + tid;
+            int t = v0 / kvx, p = v0 - t * kvx;
+            float m[XB];
+            int tj[XB];
 #pragma unroll
             for (int j = 0; j < XB; ++j) {
-                const int v = base + j * NTH + tid;
-                const float m = v < nvx ? amax8(xa[j]) : 0.0f;
-                if (kvx >= kWave) {
-                    const int vw = __builtin_amdgcn_readfirstlane(v);  // lane 0's vector
-                    const int t0 = vw / kvx;
-                    const int t1 = min(t0 + 1, a.b - 1);
-                    const bool first = v / kvx == t0;
-                    const float m0 = wave_max(first ? m : 0.0f);
-                    const float m1 = wave_max(first ? 0.0f : m);
-                    if (lane == 0 && vw < nvx) {
-                        atomicMax(&amx[t0], __float_as_uint(m0));
-                        if (t1 != t0) atomicMax(&amx[t1], __float_as_uint(m1));
-                    }
-                } else if (v < nvx) {
-                    atomicMax(&amx[v / kvx], __float_as_uint(m));
+                m[j] = base + j * NTH + tid < nvx ? amax8(xa[j]) : 0.0f;
+                tj[j] = t;
+                advance(t, p);
+            }
+            if (kvx % kWave == 0) {
+#pragma unroll
+                for (int j = 0; j < XB; ++j) m[j] = fmaxf(m[j], xor_lane<1>(m[j]));
+#pragma unroll
+                for (int j = 0; j < XB; ++j) m[j] = fmaxf(m[j], xor_lane<2>(m[j]));
+#pragma unroll
+                for (int j = 0; j < XB; ++j) m[j] = fmaxf(m[j], xor_lane<4>(m[j]));
+#pragma unroll
+                for (int j = 0; j < XB; ++j) m[j] = fmaxf(m[j], xor_lane<8>(m[j]));
+#pragma unroll
+                for (int j = 0; j < XB; ++j) m[j] = fmaxf(m[j], xor_lane<16>(m[j]));
+#pragma unroll
+                for (int j = 0; j < XB; ++j) m[j] = fmaxf(m[j], xor_lane<32>(m[j]));
+                if (lane == 0) {
+#pragma unroll
+                    for (int j = 0; j < XB; ++j)
+                        if (base + j * NTH + tid < nvx) atomicMax(&amx[tj[j]], __float_as_uint(m[j]));
                 }
+            } else {
+#pragma unroll
+                for (int j = 0; j < XB; ++j)
+                    if (base + j * NTH + tid < nvx) atomicMax(&amx[tj[j]], __float_as_uint(m[j]));
             }
         };
         fold_max(0);
@@ -303,16 +330,18 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_mfvec(MfvArgs a) {
         __syncthreads();
         const bool out = bx == 0 && a.q_out != nullptr;
         auto put_q = [&](int base) __attribute__((always_inline)) {
+            const int v0 = base + tid;
+            int t = v0 / kvx, p = v0 - t * kvx;
 #pragma unroll
             for (int j = 0; j < XB; ++j) {
                 const int v = base + j * NTH + tid;
                 if (v < nvx) {
-                    const int t = v / kvx;
                     const float rc = src[t];
                     const uint2 q8 = quant8(xa[j], ssc[t], rc, __builtin_isfinite(rc));
-                    *reinterpret_cast<uint2 *>(xs + t * KP + 8 * (v - t * kvx)) = q8;
+                    *reinterpret_cast<uint2 *>(xs + t * KP + 8 * p) = q8;
                     if (out) *reinterpret_cast<uint2 *>(a.q_out + 8 * static_cast<int64_t>(v)) = q8;
                 }
+                advance(t, p);
             }
         };
         if (multi) {
@@ -407,11 +436,12 @@ template <int NW, int KS, int U, int D, bool WFIRST, bool FUSE>
 hipError_t launch_d(const MfvArgs &a, int grid, int smem, hipStream_t st) {
     const int vec_bytes = FUSE ? 8 : 16;  // K elements per 16-byte vector
     const int per_thread = (a.b * (a.K / vec_bytes) + NW * kWave - 1) / (NW * kWave);
-    if constexpr (FUSE) {  // taken for one token and K <= 8192 only
-        if (per_thread <= 1) return launch_x<NW, KS, U, D, 1, WFIRST, FUSE>(a, grid, smem, st);
-        if (per_thread <= 2) return launch_x<NW, KS, U, D, 2, WFIRST, FUSE>(a, grid, smem, st);
-        if (per_thread <= 4) return launch_x<NW, KS, U, D, 4, WFIRST, FUSE>(a, grid, smem, st);
-        return hipErrorInvalidValue;
+    if constexpr (FUSE) {  // the weights-first order does not apply: the activations always go first
+        if (per_thread <= 1) return launch_x<NW, KS, U, D, 1, false, FUSE>(a, grid, smem, st);
+        if (per_thread <= 2) return launch_x<NW, KS, U, D, 2, false, FUSE>(a, grid, smem, st);
+        if (per_thread <= 4) return launch_x<NW, KS, U, D, 4, false, FUSE>(a, grid, smem, st);
+        if (per_thread <= 8) return launch_x<NW, KS, U, D, 8, false, FUSE>(a, grid, smem, st);
+        return launch_x<NW, KS, U, D, 16, false, FUSE>(a, grid, smem, st);  // past 16: two batches, x read twice
     }
     if (per_thread <= 1) return launch_x<NW, KS, U, D, 1, WFIRST, FUSE>(a, grid, smem, st);
     if (per_thread <= 2) return launch_x<NW, KS, U, D, 2, WFIRST, FUSE>(a, grid, smem, st);
@@ -501,11 +531,28 @@ hipError_t launch_w8a8_mfvec(const int8_t *q, const float *s_a, const int8_t *w,
     return launch_pick<false>(pick(b, N, K), a, st);
 }
 
-// Every workgroup repeats the quantization of all b x K activations, so the
-// fused kernel pays only for one token: measured on MI355X against the
-// separate quantize kernel + mat-vec, it wins at b = 1 for K = 4096 and
-// loses from b = 2 on (at b = 8 it is 2-3x slower on the Qwen3-8B layers).
-bool w8a8_mfvec_fused_ok(int b, int N, int K) { return b == 1 && K <= 8192 && w8a8_mfvec_fits(b, N, K); }
+// Every workgroup repeats the quantization of all b x K activations, while
+// its first weight chunks are in flight; that pays while the work is small
+// next to the workgroup's weights.  Measured on MI355X on the Qwen3-8B layers
+// (fused call against the quantize kernel + mat-vec, b = 1..8): the fused
+// kernel wins up to b = 4 with one tile per 8-wave workgroup (N <= 4096,
+// K <= 8192) and with many tiles (N > 8192), up to b = 2 for K > 8192 and
+// for 257..512 tiles, and loses beyond (at b = 8 by 1.2-13 us).  Past eight
+// 16-byte vectors per thread the staging needs a second batch, which never
+// paid.
+bool w8a8_mfvec_fused_ok(int b, int N, int K) {
+    if (!w8a8_mfvec_fits(b, N, K)) return false;
+    const Pick p = pick(b, N, K);
+    const int threads = p.nw * kWave;
+    if (b * (K / 8) > 8 * threads) return false;
+    switch (p.id) {
+        case 0:
+        case 4: return b <= 4;
+        case 1:
+        case 2: return b <= 2;
+        default: return false;
+    }
+}
 
 hipError_t launch_w8a8_mfvec_fused(const uint16_t *x, const int8_t *w, const float *s_w, int b, int N, int K,
                                    uint16_t *y, int8_t *q_out, float *s_out, hipStream_t st) {
