@@ -12,9 +12,9 @@
 // mat-vec kernel": past a handful of tokens the stock path moved to a tiled
 // matmul with its own add order; here the integer sums make the order moot.
 //
-// Tiling: a workgroup computes a BM x 128 tile of y (BM tokens, 128 weight
+// Tiling: a workgroup computes a BM x BN tile of y (BM tokens, BN weight
 // rows) with KG groups of 4 waves; group g takes the K stages g, g + KG, ...
-// and its waves are 2 x 2, each owning a (BM/2) x 64 sub-tile of
+// and its waves are 2 x 2, each owning a (BM/2) x (BN/2) sub-tile of
 // v_mfma_i32_16x16x64_i8 accumulators.  K advances BK bytes per stage; both
 // operand tiles are staged in LDS (rows padded by 16 bytes, so that the 16
 // rows a fragment read touches fall on distinct banks), double-buffered per
@@ -36,7 +36,6 @@
 namespace iqd {
 namespace {
 
-constexpr int kBN = 128;
 constexpr int kGroupThreads = 256;  // one K group: 4 waves, 2 x 2 over the tile
 constexpr int kXcds = 8;      // workgroups are dealt round-robin to the 8 XCDs (L2 domains)
 
@@ -53,9 +52,10 @@ constexpr int row_pad() { return BK + 16; }
 // Row stride (elements) of the bf16 output tile staged in LDS: 16-byte
 // aligned rows, and rows four apart fall 16 banks apart for the 2-byte
 // writes of the epilogue.
-constexpr int out_stride() { return kBN + 8; }
+template <int BN>
+constexpr int out_stride() { return BN + 8; }
 
-template <int BM, int BK, int KG, int R>
+template <int BM, int BN, int BK, int KG, int R>
 __global__ __launch_bounds__(KG * kGroupThreads) void k_w8a8_mfma(const int8_t *__restrict__ q,
                                                                   const float *__restrict__ s_a,
                                                                   const int8_t *__restrict__ w,
@@ -63,29 +63,30 @@ __global__ __launch_bounds__(KG * kGroupThreads) void k_w8a8_mfma(const int8_t *
                                                                   uint16_t *__restrict__ y) {
     constexpr int WM = BM / 2;        // wave sub-tile rows (tokens)
     constexpr int FM = WM / 16;       // fragments along M per wave
-    constexpr int FN = 64 / 16;       // fragments along N per wave
+    constexpr int WN = BN / 2;        // wave sub-tile columns (weight rows)
+    constexpr int FN = WN / 16;       // fragments along N per wave
     constexpr int kBK = BK;
     constexpr int kRowPad = row_pad<BK>();
     constexpr int CPR = kBK / 16;     // 16-byte pieces per staged row
     constexpr int A_PIECES = BM * CPR;
-    constexpr int B_PIECES = kBN * CPR;
+    constexpr int B_PIECES = BN * CPR;
     constexpr int PIECES = (A_PIECES + B_PIECES) / kGroupThreads;
     static_assert((A_PIECES + B_PIECES) % kGroupThreads == 0, "whole pieces per thread");
-    extern __shared__ __attribute__((aligned(16))) int8_t lds_all[];  // [KG][2][(BM + kBN) * kRowPad]
-    constexpr int STAGE = (BM + kBN) * kRowPad;
+    extern __shared__ __attribute__((aligned(16))) int8_t lds_all[];  // [KG][2][(BM + BN) * kRowPad]
+    constexpr int STAGE = (BM + BN) * kRowPad;
 
     // Tile of this workgroup.  The M tiles of one N tile (which read the same
     // weight rows) are given consecutive slots of one XCD, so that the
     // weight tile is fetched into that XCD's L2 once and reused from there.
     const int mt = (M + BM - 1) / BM;
-    const int nt = (N + kBN - 1) / kBN;
+    const int nt = (N + BN - 1) / BN;
     const int L = blockIdx.x;
     const int xcd = L % kXcds, slot = L / kXcds;
     const int ntile = (slot / mt) * kXcds + xcd;
     const int mtile = slot % mt;
     if (ntile >= nt) return;  // padding slots of the last XCD round
     const int m0 = mtile * BM;
-    const int n0 = ntile * kBN;
+    const int n0 = ntile * BN;
 
     // K group kg takes the stages st = kg, kg + KG, ... of K; its 4 waves
     // split the tile 2 x 2.  The groups' partial tiles are added at the end
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(KG * kGroupThreads) void k_w8a8_mfma(const int8_t *
                     af[i] = *reinterpret_cast<const v4i *>(base + (wm * WM + i * 16 + fr) * kRowPad + kk * 64 + fk);
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    bfr[j] = *reinterpret_cast<const v4i *>(base + (BM + wn * 64 + j * 16 + fr) * kRowPad + kk * 64 + fk);
+                    bfr[j] = *reinterpret_cast<const v4i *>(base + (BM + wn * WN + j * 16 + fr) * kRowPad + kk * 64 + fk);
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(KG * kGroupThreads) void k_w8a8_mfma(const int8_t *
     float sw[FN], sa[FM][4];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-        const int n = n0 + wn * 64 + j * 16 + fr;
+        const int n = n0 + wn * WN + j * 16 + fr;
         sw[j] = n < N ? s_w[n] : 0.0f;
     }
 #pragma unroll
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(KG * kGroupThreads) void k_w8a8_mfma(const int8_t *
 
     // Epilogue into a bf16 tile in LDS, then stores of 16 contiguous bytes
     // (8 outputs of one token) by every thread of the workgroup.
-    constexpr int OTS = out_stride();
+    constexpr int OTS = out_stride<BN>();
     uint16_t *ot = reinterpret_cast<uint16_t *>(lds_all);  // [BM][OTS]
     if (kg == 0) {
 #pragma unroll
@@ -235,11 +236,11 @@ __global__ __launch_bounds__(KG * kGroupThreads) void k_w8a8_mfma(const int8_t *
             for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    ot[(wm * WM + i * 16 + (lane >> 4) * 4 + r) * OTS + wn * 64 + j * 16 + fr] =
+                    ot[(wm * WM + i * 16 + (lane >> 4) * 4 + r) * OTS + wn * WN + j * 16 + fr] =
                         w8a8_epilogue(acc[i][j][r], sa[i][r], sw[j]);
     }
     __syncthreads();
-    constexpr int PPR = kBN / 8;  // 16-byte pieces per tile row
+    constexpr int PPR = BN / 8;  // 16-byte pieces per tile row
     for (int p = static_cast<int>(threadIdx.x); p < BM * PPR; p += KG * kGroupThreads) {
         const int row = p / PPR, c = (p % PPR) * 8;
         const int m = m0 + row, n = n0 + c;
@@ -256,22 +257,22 @@ __global__ __launch_bounds__(KG * kGroupThreads) void k_w8a8_mfma(const int8_t *
     }
 }
 
-template <int BM, int BK, int KG, int R>
+template <int BM, int BN, int BK, int KG, int R>
 hipError_t launch_tiles(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int b, int N, int K,
                         uint16_t *y, hipStream_t st) {
-    constexpr int WM = BM / 2, FM = WM / 16, FN = 4;
-    const size_t stages = static_cast<size_t>(KG) * 2 * (BM + kBN) * row_pad<BK>();
+    constexpr int WM = BM / 2, FM = WM / 16, FN = BN / 32;
+    const size_t stages = static_cast<size_t>(KG) * 2 * (BM + BN) * row_pad<BK>();
     const size_t xch = static_cast<size_t>(KG - 1) * 4 * FM * FN * kWave * 16;
-    const size_t otile = static_cast<size_t>(BM) * out_stride() * 2;
+    const size_t otile = static_cast<size_t>(BM) * out_stride<BN>() * 2;
     size_t smem = stages > xch ? stages : xch;
     if (otile > smem) smem = otile;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w8a8_mfma<BM, BK, KG, R>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w8a8_mfma<BM, BN, BK, KG, R>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     if (e != hipSuccess) return e;
     const int mt = (b + BM - 1) / BM;
-    const int nt = (N + kBN - 1) / kBN;
+    const int nt = (N + BN - 1) / BN;
     const int nt_pad = (nt + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((k_w8a8_mfma<BM, BK, KG, R>), dim3(mt * nt_pad), dim3(KG * kGroupThreads), smem, st, q, s_a, w,
+    hipLaunchKernelGGL((k_w8a8_mfma<BM, BN, BK, KG, R>), dim3(mt * nt_pad), dim3(KG * kGroupThreads), smem, st, q, s_a, w,
                        s_w, b, N, K, y);
     return hipGetLastError();
 }
@@ -292,14 +293,18 @@ hipError_t launch_w8a8_mfma(const int8_t *q, const float *s_a, const int8_t *w, 
         return hipSuccess;
     }
     // Tile choice, measured at b = 512 on the Qwen3-8B layers against 32- to
-    // 128-token tiles, 64- or 128-byte stages, 1, 2 or 4 K groups and ring
-    // depths 2 to 8: while the 64 x 128 tiles fit one per CU, two K groups
-    // (8 waves) share each tile; past that, 128 x 128 tiles with one K
-    // group, two workgroups per CU, whose barriers do not wait for each other.
-    const int64_t tiles = static_cast<int64_t>((b + 63) / 64) * ((N + kBN - 1) / kBN);
+    // 128-token and 64- or 128-row tiles, 64- or 128-byte stages, 1, 2 or 4 K
+    // groups and ring depths 2 to 8: while the 64 x 128 tiles fit one per CU,
+    // two K groups (8 waves) share each tile; past that, tiles with one K
+    // group, two or more workgroups per CU, whose barriers do not wait for
+    // each other: 128 x 128 when there are at least as many as CUs, else
+    // 64 x 64.
     const int cus = device_info().cus;
-    if (tiles <= cus) return launch_tiles<64, 128, 2, 4>(q, s_a, w, s_w, b, N, K, y, st);
-    return launch_tiles<128, 128, 1, 3>(q, s_a, w, s_w, b, N, K, y, st);
+    const int64_t tiles = static_cast<int64_t>((b + 63) / 64) * ((N + 127) / 128);
+    const int64_t big = static_cast<int64_t>((b + 127) / 128) * ((N + 127) / 128);
+    if (tiles <= cus) return launch_tiles<64, 128, 128, 2, 4>(q, s_a, w, s_w, b, N, K, y, st);
+    if (big < cus) return launch_tiles<64, 64, 128, 1, 3>(q, s_a, w, s_w, b, N, K, y, st);
+    return launch_tiles<128, 128, 128, 1, 3>(q, s_a, w, s_w, b, N, K, y, st);
 }
 
 }  // namespace iqd

@@ -130,6 +130,31 @@ def test_matrix_core_shape_classes(iqd, N, K):
         assert_bits_equal(host_bits(y), ref[:b], f"N={N} K={K} b={b} vs b=1")
 
 
+# The three tile classes of the matrix-core GEMM for b > 16, with token and
+# row counts that are no multiple of any tile: 64 x 64 tiles (fewer 128 x 128
+# tiles than CUs), 64 x 128 tiles with two K groups (at most one per CU), and
+# 128 x 128 tiles.  Sampled rows against the oracle, every row against the
+# mat-vec over 16-token chunks.
+@pytest.mark.parametrize("b,N,K", [(100, 20000, 272), (130, 2000, 1040), (300, 33000, 272)])
+def test_prefill_tile_classes_ragged(iqd, b, N, K):
+    t = torch()
+    g = W.rng(b * 7 + N + K)
+    w = W.int8_weights(g, N, K)
+    s_w = W.log_uniform_scales(g, N)
+    x = W.normal_bf16(g, b, K)
+    oq, osa = oracle.quantize_token(x)
+    q, sa = gpu_quant(iqd, x)
+    wd, swd = dev(w), dev(s_w)
+    y = iqd.w8a8_linear(q, sa, wd, swd)
+    rows = np.unique(np.concatenate([sample_rows(N, 24, N + b), np.arange(N - 9, N)]))
+    assert_bits_equal(host_bits(y)[:, rows], oracle.w8a8(oq, osa, w[rows], s_w[rows]), f"b={b} N={N} K={K} vs oracle")
+    ref = t.empty((b, N), dtype=t.bfloat16, device="cuda")
+    for t0 in range(0, b, 16):
+        t1 = min(b, t0 + 16)
+        iqd.w8a8_linear(q[t0:t1], sa[t0:t1], wd, swd, y=ref[t0:t1])
+    assert_bits_equal(host_bits(y), host_bits(ref), f"b={b} N={N} K={K} vs mat-vec")
+
+
 def test_max_k_and_extreme_codes(iqd):
     """K = 131056 (the largest multiple of 16 under the bound) with every
     product at (-128)*(-128): acc = 2147287040, close to 2^31."""
