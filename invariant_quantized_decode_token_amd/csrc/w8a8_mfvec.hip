@@ -113,13 +113,6 @@ __device__ __forceinline__ float amax8(const v4i &v) {
     return m;
 }
 
-// Maximum over the lanes of a wave (exact: max does not round).
-__device__ __forceinline__ float wave_max(float m) {
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) m = fmaxf(m, shfl_xor(m, mask));
-    return m;
-}
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
 }
