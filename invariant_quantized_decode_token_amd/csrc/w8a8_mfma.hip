@@ -12,9 +12,9 @@
 // mat-vec kernel": past a handful of tokens the stock path moved to a tiled
 // matmul with its own add order; here the integer sums make the order moot.
 //
-// Tiling: a workgroup of 4 waves computes a BM x BN tile of y (BM tokens, BN
-// weight rows); its waves are 2 x 2, each owning a (BM/2) x (BN/2) sub-tile
-// of v_mfma_i32_16x16x64_i8 accumulators.  K advances 128 bytes per stage.
+// Tiling: a workgroup of GM x GN waves computes a BM x BN tile of y (BM
+// tokens, BN weight rows); each wave owns a (BM/GM) x (BN/GN) sub-tile of
+// v_mfma_i32_16x16x64_i8 accumulators.  K advances 128 bytes per stage.
 //  * Operands go from global memory straight into LDS (buffer loads with the
 //    LDS destination, 16 bytes per lane): an S-stage ring, S - 1 stages in
 //    flight, one barrier per stage, no registers spent on staging.
@@ -42,7 +42,6 @@
 namespace iqd {
 namespace {
 
-constexpr int kThreads = 256;  // 4 waves, 2 x 2 over the tile
 constexpr int kXcds = 8;       // workgroups are dealt round-robin to the 8 XCDs (L2 domains)
 constexpr int kBK = 128;       // K bytes per stage
 constexpr int kCPR = kBK / 16; // 16-byte chunks per staged row
@@ -97,15 +96,16 @@ __device__ __forceinline__ uint32_t slot_of(int row, int c) {
 template <int BN>
 constexpr int out_stride() { return BN + 8; }
 
-template <int BM, int BN, int S>
-__global__ __launch_bounds__(kThreads) void k_w8a8_mfma(const int8_t *__restrict__ q, const float *__restrict__ s_a,
+template <int BM, int BN, int S, int GM, int GN>
+__global__ __launch_bounds__(64 * GM * GN) void k_w8a8_mfma(const int8_t *__restrict__ q, const float *__restrict__ s_a,
                                                         const int8_t *__restrict__ w, const float *__restrict__ s_w,
                                                         int M, int N, int K, uint16_t *__restrict__ y) {
-    constexpr int WM = BM / 2, WN = BN / 2;  // wave sub-tile
+    constexpr int NWV = GM * GN, NTH = kWave * NWV;  // waves, GM x GN over the tile
+    constexpr int WM = BM / GM, WN = BN / GN;        // wave sub-tile
     constexpr int FM = WM / 16, FN = WN / 16;
-    constexpr int PA = BM / 32, PB = BN / 32;  // 1 KiB load instructions per wave per stage
+    constexpr int PA = BM / (8 * NWV), PB = BN / (8 * NWV);  // 1 KiB load instructions per wave per stage
     constexpr int STAGE = (BM + BN) * kBK;
-    static_assert(BM % 32 == 0 && BN % 32 == 0 && S >= 2, "tile and ring");
+    static_assert(BM % (8 * NWV) == 0 && BN % (8 * NWV) == 0 && S >= 2, "tile and ring");
     extern __shared__ __attribute__((aligned(16))) int8_t lds_all[];  // [S][STAGE], then the output tile
 
     // Tile of this workgroup.  The M tiles of one N tile (which read the same
@@ -123,20 +123,20 @@ __global__ __launch_bounds__(kThreads) void k_w8a8_mfma(const int8_t *__restrict
 
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int lane = lane_id();
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / GN, wn = wave % GN;
     const int nst = (K + kBK - 1) / kBK;
     const __amdgpu_buffer_rsrc_t ra = rsrc(q, static_cast<int64_t>(M) * K);
     const __amdgpu_buffer_rsrc_t rb = rsrc(w, static_cast<int64_t>(N) * K);
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_all));
 
-    // Load instruction p of this wave fills LDS slots 64 (4 p + wave) ..
+    // Load instruction p of this wave fills LDS slots 64 (NWV p + wave) ..
     // + 63 of a stage: lane -> (row, slot) -> the logical chunk stored there.
     // Instructions p < PA hold activation rows, the rest weight rows.
     uint32_t goff[PA + PB];
     int gk[PA + PB];  // byte offset of the lane's chunk within the stage's K range
 #pragma unroll
     for (int p = 0; p < PA + PB; ++p) {
-        const int u = (4 * p + wave) * kWave + lane;
+        const int u = (NWV * p + wave) * kWave + lane;
         const int row = u / kCPR;
         const int c = (u % kCPR) ^ ((row >> 1) & 7);
         gk[p] = 16 * c;
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_w8a8_mfma(const int8_t *__restrict
         for (int p = 0; p < PA + PB; ++p) {
             const bool in = goff[p] != kOob && k0 + gk[p] < K;
             const uint32_t off = in ? goff[p] + static_cast<uint32_t>(k0) : kOob;
-            lds_i8 *dst = (lds_i8 *)(lds_all + buf * STAGE + (4 * p + wave) * 1024);
+            lds_i8 *dst = (lds_i8 *)(lds_all + buf * STAGE + (NWV * p + wave) * 1024);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(p < PA ? ra : rb, dst, 16, off, 0, 0, 0);
         }
     };
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void k_w8a8_mfma(const int8_t *__restrict
                     w8a8_epilogue(acc[i][j][r], sa[i][r], sw[j]);
     __syncthreads();
     constexpr int PPR = BN / 8;  // 16-byte pieces per tile row
-    for (int p = static_cast<int>(threadIdx.x); p < BM * PPR; p += kThreads) {
+    for (int p = static_cast<int>(threadIdx.x); p < BM * PPR; p += NTH) {
         const int row = p / PPR, c = (p % PPR) * 8;
         const int m = m0 + row, n = n0 + c;
         if (m >= M || n >= N) continue;
@@ -249,19 +249,19 @@ __global__ __launch_bounds__(kThreads) void k_w8a8_mfma(const int8_t *__restrict
     }
 }
 
-template <int BM, int BN, int S>
+template <int BM, int BN, int S, int GM, int GN>
 hipError_t launch_tiles(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int b, int N, int K,
                         uint16_t *y, hipStream_t st) {
     const size_t ring = static_cast<size_t>(S) * (BM + BN) * kBK;
     const size_t otile = static_cast<size_t>(BM) * out_stride<BN>() * 2;
     const size_t smem = ring > otile ? ring : otile;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w8a8_mfma<BM, BN, S>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w8a8_mfma<BM, BN, S, GM, GN>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     if (e != hipSuccess) return e;
     const int mt = (b + BM - 1) / BM;
     const int nt = (N + BN - 1) / BN;
     const int nt_pad = (nt + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((k_w8a8_mfma<BM, BN, S>), dim3(mt * nt_pad), dim3(kThreads), smem, st, q, s_a, w, s_w, b, N, K,
+    hipLaunchKernelGGL((k_w8a8_mfma<BM, BN, S, GM, GN>), dim3(mt * nt_pad), dim3(kWave * GM * GN), smem, st, q, s_a, w, s_w, b, N, K,
                        y);
     return hipGetLastError();
 }
@@ -282,17 +282,14 @@ hipError_t launch_w8a8_mfma(const int8_t *q, const float *s_a, const int8_t *w, 
         return hipSuccess;
     }
     // Tile choice, measured at b = 512 on the Qwen3-8B layers (weights read
-    // from HBM) against 64- and 128-token and -row tiles and rings of 2 to 4
-    // stages: for long K (12288) 64 x 128 tiles with 4 stages while they fit
-    // one per CU; otherwise 64 x 64 tiles with 3 stages while they number at
-    // most two per CU, and 128 x 64 tiles with 2 stages past that (three
-    // 48 KiB workgroups per CU).
+    // from HBM) against 64- to 256-token and -row tiles, 4 or 8 waves and
+    // rings of 2 to 4 stages: 8 waves and two workgroups per CU throughout;
+    // 128 x 128 tiles with 2 stages while they number at least two per CU,
+    // 128 x 64 tiles with 3 stages below that.
     const int cus = device_info().cus;
-    const int64_t wide = static_cast<int64_t>((b + 63) / 64) * ((N + 127) / 128);
-    const int64_t small = static_cast<int64_t>((b + 63) / 64) * ((N + 63) / 64);
-    if (K > 8192 && wide <= cus) return launch_tiles<64, 128, 4>(q, s_a, w, s_w, b, N, K, y, st);
-    if (small <= 2 * cus) return launch_tiles<64, 64, 3>(q, s_a, w, s_w, b, N, K, y, st);
-    return launch_tiles<128, 64, 2>(q, s_a, w, s_w, b, N, K, y, st);
+    const int64_t big = static_cast<int64_t>((b + 127) / 128) * ((N + 127) / 128);
+    if (big >= 2 * cus) return launch_tiles<128, 128, 2, 2, 4>(q, s_a, w, s_w, b, N, K, y, st);
+    return launch_tiles<128, 64, 3, 4, 2>(q, s_a, w, s_w, b, N, K, y, st);
 }
 
 }  // namespace iqd

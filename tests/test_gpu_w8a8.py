@@ -130,11 +130,11 @@ def test_matrix_core_shape_classes(iqd, N, K):
         assert_bits_equal(host_bits(y), ref[:b], f"N={N} K={K} b={b} vs b=1")
 
 
-# The three tile classes of the matrix-core GEMM for b > 16, with token and
-# row counts that are no multiple of any tile: 64 x 64 tiles (fewer 128 x 128
-# tiles than CUs), 64 x 128 tiles with two K groups (at most one per CU), and
-# 128 x 128 tiles.  Sampled rows against the oracle, every row against the
-# mat-vec over 16-token chunks.
+# Both tile classes of the matrix-core GEMM for b > 16, with token and row
+# counts that are no multiple of any tile: 128 x 64 tiles (fewer than two
+# 128 x 128 tiles per CU; one and two M tiles, K of 2 and 8 stages plus a
+# ragged one) and 128 x 128 tiles.  Sampled rows against the oracle, every
+# row against the mat-vec over 16-token chunks.
 @pytest.mark.parametrize("b,N,K", [(100, 20000, 272), (130, 2000, 1040), (300, 33000, 272)])
 def test_prefill_tile_classes_ragged(iqd, b, N, K):
     t = torch()
