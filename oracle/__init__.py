@@ -82,6 +82,9 @@ def _load():
         "oracle_lm_head_argmax": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, ctypes.c_int]),
         "oracle_pow2_nearest": (f32, [f32]),
         "oracle_pow2_requant": (ctypes.c_int, [P, P, I64, I64, P, P]),
+        "oracle_attn_exp": (f32, [f32]),
+        "oracle_attn_decode": (ctypes.c_int, [P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, I64, f32, I64, I64,
+                                              P, ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -251,3 +254,43 @@ def pow2_requant(w, s_w):
     so = np.empty((N,), np.float32)
     _check(_load().oracle_pow2_requant(_ptr(w), _ptr(s_w), N, K, _ptr(wo), _ptr(so)), "pow2_requant")
     return wo, so
+
+
+# --- decode attention over a KV cache in fixed 256-cell chunks -------------------
+
+ATTN_CHUNK = 256
+
+
+def attn_exp(x) -> np.float32:
+    """The attention recipe's e^x (x <= 0), binary32 operations only."""
+    return np.float32(_load().oracle_attn_exp(float(np.float32(x))))
+
+
+def _cache_view(c: np.ndarray, name: str):
+    """A bf16 cache [cells, heads, D] (uint16 bits, any cell and head strides,
+    unit stride along D) -> (array, cell stride, head stride) in elements."""
+    if c.dtype != np.uint16 or c.ndim != 3 or c.strides[2] != 2 or c.strides[0] % 2 or c.strides[1] % 2:
+        raise TypeError(f"{name}: expected uint16 [cells, heads, D] with unit stride along D")
+    return c, c.strides[0] // 2, c.strides[1] // 2
+
+
+def attn_decode(q, k_cache, v_cache, pos0: int, scale, heads=None, nthreads: int = 0) -> np.ndarray:
+    """q bf16 bits [b, Hq, D]; k_cache, v_cache bf16 bits [cells, Hkv, D]
+    (views with their own strides are fine); query t at position pos0 + t.
+    -> out bf16 bits [b, Hq, D] (zeros outside `heads`, a (lo, hi) range)."""
+    q = _arr(q, np.uint16)
+    b, Hq, D = q.shape
+    k, kc, kh = _cache_view(k_cache, "k_cache")
+    v, vc, vh = _cache_view(v_cache, "v_cache")
+    Hkv = k.shape[1]
+    if v.shape[1] != Hkv or k.shape[2] != D or v.shape[2] != D:
+        raise ValueError("cache shapes do not match q")
+    if pos0 + b > min(k.shape[0], v.shape[0]):
+        raise ValueError("positions past the cache")
+    h0, h1 = heads if heads is not None else (0, Hq)
+    out = np.zeros((b, Hq, D), np.uint16)
+    kp = ctypes.c_void_p(k.__array_interface__["data"][0])
+    vp = ctypes.c_void_p(v.__array_interface__["data"][0])
+    _check(_load().oracle_attn_decode(_ptr(q), kp, vp, kc, kh, vc, vh, b, Hq, Hkv, D, pos0, float(np.float32(scale)),
+                                      h0, h1, _ptr(out), nthreads), "attn_decode")
+    return out

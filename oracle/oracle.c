@@ -8,8 +8,9 @@
  * with the HIP library.
  *
  * It is deliberately plain and slow: scalar loops, one IEEE-754 binary32
- * operation per C expression, no blocking, no vectorisation, no fused
- * multiply-add.  Build with `gcc -O2 -ffp-contract=off` (no -ffast-math, no
+ * operation per C expression, no blocking, no vectorisation, no contraction:
+ * the linear layers use no fused multiply-add, and the attention recipe at
+ * the end uses only the explicit fmaf calls it names.  Build with `gcc -O2 -ffp-contract=off` (no -ffast-math, no
  * -march=native) on x86-64, where float arithmetic is SSE scalar with one
  * rounding per operation and FLT_EVAL_METHOD == 0.
  *
@@ -433,4 +434,210 @@ int oracle_pow2_requant(const int8_t *w, const float *s_w, int64_t N, int64_t K,
         }
     }
     return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention over a KV cache in fixed chunks.                          */
+/* ------------------------------------------------------------------------ */
+/*
+ * Sources:
+ *  [P1] "the bug that waited for position 384" (Fig. 5): the stock kernel
+ *       summed the cache in 128-cell chunks spread over P parallel blocks,
+ *       P taken from an occupancy query, so a batched query's last chunk
+ *       could join another block's partial and round differently.
+ *  [P2] "Fusion that lost": split-KV attention as two kernels, 256-token
+ *       chunks computed as independent partials and a merge kernel, and a
+ *       fast path that writes the output directly when there is one chunk;
+ *       the chunk count must come from the tokens present, not from the
+ *       allocated cache.  "Why the decoders disagreed?": cache slots past a
+ *       query's position are never read.  "Shipping the 6.4x as its own
+ *       backend": a merge order is one valid rounding among many; what
+ *       matters is that it is fixed.
+ *
+ * The pages fix the structure (fixed chunks, partials, a merge) but not the
+ * float order inside it.  The recipe below is this library's fixed order;
+ * every step depends only on the query's own row, its position and the
+ * cache cells 0..position, never on how many queries share a launch, the
+ * cache's allocated size or the grid.  Unlike the linear layer, it uses
+ * fused multiply-adds, each one explicit (fmaf, one rounding).
+ */
+
+#define ATTN_CHUNK 256
+
+/* e^x for x <= 0 (the only arguments the recipe forms) in binary32 operations only (every implementation that
+ * performs the same operations gets the same bits).  Cody and Waite's
+ * additive reduction x = n ln2 + r, with ln 2 split into a head of 16
+ * significant bits (n * head is exact for |n| < 256) and a tail; then the
+ * degree-7 Taylor polynomial of e^r (|r| <= ln2/2 + rounding, truncation
+ * below 6e-9 relative) in Horner form with fused multiply-adds; then the
+ * exact scaling by 2^n built from its exponent field.  For n < -125 the
+ * result is 0, so no step produces a subnormal. */
+float oracle_attn_exp(float x) {
+    const float log2e = 0x1.715476p+0f;  /* fl(1 / ln 2) */
+    const float ln2_hi = 0x1.62e4p-1f;   /* 0.693145751953125 */
+    const float ln2_lo = 0x1.7f7d1cp-20f; /* fl(ln 2 - ln2_hi) */
+    float n = rintf(x * log2e);
+    if (n < -125.0f) return 0.0f;
+    if (n > 127.0f) n = 127.0f;
+    float r = (x - n * ln2_hi) - n * ln2_lo;
+    float p = 0x1.a01a02p-13f;          /* 1/7! */
+    p = fmaf(p, r, 0x1.6c16c2p-10f);     /* 1/6! */
+    p = fmaf(p, r, 0x1.111112p-7f);      /* 1/5! */
+    p = fmaf(p, r, 0x1.555556p-5f);      /* 1/4! */
+    p = fmaf(p, r, 0x1.555556p-3f);      /* 1/3! */
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    return p * bits_f32((uint32_t)((int32_t)n + 127) << 23);
+}
+
+/* Score of one query row against one cached key.  qs = q * scale, rounded
+ * per element.  D is cut into D/8 slices of 8 consecutive dimensions; each
+ * slice is a chain of fused multiply-adds from +0 in increasing d (each step
+ * rounds once); the slice sums are then added as an adjacent-pair tree
+ * (D/8 a power of two). */
+static float attn_score(const float *qs, const uint16_t *k, int64_t D) {
+    float part[64];
+    int64_t m = D / 8;
+    for (int64_t l = 0; l < m; ++l) {
+        float a = 0.0f;
+        for (int64_t i = 0; i < 8; ++i) a = fmaf(qs[8 * l + i], oracle_bf16_to_f32(k[8 * l + i]), a);
+        part[l] = a;
+    }
+    while (m > 1) {
+        for (int64_t i = 0; i < m / 2; ++i) part[i] = part[2 * i] + part[2 * i + 1];
+        m /= 2;
+    }
+    return part[0];
+}
+
+typedef struct {
+    const uint16_t *q, *k, *v;
+    int64_t kc, kh, vc, vh; /* cell and head strides of the caches, in elements */
+    int64_t b, Hq, Hkv, D, pos0;
+    float scale;
+    int64_t h0, h1;         /* heads computed */
+    uint16_t *out;
+    int64_t r0, r1;         /* this thread's rows, r = t * (h1 - h0) + (hq - h0) */
+    int status;
+} attn_job;
+
+/* One output row (token t, query head hq):
+ *   position p = pos0 + t; the row attends cells 0..p; chunk c holds cells
+ *   [256 c, 256 c + 256) cut at p; the row has n = p / 256 + 1 chunks.
+ *   Per chunk: s_j = score(q * scale, k_j); m_c = max_j s_j;
+ *     e_j = E(s_j - m_c); l_c = sum_j e_j and o_c[d] = sum_j e_j v_j[d],
+ *     both in increasing j from +0, o with fused multiply-adds.
+ *   Merge in increasing c: M = max_c m_c, w_c = E(m_c - M);
+ *     L = w_0 l_0, O[d] = w_0 o_0[d], then L = fma(w_c, l_c, L) and
+ *     O[d] = fma(w_c, o_c[d], O[d]) for c = 1, 2, ...
+ *   out[d] = bf16(O[d] / L).
+ * With one chunk, w_0 = E(0) = 1 and the merge returns o_0 / l_0 exactly:
+ * a fast path that skips it gives the same bits. */
+static void attn_rows(attn_job *j) {
+    const int64_t D = j->D, G = j->Hq / j->Hkv, nh = j->h1 - j->h0;
+    float *qs = (float *)malloc(sizeof(float) * (size_t)D);
+    float *o = (float *)malloc(sizeof(float) * (size_t)D);
+    float *O = (float *)malloc(sizeof(float) * (size_t)D);
+    float *s = (float *)malloc(sizeof(float) * ATTN_CHUNK);
+    if (!qs || !o || !O || !s) {
+        j->status = ORACLE_ERR_ARGS;
+        free(qs), free(o), free(O), free(s);
+        return;
+    }
+    for (int64_t r = j->r0; r < j->r1; ++r) {
+        const int64_t t = r / nh, hq = j->h0 + r % nh, hk = hq / G;
+        const int64_t p = j->pos0 + t, nchunks = p / ATTN_CHUNK + 1;
+        const uint16_t *qr = j->q + (t * j->Hq + hq) * D;
+        for (int64_t d = 0; d < D; ++d) qs[d] = oracle_bf16_to_f32(qr[d]) * j->scale;
+        float M = -INFINITY; /* the largest chunk maximum, needed by the merge weights */
+        float *mc = (float *)malloc(sizeof(float) * (size_t)nchunks);
+        float *lc = (float *)malloc(sizeof(float) * (size_t)nchunks);
+        float *oc = (float *)malloc(sizeof(float) * (size_t)(nchunks * D));
+        if (!mc || !lc || !oc) {
+            j->status = ORACLE_ERR_ARGS;
+            free(mc), free(lc), free(oc);
+            break;
+        }
+        for (int64_t c = 0; c < nchunks; ++c) {
+            const int64_t c0 = c * ATTN_CHUNK;
+            const int64_t c1 = (c0 + ATTN_CHUNK < p + 1) ? c0 + ATTN_CHUNK : p + 1;
+            float m = -INFINITY;
+            for (int64_t cell = c0; cell < c1; ++cell) {
+                s[cell - c0] = attn_score(qs, j->k + cell * j->kc + hk * j->kh, D);
+                m = fmaxf(m, s[cell - c0]);
+            }
+            float l = 0.0f;
+            for (int64_t d = 0; d < D; ++d) o[d] = 0.0f;
+            for (int64_t cell = c0; cell < c1; ++cell) {
+                const float e = oracle_attn_exp(s[cell - c0] - m);
+                const uint16_t *vr = j->v + cell * j->vc + hk * j->vh;
+                l = l + e;
+                for (int64_t d = 0; d < D; ++d) o[d] = fmaf(e, oracle_bf16_to_f32(vr[d]), o[d]);
+            }
+            mc[c] = m;
+            lc[c] = l;
+            memcpy(oc + c * D, o, sizeof(float) * (size_t)D);
+            M = fmaxf(M, m);
+        }
+        float L = 0.0f;
+        for (int64_t c = 0; c < nchunks; ++c) {
+            const float w = oracle_attn_exp(mc[c] - M);
+            if (c == 0) {
+                L = w * lc[0];
+                for (int64_t d = 0; d < D; ++d) O[d] = w * oc[d];
+            } else {
+                L = fmaf(w, lc[c], L);
+                for (int64_t d = 0; d < D; ++d) O[d] = fmaf(w, oc[c * D + d], O[d]);
+            }
+        }
+        uint16_t *orow = j->out + (t * j->Hq + hq) * D;
+        for (int64_t d = 0; d < D; ++d) orow[d] = oracle_bf16_rne(f32_bits(O[d] / L));
+        free(mc), free(lc), free(oc);
+    }
+    free(qs), free(o), free(O), free(s);
+}
+
+static void *attn_worker(void *arg) {
+    attn_rows((attn_job *)arg);
+    return NULL;
+}
+
+/* q bf16 [b, Hq, D]; k and v bf16 caches addressed as base + cell * cell_stride
+ * + head * head_stride + d (strides in elements); query t sits at position
+ * pos0 + t and attends cells 0..pos0 + t.  Query head hq reads kv head
+ * hq / (Hq / Hkv).  Writes out bf16 [b, Hq, D] for heads h0 <= hq < h1. */
+int oracle_attn_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t k_cell, int64_t k_head,
+                       int64_t v_cell, int64_t v_head, int64_t b, int64_t Hq, int64_t Hkv, int64_t D, int64_t pos0,
+                       float scale, int64_t h0, int64_t h1, uint16_t *out, int nthreads) {
+    if (!q || !k || !v || !out || b < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 8 || D > 512 ||
+        (D & (D - 1)) != 0 || pos0 < 0 || h0 < 0 || h1 > Hq || h0 >= h1)
+        return ORACLE_ERR_ARGS;
+    const int64_t rows = b * (h1 - h0);
+    if (nthreads <= 0) nthreads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > rows) nthreads = (int)rows;
+    attn_job jobs[256];
+    pthread_t th[256];
+    int started[256];
+    for (int i = 0; i < nthreads; ++i) {
+        attn_job a = {q, k, v, k_cell, k_head, v_cell, v_head, b, Hq, Hkv, D, pos0, scale, h0, h1, out,
+                      rows * i / nthreads, rows * (i + 1) / nthreads, ORACLE_OK};
+        jobs[i] = a;
+        started[i] = 0;
+    }
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, attn_worker, &jobs[i]) == 0)
+            started[i] = 1;
+        else
+            attn_worker(&jobs[i]);
+    }
+    attn_worker(&jobs[0]);
+    int status = ORACLE_OK;
+    for (int i = 1; i < nthreads; ++i)
+        if (started[i]) pthread_join(th[i], NULL);
+    for (int i = 0; i < nthreads; ++i)
+        if (jobs[i].status != ORACLE_OK) status = jobs[i].status;
+    return status;
 }

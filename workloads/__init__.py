@@ -14,6 +14,10 @@ Recipes (numpy ``Generator(PCG64(seed))``; draws happen in the order listed):
   * outlier channels: ``round(0.01 * K)`` channel indices from a seeded
     permutation, the same for every token, scaled by 20 in fp32 and rounded
     to bf16 again;
+  * decode attention: q, k and v ``standard_normal`` rounded to bf16 (the
+    post-norm, post-rotary statistics of a Qwen3 layer are of that order);
+    cache slots past the cells in use hold NaN bit patterns (0x7FC0), so a
+    kernel that reads past a query's position shows it in its output;
   * q8_0-style block weights: real weights ``standard_normal``, per aligned
     32-block an fp16 scale ``d = fp16(amax / 127)`` and int8 codes
     ``clamp(rint(w / d), -127, 127)`` (0 where d == 0).  This is the
@@ -38,12 +42,15 @@ QWEN3_8B = [("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 24576), ("
 QWEN3_14B = [("qkv", 5120, 7168), ("o", 5120, 5120), ("gate_up", 5120, 34816), ("down", 17408, 5120)]
 BLOCKQ8_SHAPES = [("bq8_4096", 4096, 4096), ("bq8_12288", 12288, 4096)]
 LM_HEAD = ("lm_head", 4096, 151936)
+# decode attention: (name, query heads, kv heads, head dim)
+QWEN3_8B_ATTN = ("qwen3_8b_attn", 32, 8, 128)
 
 SEED_TINY = 1001
 SEED_8B = 2001
 SEED_BQ8 = 3001
 SEED_14B = 4001
 SEED_LM_HEAD = 5001
+SEED_ATTN = 6001
 
 TOKENS_TINY = 5
 TOKENS_8B = 512
@@ -217,3 +224,33 @@ def negative_zero_operands(K: int, N: int = 4, b: int = 1):
     w = np.ones((N, K), np.int8)
     d_w = np.full((N, m), FP16_ONE, np.uint16)
     return q, d_a, w, d_w
+
+
+# -- decode attention ---------------------------------------------------------------
+
+BF16_NAN = 0x7FC0
+
+
+@dataclass
+class AttnCase:
+    q: np.ndarray        # bf16 bits [b, Hq, D]
+    k: np.ndarray        # bf16 bits [capacity, Hkv, D]
+    v: np.ndarray        # bf16 bits [capacity, Hkv, D]
+    pos0: int            # query t sits at position pos0 + t
+    scale: np.float32    # 1 / sqrt(D), rounded to binary32
+
+
+def attn_case(seed: int, b: int, cells: int, Hq: int = 32, Hkv: int = 8, D: int = 128,
+              capacity: int | None = None) -> AttnCase:
+    """b queries at positions cells - b .. cells - 1 over a cache holding
+    `cells` written cells (the queries' own keys included) in an allocation
+    of `capacity` slots; slots past `cells` are NaN."""
+    assert 1 <= b <= cells
+    capacity = cells if capacity is None else capacity
+    g = rng(seed)
+    q = normal_bf16(g, b * Hq, D).reshape(b, Hq, D)
+    k = np.full((capacity, Hkv, D), BF16_NAN, np.uint16)
+    v = np.full((capacity, Hkv, D), BF16_NAN, np.uint16)
+    k[:cells] = normal_bf16(g, cells * Hkv, D).reshape(cells, Hkv, D)
+    v[:cells] = normal_bf16(g, cells * Hkv, D).reshape(cells, Hkv, D)
+    return AttnCase(q, k, v, cells - b, np.float32(1.0 / np.sqrt(np.float64(D))))
