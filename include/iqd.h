@@ -61,7 +61,7 @@ typedef enum {
     IQD_ERR_INVALID = -1,     /* bad shape, null pointer, aliasing, bad group */
     IQD_ERR_ALIGN = -2,       /* pointer misaligned */
     IQD_ERR_RANGE = -3,       /* K above IQD_K_MAX */
-    IQD_ERR_UNSUPPORTED = -4, /* split_k not allowed for this shape */
+    IQD_ERR_UNSUPPORTED = -4, /* split_k (or an attention shape) not supported */
     IQD_ERR_WORKSPACE = -5,   /* workspace missing or too small */
     IQD_ERR_HIP = -6          /* a HIP runtime call or launch failed */
 } iqd_status;
@@ -208,6 +208,56 @@ int lm_head_argmax(const int8_t *q, const float *s_a, const int8_t *w, const flo
  */
 int pow2_requantize(const int8_t *w, const float *s_w, int64_t N, int64_t K, int8_t *w_out,
                     float *s_out, void *stream);
+
+/*
+ * attn_decode - decode / speculative-verify attention over a bf16 KV cache,
+ * batch-invariant.
+ *
+ * [P1 "the bug that waited for position 384", Fig. 5]: the stock kernel summed
+ * the cache in chunks spread over an occupancy-chosen number of blocks, so a
+ * batched query could round differently from the same query alone.
+ * [P2 "Fusion that lost"]: split-KV attention as fixed 256-token chunk
+ * partials and a merge, with a one-chunk fast path, the chunk count taken
+ * from the tokens present rather than the allocation; [P2 "Why the decoders
+ * disagreed?"]: slots past a query's position are never read; [P2 "Shipping
+ * the 6.4x as its own backend"]: a merge order is one valid rounding and must
+ * stay fixed.
+ *
+ * Query t (0 <= t < b) sits at position pos0 + t and attends cells
+ * 0 .. pos0 + t (its own key and value already written).  Query head hq reads
+ * kv head hq / (Hq / Hkv).  Per query row, in binary32:
+ *   qs = fl(q * scale); s_j = tree over 16 slices of 8 dims of fused
+ *   multiply-add chains from +0 (adjacent pairs); per 256-cell chunk c:
+ *   m_c = max s_j, e_j = E(s_j - m_c), l_c = sum e_j, o_c = sum e_j v_j
+ *   (fused multiply-adds), j increasing; merge in increasing c with
+ *   w_c = E(m_c - max m): L = w_0 l_0, O = w_0 o_0, then fused multiply-adds;
+ *   out = bf16(O / L), nearest even.  E(x) = e^x for x <= 0 by Cody-Waite
+ *   reduction and a degree-7 Taylor polynomial, 0 below 2^-125.
+ * Each row's result depends on nothing but its q row, its position, scale
+ * and cells 0..pos0 + t: not on b, the cache's allocated size, the strides
+ * or the grid.
+ *
+ *   q_bf16   in  bf16 [b, Hq, D], contiguous, 16-byte aligned
+ *   k_cache  in  bf16; the element (cell j, kv head h, dim d) is at
+ *   v_cache      cache + j * cell_stride + h * head_stride + d (strides in
+ *                elements, multiples of 8, so every 16-byte row piece is
+ *                aligned); both must hold cells 0 .. pos0 + b - 1, which are
+ *                the only cells read; 16-byte aligned
+ *   out_bf16 out bf16 [b, Hq, D], contiguous, 16-byte aligned
+ *   workspace    attn_workspace_bytes(b, Hq, Hkv, D, pos0) bytes, 16-byte
+ *                aligned (none when pos0 + b <= 256): fp32 chunk partials
+ * Supported: D = 128; Hq a multiple of Hkv with Hq / Hkv <= 16 (else
+ * IQD_ERR_UNSUPPORTED); 1 <= b <= 65535; 0 <= pos0 and pos0 + b <= 2^30;
+ * scale finite.
+ */
+int attn_decode(const void *q_bf16, const void *k_cache, const void *v_cache, int64_t k_cell_stride,
+                int64_t k_head_stride, int64_t v_cell_stride, int64_t v_head_stride, int64_t b, int64_t Hq,
+                int64_t Hkv, int64_t D, int64_t pos0, float scale, void *out_bf16, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/* Workspace bytes attn_decode needs (0 if none, or for arguments it would
+ * reject). */
+size_t attn_workspace_bytes(int64_t b, int64_t Hq, int64_t Hkv, int64_t D, int64_t pos0);
 
 /* Workspace bytes the op needs for these sizes (0 if none); 0 also for
  * arguments the op would reject. */

@@ -55,6 +55,9 @@ SIGNATURES = {
     "blockq8_linear": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]),
     "lm_head_argmax": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, P, SZ, P]),
     "pow2_requantize": (ctypes.c_int, [P, P, I64, I64, P, P, P]),
+    "attn_decode": (ctypes.c_int, [P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, I64, ctypes.c_float, P, P, SZ,
+                                   P]),
+    "attn_workspace_bytes": (SZ, [I64, I64, I64, I64, I64]),
     "iqd_workspace_bytes": (SZ, [ctypes.c_int, I64, I64, I64, I32]),
     "iqd_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "iqd_last_hip_error": (ctypes.c_char_p, []),
@@ -275,3 +278,42 @@ def pow2_requantize(w, s_w, w_out=None, s_out=None):
     st = load().pow2_requantize(_ptr(w), _ptr(s_w), N, K, _ptr(w_out), _ptr(s_out), _stream_ptr())
     _raise(st, "pow2_requantize")
     return w_out, s_out
+
+
+def attn_workspace_bytes(b: int, Hq: int, Hkv: int, D: int, pos0: int) -> int:
+    return int(load().attn_workspace_bytes(b, Hq, Hkv, D, pos0))
+
+
+def _check_cache(t, name: str, Hkv: int, D: int):
+    """A bf16 cache [cells, Hkv, D] with unit stride along D; its cell and
+    head strides are passed as they are (a view into a larger buffer is fine)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be a bf16 cuda tensor")
+    if t.dim() != 3 or t.shape[1] != Hkv or t.shape[2] != D or t.stride(2) != 1:
+        raise ValueError(f"{name} must be [cells, {Hkv}, {D}] with unit stride along the last dimension")
+
+
+def attn_decode(q, k_cache, v_cache, pos0: int, scale: float, out=None, workspace=None):
+    """q bf16 [b, Hq, D]; k_cache, v_cache bf16 [cells, Hkv, D] (strided views
+    allowed); query t at position pos0 + t -> out bf16 [b, Hq, D]."""
+    torch = _torch()
+    _check_tensor(q, "q", (torch.bfloat16,))
+    b, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    _check_cache(k_cache, "k_cache", Hkv, D)
+    _check_cache(v_cache, "v_cache", Hkv, D)
+    if pos0 + b > min(k_cache.shape[0], v_cache.shape[0]):
+        raise ValueError("the caches must hold cells 0 .. pos0 + b - 1")
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor(out, "out", (torch.bfloat16,), (b, Hq, D))
+    need = attn_workspace_bytes(b, Hq, Hkv, D, pos0)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), k_cache.stride(0), k_cache.stride(1),
+                            v_cache.stride(0), v_cache.stride(1), b, Hq, Hkv, D, pos0, float(scale), _ptr(out),
+                            _ptr(workspace), wsb, _stream_ptr())
+    _raise(st, "attn_decode")
+    return out

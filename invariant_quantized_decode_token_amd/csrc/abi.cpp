@@ -126,6 +126,23 @@ size_t ws_lm_head(int64_t b, int64_t N, bool have_logits) {
 
 }  // namespace
 
+namespace {
+
+int attn_check(int64_t b, int64_t Hq, int64_t Hkv, int64_t D, int64_t pos0) {
+    if (b < 1 || b > 65535 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || pos0 < 0 || pos0 + b > (int64_t{1} << 30) ||
+        Hq > 65535 || Hkv > 65535)
+        return IQD_ERR_INVALID;
+    if (D != 128 || Hq / Hkv > 16) return IQD_ERR_UNSUPPORTED;
+    return IQD_OK;
+}
+
+// Bytes from a cache's base to the end of the last element read.
+size_t attn_cache_extent(int64_t cells, int64_t Hkv, int64_t D, int64_t cs, int64_t hs) {
+    return static_cast<size_t>((cells - 1) * cs + (Hkv - 1) * hs + D) * 2;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *iqd_status_str(int status) {
@@ -134,7 +151,7 @@ const char *iqd_status_str(int status) {
         case IQD_ERR_INVALID: return "IQD_ERR_INVALID: bad shape, null pointer, aliasing or group";
         case IQD_ERR_ALIGN: return "IQD_ERR_ALIGN: pointer misaligned";
         case IQD_ERR_RANGE: return "IQD_ERR_RANGE: K above IQD_K_MAX (int32 accumulator bound)";
-        case IQD_ERR_UNSUPPORTED: return "IQD_ERR_UNSUPPORTED: split_k not allowed for this shape";
+        case IQD_ERR_UNSUPPORTED: return "IQD_ERR_UNSUPPORTED: split_k or attention shape not supported";
         case IQD_ERR_WORKSPACE: return "IQD_ERR_WORKSPACE: workspace missing or too small";
         case IQD_ERR_HIP: return "IQD_ERR_HIP: HIP runtime call or launch failed";
         default: return "unknown iqd status";
@@ -320,6 +337,44 @@ int lm_head_argmax(const int8_t *q, const float *s_a, const int8_t *w, const flo
         if (e != hipSuccess) return hip_status(e);
     }
     return hip_status(iqd::launch_argmax_rows(logits, static_cast<int>(b), Ni, argmax, keys, hs));
+}
+
+size_t attn_workspace_bytes(int64_t b, int64_t Hq, int64_t Hkv, int64_t D, int64_t pos0) {
+    if (attn_check(b, Hq, Hkv, D, pos0) != IQD_OK) return 0;
+    return round16(iqd::attn_workspace_bytes(b, Hq, pos0));
+}
+
+int attn_decode(const void *q_bf16, const void *k_cache, const void *v_cache, int64_t k_cell_stride,
+                int64_t k_head_stride, int64_t v_cell_stride, int64_t v_head_stride, int64_t b, int64_t Hq,
+                int64_t Hkv, int64_t D, int64_t pos0, float scale, void *out_bf16, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    if (!q_bf16 || !k_cache || !v_cache || !out_bf16) return IQD_ERR_INVALID;
+    int st = attn_check(b, Hq, Hkv, D, pos0);
+    if (st != IQD_OK) return st;
+    if (!(scale == scale) || scale - scale != 0.0f) return IQD_ERR_INVALID;  // NaN or infinite
+    if (k_cell_stride < 0 || k_head_stride < 0 || v_cell_stride < 0 || v_head_stride < 0 ||
+        k_cell_stride > kIntMax || k_head_stride > kIntMax || v_cell_stride > kIntMax || v_head_stride > kIntMax)
+        return IQD_ERR_INVALID;
+    if (!aligned(q_bf16, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out_bf16, 16) ||
+        k_cell_stride % 8 || k_head_stride % 8 || v_cell_stride % 8 || v_head_stride % 8)
+        return IQD_ERR_ALIGN;
+    const size_t ws = round16(iqd::attn_workspace_bytes(b, Hq, pos0));
+    if (ws > 0) {
+        if (!workspace || workspace_bytes < ws) return IQD_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return IQD_ERR_ALIGN;
+    }
+    const int64_t cells = pos0 + b;
+    const size_t qbytes = static_cast<size_t>(b * Hq * D) * 2;
+    if (any_overlap({{out_bf16, qbytes}, {ws ? workspace : nullptr, ws}},
+                    {{q_bf16, qbytes}, {k_cache, attn_cache_extent(cells, Hkv, D, k_cell_stride, k_head_stride)},
+                     {v_cache, attn_cache_extent(cells, Hkv, D, v_cell_stride, v_head_stride)}}))
+        return IQD_ERR_INVALID;
+    clear_stale_error();
+    return hip_status(iqd::launch_attn_decode(
+        static_cast<const uint16_t *>(q_bf16), static_cast<const uint16_t *>(k_cache),
+        static_cast<const uint16_t *>(v_cache), k_cell_stride, k_head_stride, v_cell_stride, v_head_stride,
+        static_cast<int>(b), static_cast<int>(Hq), static_cast<int>(Hkv), static_cast<int>(pos0), scale,
+        static_cast<uint16_t *>(out_bf16), workspace, static_cast<hipStream_t>(stream)));
 }
 
 int pow2_requantize(const int8_t *w, const float *s_w, int64_t N, int64_t K, int8_t *w_out, float *s_out,

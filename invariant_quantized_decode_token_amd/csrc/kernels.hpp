@@ -61,6 +61,14 @@ hipError_t launch_blockq8_combine(const float *part, int b, int N, int split, ui
 int argmax_chunks(int N);
 hipError_t launch_argmax_rows(const uint16_t *logits, int b, int N, int32_t *out, uint64_t *part, hipStream_t st);
 
+// Decode attention in fixed 256-cell chunks (D = 128, Hq / Hkv <= 16).
+// Workspace: attn_workspace_bytes(b, Hq, pos0) bytes of chunk partials.
+int64_t attn_chunks(int64_t b, int64_t pos0);
+size_t attn_workspace_bytes(int64_t b, int64_t Hq, int64_t pos0);
+hipError_t launch_attn_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t kc, int64_t kh,
+                              int64_t vc, int64_t vh, int b, int Hq, int Hkv, int pos0, float scale, uint16_t *out,
+                              void *ws, hipStream_t st);
+
 hipError_t launch_pow2_requant(const int8_t *w, const float *s, int N, int K, int8_t *w_out,
                                float *s_out, hipStream_t st);
 

@@ -18,7 +18,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = iqd.header_functions()
     assert set(names) == {"quantize_activations", "w8a8_linear", "w8a8_linear_bf16", "blockq8_linear", "lm_head_argmax",
-                          "pow2_requantize", "iqd_workspace_bytes", "iqd_status_str", "iqd_last_hip_error"}
+                          "pow2_requantize", "iqd_workspace_bytes", "iqd_status_str", "iqd_last_hip_error",
+                          "attn_decode", "attn_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -131,3 +132,30 @@ def test_w8a8_bf16_validation(lib):
     assert call(b=40, q=0) == L.IQD_ERR_WORKSPACE             # b > 16: separate quantization needs q space
     ws = iqd.workspace_bytes(L.IQD_OP_W8A8_BF16, 40, 64, 1024, 1)
     assert ws == 40 * 1024 + (40 * 4 + 15) // 16 * 16
+
+
+def attn(lib, q=A, k=2 * A, v=3 * A, out=4 * A, ws=0, wsb=0, kc=1024, kh=128, vc=1024, vh=128, b=2, Hq=32, Hkv=8,
+         D=128, pos0=10, scale=0.088):
+    return lib.attn_decode(ptr(q), ptr(k), ptr(v), kc, kh, vc, vh, b, Hq, Hkv, D, pos0, scale, ptr(out), ptr(ws), wsb,
+                           None)
+
+
+def test_attn_validation(lib):
+    assert attn(lib, q=0) == L.IQD_ERR_INVALID
+    assert attn(lib, b=0) == L.IQD_ERR_INVALID
+    assert attn(lib, Hq=30) == L.IQD_ERR_INVALID              # not a multiple of Hkv
+    assert attn(lib, pos0=-1) == L.IQD_ERR_INVALID
+    assert attn(lib, scale=float("nan")) == L.IQD_ERR_INVALID
+    assert attn(lib, scale=float("inf")) == L.IQD_ERR_INVALID
+    assert attn(lib, D=64) == L.IQD_ERR_UNSUPPORTED
+    assert attn(lib, Hq=64, Hkv=2) == L.IQD_ERR_UNSUPPORTED   # 32 query heads per kv head
+    assert attn(lib, q=A + 8) == L.IQD_ERR_ALIGN
+    assert attn(lib, kc=1020) == L.IQD_ERR_ALIGN               # rows not 16-byte aligned
+    assert attn(lib, vh=4) == L.IQD_ERR_ALIGN
+    assert attn(lib, pos0=300) == L.IQD_ERR_WORKSPACE          # two chunks need partials
+    need = iqd.attn_workspace_bytes(2, 32, 8, 128, 300)
+    assert need == (2 * 32 * 2 * 2 * 4 + 255) // 256 * 256 + 2 * 32 * 2 * 128 * 4
+    assert attn(lib, pos0=300, ws=5 * A, wsb=need - 16) == L.IQD_ERR_WORKSPACE
+    assert attn(lib, out=A + 64) == L.IQD_ERR_INVALID          # output overlaps q
+    assert iqd.attn_workspace_bytes(2, 32, 8, 128, 10) == 0    # one chunk: the fast path
+    assert iqd.attn_workspace_bytes(2, 32, 8, 64, 300) == 0    # rejected shape
