@@ -463,6 +463,8 @@ int oracle_pow2_requant(const int8_t *w, const float *s_w, int64_t N, int64_t K,
  */
 
 #define ATTN_CHUNK 256
+#define ATTN_PART 64 /* a chunk's sums are formed in four parts of 64 cells */
+#define ATTN_PARTS 4
 
 /* e^x for x <= 0 (the only arguments the recipe forms) in binary32 operations only (every implementation that
  * performs the same operations gets the same bits).  Cody and Waite's
@@ -526,8 +528,10 @@ typedef struct {
  *   position p = pos0 + t; the row attends cells 0..p; chunk c holds cells
  *   [256 c, 256 c + 256) cut at p; the row has n = p / 256 + 1 chunks.
  *   Per chunk: s_j = score(q * scale, k_j); m_c = max_j s_j;
- *     e_j = E(s_j - m_c); l_c = sum_j e_j and o_c[d] = sum_j e_j v_j[d],
- *     both in increasing j from +0, o with fused multiply-adds.
+ *     e_j = E(s_j - m_c); the chunk is cut into four parts of 64 cells;
+ *     per part, l = sum_j e_j and o[d] = sum_j e_j v_j[d], both in increasing
+ *     j from +0 (o with fused multiply-adds; an empty part gives +0); then
+ *     l_c = (l_0 + l_1) + (l_2 + l_3) and o_c likewise.
  *   Merge in increasing c: M = max_c m_c, w_c = E(m_c - M);
  *     L = w_0 l_0, O[d] = w_0 o_0[d], then L = fma(w_c, l_c, L) and
  *     O[d] = fma(w_c, o_c[d], O[d]) for c = 1, 2, ...
@@ -537,12 +541,12 @@ typedef struct {
 static void attn_rows(attn_job *j) {
     const int64_t D = j->D, G = j->Hq / j->Hkv, nh = j->h1 - j->h0;
     float *qs = (float *)malloc(sizeof(float) * (size_t)D);
-    float *o = (float *)malloc(sizeof(float) * (size_t)D);
+    float *op = (float *)malloc(sizeof(float) * (size_t)(ATTN_PARTS * D));
     float *O = (float *)malloc(sizeof(float) * (size_t)D);
     float *s = (float *)malloc(sizeof(float) * ATTN_CHUNK);
-    if (!qs || !o || !O || !s) {
+    if (!qs || !op || !O || !s) {
         j->status = ORACLE_ERR_ARGS;
-        free(qs), free(o), free(O), free(s);
+        free(qs), free(op), free(O), free(s);
         return;
     }
     for (int64_t r = j->r0; r < j->r1; ++r) {
@@ -567,17 +571,28 @@ static void attn_rows(attn_job *j) {
                 s[cell - c0] = attn_score(qs, j->k + cell * j->kc + hk * j->kh, D);
                 m = fmaxf(m, s[cell - c0]);
             }
-            float l = 0.0f;
-            for (int64_t d = 0; d < D; ++d) o[d] = 0.0f;
-            for (int64_t cell = c0; cell < c1; ++cell) {
-                const float e = oracle_attn_exp(s[cell - c0] - m);
-                const uint16_t *vr = j->v + cell * j->vc + hk * j->vh;
-                l = l + e;
-                for (int64_t d = 0; d < D; ++d) o[d] = fmaf(e, oracle_bf16_to_f32(vr[d]), o[d]);
+            /* four parts of 64 cells, each summed in increasing j from +0 (an
+             * empty part is +0), then joined as (part 0 + part 1) + (part 2 +
+             * part 3) */
+            float lp[ATTN_PARTS];
+            for (int64_t k = 0; k < ATTN_PARTS; ++k) {
+                const int64_t a0 = c0 + k * ATTN_PART;
+                const int64_t a1 = (a0 + ATTN_PART < c1) ? a0 + ATTN_PART : c1;
+                float l = 0.0f;
+                float *ok = op + k * D;
+                for (int64_t d = 0; d < D; ++d) ok[d] = 0.0f;
+                for (int64_t cell = a0; cell < a1; ++cell) {
+                    const float e = oracle_attn_exp(s[cell - c0] - m);
+                    const uint16_t *vr = j->v + cell * j->vc + hk * j->vh;
+                    l = l + e;
+                    for (int64_t d = 0; d < D; ++d) ok[d] = fmaf(e, oracle_bf16_to_f32(vr[d]), ok[d]);
+                }
+                lp[k] = l;
             }
             mc[c] = m;
-            lc[c] = l;
-            memcpy(oc + c * D, o, sizeof(float) * (size_t)D);
+            lc[c] = (lp[0] + lp[1]) + (lp[2] + lp[3]);
+            for (int64_t d = 0; d < D; ++d)
+                oc[c * D + d] = (op[d] + op[D + d]) + (op[2 * D + d] + op[3 * D + d]);
             M = fmaxf(M, m);
         }
         float L = 0.0f;
@@ -595,7 +610,7 @@ static void attn_rows(attn_job *j) {
         for (int64_t d = 0; d < D; ++d) orow[d] = oracle_bf16_rne(f32_bits(O[d] / L));
         free(mc), free(lc), free(oc);
     }
-    free(qs), free(o), free(O), free(s);
+    free(qs), free(op), free(O), free(s);
 }
 
 static void *attn_worker(void *arg) {
