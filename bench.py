@@ -64,7 +64,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--detail", action="store_true", help="per-(layer, b) kernel timings")
     p.add_argument("--no-prefill", action="store_true", help="skip timing the b=512 prefill pass")
-    p.add_argument("--extra", action="store_true", help="also time the block-q8 and LM-head paths")
+    p.add_argument("--extra", action="store_true", help="also time the block-q8, LM-head and attention paths")
     p.add_argument("--calib", action="store_true",
                    help="end with one 256 MiB device-to-device copy (a known-size kernel for HBM counter scaling)")
     return p.parse_args()
@@ -306,6 +306,30 @@ def main():
             by = Ll.N * Ll.K + 4 * Ll.N
             ext.append({"op": "lm_head_argmax", "K": Ll.K, "N": Ll.N, "b": b, "us": round(us, 2),
                         "weight_GBs": round(by / (us * 1e-6) / 1e9, 1)})
+        # decode attention, Qwen3-8B heads (32 query, 8 kv, D = 128): enough cache
+        # copies in rotation to exceed the 256 MB Infinity Cache
+        name, Hq, Hkv, D = W.QWEN3_8B_ATTN
+        for cells in (4096, 32768):
+            kv_bytes = cells * Hkv * D * 2 * 2
+            ncopy = max(2, min(32, -(-512 * 2 ** 20 // kv_bytes)))
+            case = W.attn_case(W.SEED_ATTN + cells, 8, cells)
+            ks = [torch.from_numpy(case.k.view(np.int16)).view(torch.bfloat16).to(dev) for _ in range(ncopy)]
+            vs = [torch.from_numpy(case.v.view(np.int16)).view(torch.bfloat16).to(dev) for _ in range(ncopy)]
+            qa = torch.from_numpy(case.q.view(np.int16)).view(torch.bfloat16).to(dev)
+            for b in (1, 8):
+                oa = torch.empty((b, Hq, D), dtype=torch.bfloat16, device=dev)
+                wsa = torch.empty((max(16, iqd.attn_workspace_bytes(b, Hq, Hkv, D, cells - b)),), dtype=torch.uint8,
+                                  device=dev)
+
+                def at(b=b, oa=oa, wsa=wsa):
+                    for c in range(ncopy):
+                        iqd.attn_decode(qa[:b], ks[c], vs[c], cells - b, float(case.scale), out=oa, workspace=wsa)
+                g = capture(at)
+                g.replay()
+                us = time_graph(g, 10) * 1e3 / ncopy
+                ext.append({"op": "attn_decode", "cells": cells, "Hq": Hq, "Hkv": Hkv, "D": D, "b": b,
+                            "us": round(us, 2), "kv_GBs": round(kv_bytes / (us * 1e-6) / 1e9, 1)})
+            del ks, vs
         out["extra"] = ext
 
     if not args.no_cpu:

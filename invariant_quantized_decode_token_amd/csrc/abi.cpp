@@ -133,6 +133,9 @@ int attn_check(int64_t b, int64_t Hq, int64_t Hkv, int64_t D, int64_t pos0) {
         Hq > 65535 || Hkv > 65535)
         return IQD_ERR_INVALID;
     if (D != 128 || Hq / Hkv > 16) return IQD_ERR_UNSUPPORTED;
+    // launch sizes: (chunks x kv heads, padded) x row groups and b x Hq workgroups
+    const int64_t chunks = (pos0 + b - 1) / 256 + 1;
+    if ((chunks * Hkv + 8) * b > kIntMax || b * Hq > kIntMax) return IQD_ERR_UNSUPPORTED;
     return IQD_OK;
 }
 

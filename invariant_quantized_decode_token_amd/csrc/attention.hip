@@ -17,7 +17,9 @@
 //   s_j    = tree over 16 slices of (fma chain over the slice's 8 dims from +0)
 //   chunk c (cells [256c, 256c+256) cut at p):
 //     m_c  = max_j s_j,  e_j = E(s_j - m_c),
-//     l_c  = sum_j e_j and o_c[d] = sum_j e_j v_j[d] (fma), j increasing from +0
+//     per part k of 64 cells: l_k = sum_j e_j and o_k[d] = sum_j e_j v_j[d]
+//     (fma), j increasing from +0 (+0 for an empty part);
+//     l_c = (l_0 + l_1) + (l_2 + l_3), o_c likewise
 //   merge, c increasing: M = max m_c, w_c = E(m_c - M),
 //     L = w_0 l_0, O = w_0 o_0, then L = fma(w_c, l_c, L), O = fma(w_c, o_c, O)
 //   out[d] = bf16(O[d] / L)
@@ -25,9 +27,11 @@
 // polynomial, all in binary32 operations.  With one chunk the merge returns
 // o_0 / l_0 exactly, so the chunk kernel writes that directly.
 //
-// Layout: one workgroup per (chunk, kv head, group of up to 16 query rows);
+// Layout: one workgroup per (chunk, kv head, group of up to 4 or 16 query rows);
 // a row is (query token, query head) with the query heads of one kv head
-// adjacent.  The K and V chunk rows are read once per workgroup.
+// adjacent.  Wave w of the workgroup owns part w of the chunk (64 cells) and
+// issues all of that part's key and value loads before computing; the K and
+// V chunk rows are read once per workgroup.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -36,8 +40,10 @@ namespace {
 
 constexpr int kChunk = 256;
 constexpr int kD = 128;
-constexpr int kRows = 16;  // query rows per workgroup
-constexpr int kThreads = 256;
+constexpr int kXcds = 8;
+constexpr int kPart = 64;  // a chunk's sums are formed in four parts of 64 cells, one per wave
+constexpr int kParts = 4;
+constexpr int kThreads = kWave * kParts;
 
 // e^x for x <= 0, binary32 operations only (see the file header).
 __device__ __forceinline__ float attn_exp(float x) {
@@ -64,7 +70,7 @@ struct AttnArgs {
     const uint16_t *k;  // cell * kc + head * kh + d
     const uint16_t *v;
     int64_t kc, kh, vc, vh;
-    int b, Hq, G, pos0;
+    int b, Hq, Hkv, G, pos0;
     float scale;
     uint16_t *out;      // [b, Hq, 128]
     float *ml;          // [b * Hq][nc][2]: chunk max and sum (rows with >= 2 chunks)
@@ -72,10 +78,20 @@ struct AttnArgs {
     int nc;             // chunks of the longest row
 };
 
+// RM: the most query rows a workgroup holds (4 for single-token decode with
+// up to 4 query heads per kv head, 16 otherwise).
+template <int RM>
 __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
-    const int c = blockIdx.x, hk = blockIdx.y;
-    const int bq = kRows / a.G;                 // query tokens per workgroup
-    const int t0 = blockIdx.z * bq;
+    // Workgroups are dealt to the XCDs in turn; the row groups of one
+    // (chunk, kv head) take consecutive slots of one XCD, so its K and V rows
+    // come from that XCD's L2 after the first read.
+    const int bq = RM / a.G;                    // query tokens per workgroup
+    const int nrg = (a.b + bq - 1) / bq;        // row groups
+    const int id = blockIdx.x, xcd = id % kXcds, slot = id / kXcds;
+    const int tile = (slot / nrg) * kXcds + xcd, rg = slot % nrg;
+    if (tile >= a.nc * a.Hkv) return;           // padding slots of the last round
+    const int c = tile / a.Hkv, hk = tile % a.Hkv;
+    const int t0 = rg * bq;
     const int nq = min(bq, a.b - t0);
     const int R = nq * a.G;                     // rows of this workgroup
     const int j0 = c * kChunk;
@@ -85,9 +101,39 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
     const int tid = static_cast<int>(threadIdx.x);
     const int wave = tid / kWave, lane = tid % kWave;
 
-    __shared__ __attribute__((aligned(16))) float qs[kRows][kD];
-    __shared__ float sc[kRows][kChunk];
-    __shared__ float mrow[kRows], lrow[kRows];
+    __shared__ __attribute__((aligned(16))) float qs[RM][kD];
+    __shared__ __attribute__((aligned(16))) float sc[kChunk][RM];  // scores, then e: [cell][row]
+    __shared__ __attribute__((aligned(16))) float op[kParts][RM][kD];
+    __shared__ float lp[kParts][RM];
+    __shared__ float mrow[RM];
+
+    // Wave w owns part w: cells 64 w .. 64 w + 63 of the chunk, for the scores
+    // and for the value sums.  Its loads go out first, all at once: the values
+    // (lane: dims 2 lane, 2 lane + 1 of each cell), then the keys (four lanes
+    // per cell, lane `sub` holding dims 32 sub .. 32 sub + 31).  Cells past
+    // the last one read cell j0 instead (in range, never used).
+    const int pbase = kPart * wave;
+    uint32_t vw[kPart];
+    {
+        const uint32_t *vp = reinterpret_cast<const uint32_t *>(a.v + static_cast<int64_t>(j0) * a.vc + hk * a.vh) +
+                             lane;
+        const int64_t vstep = a.vc / 2;  // in 32-bit words
+#pragma unroll
+        for (int i = 0; i < kPart; ++i) {
+            const int jj = pbase + i;
+            vw[i] = vp[(jj < ncell ? jj : 0) * vstep];
+        }
+    }
+    const int cs = lane >> 2, sub = lane & 3;
+    v4i kw[4][4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const int jj = pbase + 16 * st + cs;
+        const int j = j0 + (jj < ncell ? jj : 0);
+        const v4i *kp = reinterpret_cast<const v4i *>(a.k + static_cast<int64_t>(j) * a.kc + hk * a.kh + 32 * sub);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kw[st][i] = kp[i];
+    }
 
     // Row r: token t0 + r / G, query head hk * G + r % G.
     for (int i = tid; i < R * kD; i += kThreads) {
@@ -97,131 +143,163 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
     }
     __syncthreads();
 
-    // Scores: four lanes per cell, lane `sub` holding dims 32 sub .. 32 sub + 31
-    // (slices 4 sub .. 4 sub + 3); 16 cells per wave and step.  Lanes past the
-    // chunk's last cell read cell j0 (in range) and store nothing.
-    {
-        const int cs = lane >> 2, sub = lane & 3;
-        for (int jb = wave * 16; jb < ncell; jb += 4 * 16) {
-            const int jj = jb + cs;
-            const bool valid = jj < ncell;
-            const int j = j0 + (valid ? jj : 0);
-            const v4i *kp = reinterpret_cast<const v4i *>(a.k + j * a.kc + hk * a.kh + 32 * sub);
-            float kf[32];
+    // Scores: per cell, slice chains of 8 fused multiply-adds, then the tree:
+    // two levels in the lane, two across the cell's four lanes.
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const v4i w = kp[i];
+    for (int st = 0; st < 4; ++st) {
+        const int jj = pbase + 16 * st + cs;
+        if (pbase + 16 * st >= ncell) break;  // wave-uniform
+        float kf[32];
 #pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    kf[8 * i + 2 * h] = bf16_to_f32(static_cast<uint32_t>(w[h]) & 0xFFFFu);
-                    kf[8 * i + 2 * h + 1] = __uint_as_float(static_cast<uint32_t>(w[h]) & 0xFFFF0000u);
-                }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                kf[8 * i + 2 * h] = bf16_to_f32(static_cast<uint32_t>(kw[st][i][h]) & 0xFFFFu);
+                kf[8 * i + 2 * h + 1] = __uint_as_float(static_cast<uint32_t>(kw[st][i][h]) & 0xFFFF0000u);
             }
-            for (int r = 0; r < R; ++r) {
-                const float4 *qr = reinterpret_cast<const float4 *>(&qs[r][32 * sub]);
-                float part[4];
+        for (int r = 0; r < R; ++r) {
+            const float4 *qr = reinterpret_cast<const float4 *>(&qs[r][32 * sub]);
+            float part[4];
 #pragma unroll
-                for (int sl = 0; sl < 4; ++sl) {
-                    const float4 x0 = qr[2 * sl], x1 = qr[2 * sl + 1];
-                    float acc = __builtin_fmaf(x0.x, kf[8 * sl + 0], 0.0f);
-                    acc = __builtin_fmaf(x0.y, kf[8 * sl + 1], acc);
-                    acc = __builtin_fmaf(x0.z, kf[8 * sl + 2], acc);
-                    acc = __builtin_fmaf(x0.w, kf[8 * sl + 3], acc);
-                    acc = __builtin_fmaf(x1.x, kf[8 * sl + 4], acc);
-                    acc = __builtin_fmaf(x1.y, kf[8 * sl + 5], acc);
-                    acc = __builtin_fmaf(x1.z, kf[8 * sl + 6], acc);
-                    acc = __builtin_fmaf(x1.w, kf[8 * sl + 7], acc);
-                    part[sl] = acc;
-                }
-                float s = (part[0] + part[1]) + (part[2] + part[3]);
-                s = s + xor_lane<1>(s);  // slices 0-7 with 8-15 of the pair of lanes
-                s = s + xor_lane<2>(s);  // the root
-                if (valid && sub == 0) sc[r][jj] = s;
+            for (int sl = 0; sl < 4; ++sl) {
+                const float4 x0 = qr[2 * sl], x1 = qr[2 * sl + 1];
+                float acc = __builtin_fmaf(x0.x, kf[8 * sl + 0], 0.0f);
+                acc = __builtin_fmaf(x0.y, kf[8 * sl + 1], acc);
+                acc = __builtin_fmaf(x0.z, kf[8 * sl + 2], acc);
+                acc = __builtin_fmaf(x0.w, kf[8 * sl + 3], acc);
+                acc = __builtin_fmaf(x1.x, kf[8 * sl + 4], acc);
+                acc = __builtin_fmaf(x1.y, kf[8 * sl + 5], acc);
+                acc = __builtin_fmaf(x1.z, kf[8 * sl + 6], acc);
+                acc = __builtin_fmaf(x1.w, kf[8 * sl + 7], acc);
+                part[sl] = acc;
             }
+            float s = (part[0] + part[1]) + (part[2] + part[3]);
+            s = s + xor_lane<1>(s);  // slices 0-7 with 8-15 of the pair of lanes
+            s = s + xor_lane<2>(s);  // the root
+            if (jj < ncell && sub == 0) sc[jj][r] = s;
         }
     }
     __syncthreads();
 
-    // Per row: the chunk maximum over its own cells, then e_j (0 past them).
-    for (int r = wave; r < R; r += 4) {
+    // Per row: the chunk maximum over its own cells, then e_j (+0 past them,
+    // to the end of the chunk; +0 for rows the workgroup does not hold).
+    for (int r = wave; r < RM; r += kParts) {
         const int p = a.pos0 + t0 + r / a.G;
-        const int ncr = min(ncell, p + 1 - j0);  // wave-uniform
-        if (ncr <= 0) continue;
+        const int ncr = r < R ? min(ncell, p + 1 - j0) : 0;  // wave-uniform
         float m = -__builtin_inff();
-        for (int i = lane; i < ncr; i += kWave) m = fmaxf(m, sc[r][i]);
+        for (int i = lane; i < ncr; i += kWave) m = fmaxf(m, sc[i][r]);
         m = fmaxf(m, xor_lane<1>(m));
         m = fmaxf(m, xor_lane<2>(m));
         m = fmaxf(m, xor_lane<4>(m));
         m = fmaxf(m, xor_lane<8>(m));
         m = fmaxf(m, xor_lane<16>(m));
         m = fmaxf(m, xor_lane<32>(m));
-        for (int i = lane; i < ncell; i += kWave) sc[r][i] = i < ncr ? attn_exp(sc[r][i] - m) : 0.0f;
+        for (int i = lane; i < kChunk; i += kWave) sc[i][r] = i < ncr ? attn_exp(sc[i][r] - m) : 0.0f;
         if (lane == 0) mrow[r] = m;
     }
     __syncthreads();
 
-    // l_r = sum of e_j in increasing j: one lane per row.
-    if (tid < R) {
-        const int p = a.pos0 + t0 + tid / a.G;
-        const int ncr = min(ncell, p + 1 - j0);
-        float l = 0.0f;
-        for (int j = 0; j < ncr; ++j) l = l + sc[tid][j];
-        lrow[tid] = l;
-    }
-
-    // o_r[d] = sum of e_j v_j[d] in increasing j.  Wave w owns rows w, w + 4,
-    // w + 8, w + 12; lane owns dims 2 lane, 2 lane + 1.  Whether cell j counts
-    // for a row is wave-uniform (a branch, not a select).
-    float o[4][2];
-    int ncr4[4];
+    // This wave's part: l and o[d] = sums of e_j and e_j v_j[d] over the
+    // part's cells in increasing j, from +0.  Cells outer (each value
+    // unpacked once), rows inner.  When every row attends the whole part no
+    // cell is skipped; otherwise a row's cells past its position leave its
+    // sums untouched (a select, so not even the sign of a zero changes).
+    {
+        int n[RM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        o[i][0] = 0.0f;
-        o[i][1] = 0.0f;
-        const int r = wave + 4 * i;
-        ncr4[i] = r < R ? min(ncell, a.pos0 + t0 + r / a.G + 1 - j0) : 0;
-    }
-    const uint32_t *vp = reinterpret_cast<const uint32_t *>(a.v + static_cast<int64_t>(j0) * a.vc + hk * a.vh) + lane;
-    const int64_t vstep = a.vc / 2;  // in 32-bit words
-    for (int j = 0; j < ncell; ++j) {
-        const uint32_t w = vp[j * vstep];
-        const float v0 = bf16_to_f32(w & 0xFFFFu), v1 = __uint_as_float(w & 0xFFFF0000u);
+        for (int r = 0; r < RM; ++r)
+            n[r] = r < R ? min(kPart, min(ncell, a.pos0 + t0 + r / a.G + 1 - j0) - pbase) : kPart;
+        int nmin = kPart;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (j < ncr4[i]) {
-                const float e = sc[wave + 4 * i][j];
-                o[i][0] = __builtin_fmaf(e, v0, o[i][0]);
-                o[i][1] = __builtin_fmaf(e, v1, o[i][1]);
+        for (int r = 0; r < RM; ++r) nmin = min(nmin, n[r]);
+        float o[RM][2];
+#pragma unroll
+        for (int r = 0; r < RM; ++r) o[r][0] = o[r][1] = 0.0f;
+        if (nmin == kPart) {
+#pragma unroll
+            for (int i = 0; i < kPart; ++i) {
+                const float v0 = bf16_to_f32(vw[i] & 0xFFFFu), v1 = __uint_as_float(vw[i] & 0xFFFF0000u);
+                const float4 *e4 = reinterpret_cast<const float4 *>(&sc[pbase + i][0]);
+#pragma unroll
+                for (int q4 = 0; q4 < RM / 4; ++q4) {
+                    const float4 e = e4[q4];
+                    o[4 * q4 + 0][0] = __builtin_fmaf(e.x, v0, o[4 * q4 + 0][0]);
+                    o[4 * q4 + 0][1] = __builtin_fmaf(e.x, v1, o[4 * q4 + 0][1]);
+                    o[4 * q4 + 1][0] = __builtin_fmaf(e.y, v0, o[4 * q4 + 1][0]);
+                    o[4 * q4 + 1][1] = __builtin_fmaf(e.y, v1, o[4 * q4 + 1][1]);
+                    o[4 * q4 + 2][0] = __builtin_fmaf(e.z, v0, o[4 * q4 + 2][0]);
+                    o[4 * q4 + 2][1] = __builtin_fmaf(e.z, v1, o[4 * q4 + 2][1]);
+                    o[4 * q4 + 3][0] = __builtin_fmaf(e.w, v0, o[4 * q4 + 3][0]);
+                    o[4 * q4 + 3][1] = __builtin_fmaf(e.w, v1, o[4 * q4 + 3][1]);
+                }
+            }
+        } else if (nmin < kPart) {
+#pragma unroll
+            for (int i = 0; i < kPart; ++i) {
+                const float v0 = bf16_to_f32(vw[i] & 0xFFFFu), v1 = __uint_as_float(vw[i] & 0xFFFF0000u);
+                const float4 *e4 = reinterpret_cast<const float4 *>(&sc[pbase + i][0]);
+#pragma unroll
+                for (int q4 = 0; q4 < RM / 4; ++q4) {
+                    const float4 e = e4[q4];
+                    const float ev[4] = {e.x, e.y, e.z, e.w};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int r = 4 * q4 + u;
+                        const float x0 = __builtin_fmaf(ev[u], v0, o[r][0]);
+                        const float x1 = __builtin_fmaf(ev[u], v1, o[r][1]);
+                        o[r][0] = i < n[r] ? x0 : o[r][0];
+                        o[r][1] = i < n[r] ? x1 : o[r][1];
+                    }
+                }
             }
         }
-    }
-    __syncthreads();  // lrow
-
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = wave + 4 * i;
-        if (ncr4[i] <= 0) continue;
+        for (int r = 0; r < RM; ++r)
+            if (r < R) reinterpret_cast<float2 *>(&op[wave][r][0])[lane] = make_float2(o[r][0], o[r][1]);
+        if (lane < R) {
+            // e is +0 past the row's cells, and l >= +0 throughout: adding those
+            // +0 terms leaves l as it is
+            float l = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kPart; ++i) l = l + sc[pbase + i][lane];
+            lp[wave][lane] = l;
+        }
+    }
+    __syncthreads();
+
+    // Join the parts, (0 + 1) + (2 + 3), and write: the output itself when the
+    // row has one chunk (what the merge would give), else the chunk partial.
+    for (int i = tid; i < R * (kD / 2); i += kThreads) {
+        const int r = i / (kD / 2), dp = i % (kD / 2);
         const int t = t0 + r / a.G, hq = hk * a.G + r % a.G;
         const int p = a.pos0 + t;
+        if (p < j0) continue;  // the row does not reach this chunk
+        const float2 o0 = reinterpret_cast<const float2 *>(&op[0][r][0])[dp];
+        const float2 o1 = reinterpret_cast<const float2 *>(&op[1][r][0])[dp];
+        const float2 o2 = reinterpret_cast<const float2 *>(&op[2][r][0])[dp];
+        const float2 o3 = reinterpret_cast<const float2 *>(&op[3][r][0])[dp];
+        const float ox = (o0.x + o1.x) + (o2.x + o3.x);
+        const float oy = (o0.y + o1.y) + (o2.y + o3.y);
+        const float l = (lp[0][r] + lp[1][r]) + (lp[2][r] + lp[3][r]);
         const int64_t row = static_cast<int64_t>(t) * a.Hq + hq;
-        if (p < kChunk) {  // one chunk: out = o / l, what the merge would give
-            const float l = lrow[r];
-            const uint32_t packed = static_cast<uint32_t>(bf16_rne(o[i][0] / l)) |
-                                    (static_cast<uint32_t>(bf16_rne(o[i][1] / l)) << 16);
-            reinterpret_cast<uint32_t *>(a.out + row * kD)[lane] = packed;
+        if (p < kChunk) {
+            const uint32_t packed =
+                static_cast<uint32_t>(bf16_rne(ox / l)) | (static_cast<uint32_t>(bf16_rne(oy / l)) << 16);
+            reinterpret_cast<uint32_t *>(a.out + row * kD)[dp] = packed;
         } else {
-            float *op = a.o + (row * a.nc + c) * kD;
-            reinterpret_cast<float2 *>(op)[lane] = make_float2(o[i][0], o[i][1]);
-            if (lane == 0) {
+            reinterpret_cast<float2 *>(a.o + (row * a.nc + c) * kD)[dp] = make_float2(ox, oy);
+            if (dp == 0) {
                 a.ml[(row * a.nc + c) * 2] = mrow[r];
-                a.ml[(row * a.nc + c) * 2 + 1] = lrow[r];
+                a.ml[(row * a.nc + c) * 2 + 1] = l;
             }
         }
     }
 }
 
 // Merge the chunk partials of every row with two or more chunks, in
-// increasing chunk order.  One wave per row; lane owns dims 2 lane, +1.
+// increasing chunk order.  One wave per row; lane owns dims 2 lane, +1.  The
+// maximum is an exact reduction (any order); the weights of 64 chunks are
+// formed a lane each, then applied in order.
 __global__ __launch_bounds__(kWave) void k_attn_merge(AttnArgs a) {
     const int64_t row = blockIdx.x;
     const int t = static_cast<int>(row / a.Hq);
@@ -230,23 +308,44 @@ __global__ __launch_bounds__(kWave) void k_attn_merge(AttnArgs a) {
     if (n < 2) return;
     const int lane = static_cast<int>(threadIdx.x);
     const float *ml = a.ml + row * a.nc * 2;
-    const float2 *op = reinterpret_cast<const float2 *>(a.o + row * a.nc * kD) + lane;
+    const float2 *opart = reinterpret_cast<const float2 *>(a.o + row * a.nc * kD) + lane;
+    __shared__ float wsh[kWave], lsh[kWave];
     float M = -__builtin_inff();
-    for (int c = 0; c < n; ++c) M = fmaxf(M, ml[2 * c]);
-    float L, O0, O1;
-    {
-        const float w = attn_exp(ml[0] - M);
-        const float2 oc = op[0];
-        L = w * ml[1];
-        O0 = w * oc.x;
-        O1 = w * oc.y;
-    }
-    for (int c = 1; c < n; ++c) {
-        const float w = attn_exp(ml[2 * c] - M);
-        const float2 oc = op[static_cast<int64_t>(c) * (kD / 2)];
-        L = __builtin_fmaf(w, ml[2 * c + 1], L);
-        O0 = __builtin_fmaf(w, oc.x, O0);
-        O1 = __builtin_fmaf(w, oc.y, O1);
+    for (int c = lane; c < n; c += kWave) M = fmaxf(M, ml[2 * c]);
+    M = fmaxf(M, xor_lane<1>(M));
+    M = fmaxf(M, xor_lane<2>(M));
+    M = fmaxf(M, xor_lane<4>(M));
+    M = fmaxf(M, xor_lane<8>(M));
+    M = fmaxf(M, xor_lane<16>(M));
+    M = fmaxf(M, xor_lane<32>(M));
+    float L = 0.0f, O0 = 0.0f, O1 = 0.0f;
+    for (int c0 = 0; c0 < n; c0 += kWave) {
+        const int cn = min(kWave, n - c0);
+        __syncthreads();
+        if (lane < cn) {
+            wsh[lane] = attn_exp(ml[2 * (c0 + lane)] - M);
+            lsh[lane] = ml[2 * (c0 + lane) + 1];
+        }
+        __syncthreads();
+        for (int i0 = 0; i0 < cn; i0 += 8) {
+            float2 oc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) oc[i] = opart[static_cast<int64_t>(c0 + min(i0 + i, cn - 1)) * (kD / 2)];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i0 + i >= cn) break;
+                const float w = wsh[i0 + i];
+                if (c0 + i0 + i == 0) {
+                    L = w * lsh[0];
+                    O0 = w * oc[i].x;
+                    O1 = w * oc[i].y;
+                } else {
+                    L = __builtin_fmaf(w, lsh[i0 + i], L);
+                    O0 = __builtin_fmaf(w, oc[i].x, O0);
+                    O1 = __builtin_fmaf(w, oc[i].y, O1);
+                }
+            }
+        }
     }
     const uint32_t packed =
         static_cast<uint32_t>(bf16_rne(O0 / L)) | (static_cast<uint32_t>(bf16_rne(O1 / L)) << 16);
@@ -278,6 +377,7 @@ hipError_t launch_attn_decode(const uint16_t *q, const uint16_t *k, const uint16
     a.vh = vh;
     a.b = b;
     a.Hq = Hq;
+    a.Hkv = Hkv;
     a.G = Hq / Hkv;
     a.pos0 = pos0;
     a.scale = scale;
@@ -287,9 +387,17 @@ hipError_t launch_attn_decode(const uint16_t *q, const uint16_t *k, const uint16
     const size_t mlb = static_cast<size_t>(b) * Hq * a.nc * 2 * sizeof(float);
     a.ml = merge ? static_cast<float *>(ws) : nullptr;
     a.o = merge ? reinterpret_cast<float *>(static_cast<char *>(ws) + (mlb + 255) / 256 * 256) : nullptr;
-    const int bq = kRows / a.G;
-    const dim3 grid(static_cast<unsigned>(a.nc), static_cast<unsigned>(Hkv), static_cast<unsigned>((b + bq - 1) / bq));
-    hipLaunchKernelGGL(k_attn_chunk, grid, dim3(kThreads), 0, st, a);
+    // rows per workgroup: 4 when every kv head's rows fit in 4, else 16
+    const bool small = a.G * b <= 4;
+    const int rm = small ? 4 : 16;
+    const int bq = rm / a.G;
+    const int64_t nrg = (b + bq - 1) / bq;
+    const int64_t tiles = static_cast<int64_t>(a.nc) * Hkv;
+    const int64_t wgs = (tiles + kXcds - 1) / kXcds * kXcds * nrg;  // every XCD gets whole tiles
+    if (small)
+        hipLaunchKernelGGL(k_attn_chunk<4>, dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_attn_chunk<16>, dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !merge) return e;
     hipLaunchKernelGGL(k_attn_merge, dim3(static_cast<unsigned>(b) * Hq), dim3(kWave), 0, st, a);
