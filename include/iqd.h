@@ -246,7 +246,8 @@ int pow2_requantize(const int8_t *w, const float *s_w, int64_t N, int64_t K, int
  *   out_bf16 out bf16 [b, Hq, D], contiguous, 16-byte aligned
  *   workspace    attn_workspace_bytes(b, Hq, Hkv, D, pos0) bytes, 16-byte
  *                aligned (none when pos0 + b <= 256): fp32 chunk partials
- * Supported: D = 128; Hq a multiple of Hkv with Hq / Hkv <= 16; b * Hq and
+ * Supported: D = 128; Hq a multiple of Hkv with Hq / Hkv <= 16; cell
+ * strides below 2^22 elements; b * Hq and
  * (chunks * Hkv + 8) * b below 2^31, chunks = (pos0 + b - 1) / 256 + 1 (else
  * IQD_ERR_UNSUPPORTED); 1 <= b <= 65535; 0 <= pos0 and pos0 + b <= 2^30;
  * scale finite.

@@ -65,6 +65,14 @@ __device__ __forceinline__ float attn_exp(float x) {
     return n < -125.0f ? 0.0f : p * two_n;
 }
 
+typedef __attribute__((address_space(3))) int8_t lds_i8;
+
+// Buffer resource over [base, base + bytes): loads past the end read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void *base, int64_t bytes) {
+    const int nr = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : static_cast<int>(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, nr, 0x00020000);
+}
+
 struct AttnArgs {
     const uint16_t *q;  // [b, Hq, 128]
     const uint16_t *k;  // cell * kc + head * kh + d
@@ -106,6 +114,10 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) float op[kParts][RM][kD];
     __shared__ float lp[kParts][RM];
     __shared__ float mrow[RM];
+    // RM == 4: each part's values staged in LDS as [cell][64 words] (16-byte
+    // direct-to-LDS loads: a quarter of the load instructions of 4-byte ones)
+    constexpr bool kStageV = RM == 4;
+    __shared__ __attribute__((aligned(16))) uint32_t vst[kStageV ? kParts * kPart * (kD / 2) : 1];
 
     // Wave w owns part w: cells 64 w .. 64 w + 63 of the chunk, for the scores
     // and for the value sums.  Its loads go out first, all at once: the values
@@ -113,8 +125,20 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
     // per cell, lane `sub` holding dims 32 sub .. 32 sub + 31).  Cells past
     // the last one read cell j0 instead (in range, never used).
     const int pbase = kPart * wave;
-    uint32_t vw[kPart];
-    {
+    uint32_t vw[kStageV ? 1 : kPart];
+    if constexpr (kStageV) {
+        // instruction i: lane L loads bytes 16 (L % 16) .. + 15 of cell
+        // 4 i + L / 16 of the part, landing at word 64 (4 i + L / 16) + 4 (L % 16)
+        const __amdgpu_buffer_rsrc_t vr =
+            attn_rsrc(a.v + static_cast<int64_t>(j0) * a.vc + hk * a.vh, static_cast<int64_t>(kChunk) * a.vc * 2);
+#pragma unroll
+        for (int i = 0; i < kPart / 4; ++i) {
+            const int jj = pbase + 4 * i + (lane >> 4);
+            const uint32_t off = static_cast<uint32_t>((jj < ncell ? jj : 0) * a.vc * 2 + 16 * (lane & 15));
+            lds_i8 *dst = (lds_i8 *)(vst + (wave * kPart + 4 * i) * (kD / 2));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, dst, 16, off, 0, 0, 0);
+        }
+    } else {
         const uint32_t *vp = reinterpret_cast<const uint32_t *>(a.v + static_cast<int64_t>(j0) * a.vc + hk * a.vh) +
                              lane;
         const int64_t vstep = a.vc / 2;  // in 32-bit words
@@ -157,7 +181,9 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
                 kf[8 * i + 2 * h] = bf16_to_f32(static_cast<uint32_t>(kw[st][i][h]) & 0xFFFFu);
                 kf[8 * i + 2 * h + 1] = __uint_as_float(static_cast<uint32_t>(kw[st][i][h]) & 0xFFFF0000u);
             }
-        for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+            if (r >= R) break;  // wave-uniform
             const float4 *qr = reinterpret_cast<const float4 *>(&qs[r][32 * sub]);
             float part[4];
 #pragma unroll
@@ -215,10 +241,17 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
         float o[RM][2];
 #pragma unroll
         for (int r = 0; r < RM; ++r) o[r][0] = o[r][1] = 0.0f;
+        auto vword = [&](int i) __attribute__((always_inline)) {
+            if constexpr (kStageV)
+                return vst[(wave * kPart + i) * (kD / 2) + lane];
+            else
+                return vw[i];
+        };
         if (nmin == kPart) {
 #pragma unroll
             for (int i = 0; i < kPart; ++i) {
-                const float v0 = bf16_to_f32(vw[i] & 0xFFFFu), v1 = __uint_as_float(vw[i] & 0xFFFF0000u);
+                const uint32_t w = vword(i);
+                const float v0 = bf16_to_f32(w & 0xFFFFu), v1 = __uint_as_float(w & 0xFFFF0000u);
                 const float4 *e4 = reinterpret_cast<const float4 *>(&sc[pbase + i][0]);
 #pragma unroll
                 for (int q4 = 0; q4 < RM / 4; ++q4) {
@@ -236,7 +269,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
         } else if (nmin < kPart) {
 #pragma unroll
             for (int i = 0; i < kPart; ++i) {
-                const float v0 = bf16_to_f32(vw[i] & 0xFFFFu), v1 = __uint_as_float(vw[i] & 0xFFFF0000u);
+                const uint32_t w = vword(i);
+                const float v0 = bf16_to_f32(w & 0xFFFFu), v1 = __uint_as_float(w & 0xFFFF0000u);
                 const float4 *e4 = reinterpret_cast<const float4 *>(&sc[pbase + i][0]);
 #pragma unroll
                 for (int q4 = 0; q4 < RM / 4; ++q4) {
@@ -310,8 +344,17 @@ __global__ __launch_bounds__(kWave) void k_attn_merge(AttnArgs a) {
     const float *ml = a.ml + row * a.nc * 2;
     const float2 *opart = reinterpret_cast<const float2 *>(a.o + row * a.nc * kD) + lane;
     __shared__ float wsh[kWave], lsh[kWave];
-    float M = -__builtin_inff();
-    for (int c = lane; c < n; c += kWave) M = fmaxf(M, ml[2 * c]);
+    // The first chunks' values go out before anything waits.
+    float2 oc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) oc[i] = opart[static_cast<int64_t>(min(i, n - 1)) * (kD / 2)];
+    float mine_m = -__builtin_inff(), mine_l = 0.0f;
+    if (lane < n) {
+        mine_m = ml[2 * lane];
+        mine_l = ml[2 * lane + 1];
+    }
+    float M = mine_m;
+    for (int c = lane + kWave; c < n; c += kWave) M = fmaxf(M, ml[2 * c]);
     M = fmaxf(M, xor_lane<1>(M));
     M = fmaxf(M, xor_lane<2>(M));
     M = fmaxf(M, xor_lane<4>(M));
@@ -323,14 +366,17 @@ __global__ __launch_bounds__(kWave) void k_attn_merge(AttnArgs a) {
         const int cn = min(kWave, n - c0);
         __syncthreads();
         if (lane < cn) {
-            wsh[lane] = attn_exp(ml[2 * (c0 + lane)] - M);
-            lsh[lane] = ml[2 * (c0 + lane) + 1];
+            const float m = c0 == 0 ? mine_m : ml[2 * (c0 + lane)];
+            wsh[lane] = attn_exp(m - M);
+            lsh[lane] = c0 == 0 ? mine_l : ml[2 * (c0 + lane) + 1];
         }
         __syncthreads();
         for (int i0 = 0; i0 < cn; i0 += 8) {
-            float2 oc[8];
+            if (c0 + i0 > 0) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) oc[i] = opart[static_cast<int64_t>(c0 + min(i0 + i, cn - 1)) * (kD / 2)];
+                for (int i = 0; i < 8; ++i)
+                    oc[i] = opart[static_cast<int64_t>(c0 + min(i0 + i, cn - 1)) * (kD / 2)];
+            }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 if (i0 + i >= cn) break;
