@@ -83,6 +83,10 @@ def _load():
         "oracle_pow2_nearest": (f32, [f32]),
         "oracle_pow2_requant": (ctypes.c_int, [P, P, I64, I64, P, P]),
         "oracle_attn_exp": (f32, [f32]),
+        "oracle_e4m3_to_f32": (f32, [ctypes.c_uint8]),
+        "oracle_f32_to_e4m3": (ctypes.c_uint8, [f32]),
+        "oracle_quantize_fp8": (ctypes.c_int, [P, I64, I64, P, P]),
+        "oracle_fp8_linear": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, ctypes.c_int]),
         "oracle_attn_decode": (ctypes.c_int, [P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, I64, f32, I64, I64,
                                               P, ctypes.c_int]),
     }
@@ -294,3 +298,37 @@ def attn_decode(q, k_cache, v_cache, pos0: int, scale, heads=None, nthreads: int
     _check(_load().oracle_attn_decode(_ptr(q), kp, vp, kc, kh, vc, vh, b, Hq, Hkv, D, pos0, float(np.float32(scale)),
                                       h0, h1, _ptr(out), nthreads), "attn_decode")
     return out
+
+
+# --- FP8 (E4M3) W8A8 linear with the fixed tree ----------------------------------
+
+def e4m3_to_f32(code: int) -> np.float32:
+    return np.float32(_load().oracle_e4m3_to_f32(int(code) & 0xFF))
+
+
+def f32_to_e4m3(x) -> int:
+    return int(_load().oracle_f32_to_e4m3(float(np.float32(x))))
+
+
+def quantize_fp8(x_bits: np.ndarray):
+    """bf16 bits [b, K] -> (e4m3 codes uint8 [b, K], s_a fp32 [b])."""
+    x = _arr(x_bits, np.uint16)
+    b, K = x.shape
+    q = np.empty((b, K), np.uint8)
+    s = np.empty((b,), np.float32)
+    _check(_load().oracle_quantize_fp8(_ptr(x), b, K, _ptr(q), _ptr(s)), "quantize_fp8")
+    return q, s
+
+
+def fp8_linear(q, s_a, w, s_w, nthreads: int = 0) -> np.ndarray:
+    """e4m3 q [b, K], s_a [b], e4m3 w [N, K], s_w [N] -> y bf16 bits [b, N]."""
+    q = _arr(q, np.uint8)
+    w = _arr(w, np.uint8)
+    s_a = _arr(s_a, np.float32)
+    s_w = _arr(s_w, np.float32)
+    b, K = q.shape
+    N = w.shape[0]
+    y = np.empty((b, N), np.uint16)
+    _check(_load().oracle_fp8_linear(_ptr(q), _ptr(s_a), _ptr(w), _ptr(s_w), b, N, K, _ptr(y), nthreads),
+           "fp8_linear")
+    return y

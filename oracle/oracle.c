@@ -656,3 +656,147 @@ int oracle_attn_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v, 
         if (jobs[i].status != ORACLE_OK) status = jobs[i].status;
     return status;
 }
+
+/* ------------------------------------------------------------------------ */
+/* FP8 (E4M3) W8A8 linear with a fixed summation tree.                        */
+/* ------------------------------------------------------------------------ */
+/*
+ * Sources:
+ *  [P2] "My speculative decoder got slower", "The FP8 kernel that was secretly
+ *       FP16" and "A trained drafter and two matmul schedules": projection
+ *       weights in FP8; "Two matmul schedules that survived": with split-K the
+ *       running float sum is rounded at points set by the block size, so
+ *       schedules differ in the last bits.
+ *  [P3] "Deterministic LLM Inference Across GPU Kernels ...", Abstract: across
+ *       FP8 GEMM implementations the differences grow with the reduction depth
+ *       (unlike int8, whose accumulation is exact).
+ *
+ * Readings: the format is OCP E4M3 (1 sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, no infinities, S.1111.111 is NaN, largest finite 448).
+ * Activations are quantized per token like the int8 path with 448 in place
+ * of 127; weights come with one fp32 scale per row.  The product of two E4M3
+ * values is exact in binary32 (4 + 4 significant bits, exponents within
+ * [-18, 18]), so only the summation order needs fixing: K is cut into groups
+ * of 16; each group sum adds its products in increasing k from +0 (one
+ * rounding per addition); the K/16 group sums are the leaves of the canonical
+ * tree (zero-padded to a power of two, adjacent pairs); the epilogue is the
+ * linear layer's, bf16(fl(fl(root * s_a) * s_w)).
+ */
+
+float oracle_e4m3_to_f32(uint8_t c) {
+    const int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    float v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexpf((float)m, -9); /* subnormal: m * 2^-9 */
+    else
+        v = ldexpf((float)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* Nearest finite E4M3 value, ties to the even code (mantissa bit 0 clear);
+ * magnitudes past 448 saturate to 448; the sign is kept (-0 gives 0x80); NaN
+ * gives 0x7F with its sign.  By exhaustive search over the 127 non-negative
+ * finite codes; differences are exact in double. */
+uint8_t oracle_f32_to_e4m3(float x) {
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    if (isnan(x)) return (uint8_t)(sign | 0x7F);
+    const double a = fabs((double)x);
+    int best = 0;
+    double bd = a; /* distance to +0 */
+    for (int c = 1; c < 0x7F; ++c) {
+        const double d = fabs(a - (double)oracle_e4m3_to_f32((uint8_t)c));
+        if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+            bd = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* Per-token FP8 quantization: s = fl(amax / 448), q = e4m3(fl(x / s)); an
+ * all-zero token gives s = 0 and q = +0 codes. */
+int oracle_quantize_fp8(const uint16_t *x, int64_t b, int64_t K, uint8_t *q, float *s) {
+    if (!x || !q || !s || b < 1 || K < 1) return ORACLE_ERR_ARGS;
+    for (int64_t t = 0; t < b; ++t) {
+        const uint16_t *xr = x + t * K;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            const float v = fabsf(oracle_bf16_to_f32(xr[k]));
+            if (v > amax) amax = v;
+        }
+        const float sc = amax / 448.0f;
+        s[t] = sc;
+        for (int64_t k = 0; k < K; ++k)
+            q[t * K + k] = sc == 0.0f ? 0x00 : oracle_f32_to_e4m3(oracle_bf16_to_f32(xr[k]) / sc);
+    }
+    return ORACLE_OK;
+}
+
+/* Sum of one 16-element group: products in increasing k added from +0. */
+static float fp8_group_sum(const uint8_t *a, const uint8_t *w) {
+    float s = 0.0f;
+    for (int i = 0; i < 16; ++i) s = s + oracle_e4m3_to_f32(a[i]) * oracle_e4m3_to_f32(w[i]);
+    return s;
+}
+
+typedef struct {
+    const uint8_t *q, *w;
+    const float *sa, *sw;
+    int64_t b, N, K;
+    uint16_t *y;
+    int64_t n0, n1;
+    int status;
+} fp8_job;
+
+static void *fp8_worker(void *arg) {
+    fp8_job *j = (fp8_job *)arg;
+    const int64_t G = j->K / 16;
+    float *leaf = (float *)malloc(sizeof(float) * (size_t)G);
+    if (!leaf) {
+        j->status = ORACLE_ERR_ARGS;
+        return NULL;
+    }
+    for (int64_t n = j->n0; n < j->n1; ++n)
+        for (int64_t t = 0; t < j->b; ++t) {
+            for (int64_t g = 0; g < G; ++g) leaf[g] = fp8_group_sum(j->q + t * j->K + 16 * g, j->w + n * j->K + 16 * g);
+            const float root = oracle_tree_sum(leaf, G);
+            const float u = root * j->sa[t];
+            j->y[t * j->N + n] = oracle_bf16_rne(f32_bits(u * j->sw[n]));
+        }
+    free(leaf);
+    return NULL;
+}
+
+/* q e4m3 [b, K], s_a fp32 [b], w e4m3 [N, K], s_w fp32 [N] -> y bf16 [b, N];
+ * K a multiple of 16.  Threads split output rows only. */
+int oracle_fp8_linear(const uint8_t *q, const float *s_a, const uint8_t *w, const float *s_w, int64_t b, int64_t N,
+                      int64_t K, uint16_t *y, int nthreads) {
+    if (!q || !s_a || !w || !s_w || !y || b < 1 || N < 1 || K < 16 || K % 16 != 0) return ORACLE_ERR_ARGS;
+    if (nthreads <= 0) nthreads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > N) nthreads = (int)N;
+    fp8_job jobs[256];
+    pthread_t th[256];
+    int started[256];
+    for (int i = 0; i < nthreads; ++i) {
+        fp8_job jb = {q, w, s_a, s_w, b, N, K, y, N * i / nthreads, N * (i + 1) / nthreads, ORACLE_OK};
+        jobs[i] = jb;
+        started[i] = 0;
+    }
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, fp8_worker, &jobs[i]) == 0)
+            started[i] = 1;
+        else
+            fp8_worker(&jobs[i]);
+    }
+    fp8_worker(&jobs[0]);
+    int status = ORACLE_OK;
+    for (int i = 1; i < nthreads; ++i)
+        if (started[i]) pthread_join(th[i], NULL);
+    for (int i = 0; i < nthreads; ++i)
+        if (jobs[i].status != ORACLE_OK) status = jobs[i].status;
+    return status;
+}

@@ -14,6 +14,12 @@ Recipes (numpy ``Generator(PCG64(seed))``; draws happen in the order listed):
   * outlier channels: ``round(0.01 * K)`` channel indices from a seeded
     permutation, the same for every token, scaled by 20 in fp32 and rounded
     to bf16 again;
+  * FP8 (E4M3) weights, drawn as codes: sign uniform, exponent field
+    ``rint(normal(12.5, 1.5))`` clipped to [0, 15], mantissa uniform on
+    [0, 7], the NaN code (exponent 15, mantissa 7) replaced by the largest
+    finite one, 0x7E; magnitudes then cluster a few octaves below 448, as for
+    weights quantized per row at amax / 448.  Per-row fp32 scales
+    log-uniform on [1e-5, 1e-3];
   * decode attention: q, k and v ``standard_normal`` rounded to bf16 (the
     post-norm, post-rotary statistics of a Qwen3 layer are of that order);
     cache slots past the cells in use hold NaN bit patterns (0x7FC0), so a
@@ -51,6 +57,7 @@ SEED_BQ8 = 3001
 SEED_14B = 4001
 SEED_LM_HEAD = 5001
 SEED_ATTN = 6001
+SEED_FP8 = 7001
 
 TOKENS_TINY = 5
 TOKENS_8B = 512
@@ -254,3 +261,36 @@ def attn_case(seed: int, b: int, cells: int, Hq: int = 32, Hkv: int = 8, D: int 
     k[:cells] = normal_bf16(g, cells * Hkv, D).reshape(cells, Hkv, D)
     v[:cells] = normal_bf16(g, cells * Hkv, D).reshape(cells, Hkv, D)
     return AttnCase(q, k, v, cells - b, np.float32(1.0 / np.sqrt(np.float64(D))))
+
+
+# -- FP8 (E4M3) weights ------------------------------------------------------------
+
+def e4m3_weight_codes(g: np.random.Generator, N: int, K: int) -> np.ndarray:
+    sign = g.integers(0, 2, (N, K)).astype(np.uint8)
+    exp = np.clip(np.rint(g.normal(12.5, 1.5, (N, K))), 0, 15).astype(np.uint8)
+    man = g.integers(0, 8, (N, K)).astype(np.uint8)
+    codes = (sign << 7) | (exp << 3) | man
+    nan = (codes & 0x7F) == 0x7F
+    codes[nan] = (codes[nan] & 0x80) | 0x7E
+    return codes
+
+
+@dataclass
+class FP8Layer:
+    name: str
+    K: int
+    N: int
+    w: np.ndarray        # e4m3 codes uint8 [N, K]
+    s_w: np.ndarray      # fp32 [N]
+    x: np.ndarray        # bf16 bits [T, K]
+
+
+def fp8_layer(i: int, tokens: int = 16) -> FP8Layer:
+    """Qwen3-8B-shaped layer i with FP8 weights; activations as the W8A8 layers."""
+    name, K, N = QWEN3_8B[i]
+    g = rng(SEED_FP8 + i)
+    w = e4m3_weight_codes(g, N, K)
+    s_w = log_uniform_scales(g, N, 1e-5, 1e-3)
+    x = normal_bf16(g, tokens, K)
+    x, _ = add_outlier_channels(g, x)
+    return FP8Layer(name, K, N, w, s_w, x)
