@@ -67,7 +67,7 @@ typedef enum {
 } iqd_status;
 
 /* Operation codes for iqd_workspace_bytes. */
-enum { IQD_OP_W8A8 = 1, IQD_OP_BLOCKQ8 = 2, IQD_OP_LM_HEAD = 3, IQD_OP_W8A8_BF16 = 4 };
+enum { IQD_OP_W8A8 = 1, IQD_OP_BLOCKQ8 = 2, IQD_OP_LM_HEAD = 3, IQD_OP_W8A8_BF16 = 4, IQD_OP_FP8 = 5 };
 
 #define IQD_K_MAX 131071
 #define IQD_SPLIT_K_MAX 64
@@ -208,6 +208,45 @@ int lm_head_argmax(const int8_t *q, const float *s_a, const int8_t *w, const flo
  */
 int pow2_requantize(const int8_t *w, const float *s_w, int64_t N, int64_t K, int8_t *w_out,
                     float *s_out, void *stream);
+
+/*
+ * quantize_fp8 - per-token FP8 (OCP E4M3) quantization of bf16 activations.
+ *
+ * [P2 "A trained drafter and two matmul schedules"]: projection weights in FP8,
+ * the activations with them.  Per token: s = fl(amax / 448) (448 is the
+ * largest finite E4M3), q = e4m3(fl(x / s)) rounded to nearest with ties to
+ * the even code, saturating at 448, the sign kept (-0 gives 0x80); an
+ * all-zero token gives s = 0 and +0 codes.
+ *
+ *   x_bf16 in bf16 [b, K] (16-byte aligned)  ->  q out E4M3 [b, K], s_a out fp32 [b]
+ * K a multiple of 16.
+ */
+int quantize_fp8(const void *x_bf16, int64_t b, int64_t K, uint8_t *q, float *s_a, void *stream);
+
+/*
+ * fp8_linear - FP8 (E4M3) W8A8 linear with a fixed summation tree.
+ *
+ * [P2 "Two matmul schedules that survived"]: split-K and the step size move
+ * the rounding points of a float sum; [P3 Abstract]: FP8 differences between
+ * implementations grow with the reduction depth.  The product of two E4M3
+ * values is exact in binary32, so the order is all that can differ; it is
+ * fixed: K in groups of 16, each group's products added in increasing k
+ * from +0; the K/16 group sums are the leaves of the canonical tree (zero-
+ * padded to L = 2^ceil(log2(K/16)) leaves, adjacent pairs); then
+ * y = bf16(fl(fl(root * s_a) * s_w)), nearest even.
+ *
+ *   q      in  E4M3 [b, K]      s_a  in  fp32 [b]
+ *   w      in  E4M3 [N, K]      s_w  in  fp32 [N]
+ *   y_bf16 out bf16 [b, N]
+ *   split_k    1, or (b <= 16) a power of two with 64 * split_k <= L: split s
+ *              owns the aligned subtree of leaves [s L / split_k, (s+1) L /
+ *              split_k); a second kernel folds the top levels and applies the
+ *              epilogue.  Workspace: iqd_workspace_bytes(IQD_OP_FP8, ...).
+ * K a multiple of 16, 16 <= K <= IQD_K_MAX; any b (tokens in launches of 16).
+ * NaN codes (S.1111.111) give unspecified results.
+ */
+int fp8_linear(const uint8_t *q, const float *s_a, const uint8_t *w, const float *s_w, int64_t b, int64_t N,
+               int64_t K, void *y_bf16, int32_t split_k, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * attn_decode - decode / speculative-verify attention over a bf16 KV cache,

@@ -27,6 +27,7 @@ IQD_OP_W8A8 = 1
 IQD_OP_BLOCKQ8 = 2
 IQD_OP_LM_HEAD = 3
 IQD_OP_W8A8_BF16 = 4
+IQD_OP_FP8 = 5
 
 IQD_K_MAX = 131071
 IQD_SPLIT_K_MAX = 64
@@ -55,6 +56,8 @@ SIGNATURES = {
     "blockq8_linear": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]),
     "lm_head_argmax": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, P, SZ, P]),
     "pow2_requantize": (ctypes.c_int, [P, P, I64, I64, P, P, P]),
+    "quantize_fp8": (ctypes.c_int, [P, I64, I64, P, P, P]),
+    "fp8_linear": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]),
     "attn_decode": (ctypes.c_int, [P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, I64, ctypes.c_float, P, P, SZ,
                                    P]),
     "attn_workspace_bytes": (SZ, [I64, I64, I64, I64, I64]),
@@ -317,3 +320,41 @@ def attn_decode(q, k_cache, v_cache, pos0: int, scale: float, out=None, workspac
                             _ptr(workspace), wsb, _stream_ptr())
     _raise(st, "attn_decode")
     return out
+
+
+def quantize_fp8(x, q=None, scale=None):
+    """bf16 [b, K] -> (E4M3 codes uint8 [b, K], s_a fp32 [b])."""
+    torch = _torch()
+    _check_tensor(x, "x", (torch.bfloat16,))
+    b, K = x.shape
+    if q is None:
+        q = torch.empty((b, K), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((b,), dtype=torch.float32, device=x.device)
+    _check_tensor(q, "q", (torch.uint8,), (b, K))
+    _check_tensor(scale, "scale", (torch.float32,), (b,))
+    st = load().quantize_fp8(_ptr(x), b, K, _ptr(q), _ptr(scale), _stream_ptr())
+    _raise(st, "quantize_fp8")
+    return q, scale
+
+
+def fp8_linear(q, s_a, w, s_w, split_k: int = 1, y=None, workspace=None):
+    """E4M3 q [b, K], s_a [b], E4M3 w [N, K], s_w [N] -> y bf16 [b, N]."""
+    torch = _torch()
+    _check_tensor(q, "q", (torch.uint8,))
+    b, K = q.shape
+    N = w.shape[0]
+    _check_tensor(s_a, "s_a", (torch.float32,), (b,))
+    _check_tensor(w, "w", (torch.uint8,), (N, K))
+    _check_tensor(s_w, "s_w", (torch.float32,), (N,))
+    if y is None:
+        y = torch.empty((b, N), dtype=torch.bfloat16, device=q.device)
+    _check_tensor(y, "y", (torch.bfloat16,), (b, N))
+    need = workspace_bytes(IQD_OP_FP8, b, N, K, split_k)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().fp8_linear(_ptr(q), _ptr(s_a), _ptr(w), _ptr(s_w), b, N, K, _ptr(y), split_k, _ptr(workspace), wsb,
+                           _stream_ptr())
+    _raise(st, "fp8_linear")
+    return y

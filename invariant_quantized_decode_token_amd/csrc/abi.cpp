@@ -67,6 +67,15 @@ bool any_overlap(std::initializer_list<Buf> outs, std::initializer_list<Buf> ins
 
 bool is_pow2(int64_t v) { return v >= 1 && (v & (v - 1)) == 0; }
 
+int fp8_split_ok(int64_t b, int64_t K, int32_t split) {
+    if (split == 1) return IQD_OK;
+    int64_t L = 1;
+    while (L < K / 16) L *= 2;
+    if (b > 16 || !is_pow2(split) || split > IQD_SPLIT_K_MAX || 64 * static_cast<int64_t>(split) > L)
+        return IQD_ERR_UNSUPPORTED;
+    return IQD_OK;
+}
+
 int64_t pow2_ceil(int64_t v) {
     int64_t L = 1;
     while (L < v) L *= 2;
@@ -175,6 +184,10 @@ size_t iqd_workspace_bytes(int op, int64_t b, int64_t N, int64_t K, int32_t spli
             return ws_lm_head(b, N, false);
         case IQD_OP_W8A8_BF16:
             return ws_w8a8_bf16(b, K);
+        case IQD_OP_FP8:
+            return fp8_split_ok(b, K, split_k) == IQD_OK && split_k > 1
+                       ? round16(static_cast<size_t>(split_k) * b * N * 4)
+                       : 0;
         default:
             return 0;
     }
@@ -380,6 +393,57 @@ int attn_decode(const void *q_bf16, const void *k_cache, const void *v_cache, in
         static_cast<const uint16_t *>(v_cache), k_cell_stride, k_head_stride, v_cell_stride, v_head_stride,
         static_cast<int>(b), static_cast<int>(Hq), static_cast<int>(Hkv), static_cast<int>(pos0), scale,
         static_cast<uint16_t *>(out_bf16), workspace, static_cast<hipStream_t>(stream)));
+}
+
+int quantize_fp8(const void *x_bf16, int64_t b, int64_t K, uint8_t *q, float *s_a, void *stream) {
+    if (!x_bf16 || !q || !s_a) return IQD_ERR_INVALID;
+    if (b < 1 || K < 16 || K % 16 != 0 || b > kIntMax || K > kIntMax) return IQD_ERR_INVALID;
+    if (!aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(s_a, 4)) return IQD_ERR_ALIGN;
+    if (any_overlap({{q, static_cast<size_t>(b * K)}, {s_a, static_cast<size_t>(b) * 4}},
+                    {{x_bf16, static_cast<size_t>(b * K * 2)}}))
+        return IQD_ERR_INVALID;
+    clear_stale_error();
+    return hip_status(iqd::launch_quantize_fp8(static_cast<const uint16_t *>(x_bf16), static_cast<int>(b),
+                                               static_cast<int>(K), q, s_a, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_linear(const uint8_t *q, const float *s_a, const uint8_t *w, const float *s_w, int64_t b, int64_t N,
+               int64_t K, void *y_bf16, int32_t split_k, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!q || !s_a || !w || !s_w || !y_bf16) return IQD_ERR_INVALID;
+    int st = check_shape(b, N, K);
+    if (st != IQD_OK) return st;
+    st = fp8_split_ok(b, K, split_k);
+    if (st != IQD_OK) return st;
+    if (!aligned(q, 16) || !aligned(w, 16) || !aligned(s_a, 4) || !aligned(s_w, 4) || !aligned(y_bf16, 2))
+        return IQD_ERR_ALIGN;
+    const size_t ws = split_k > 1 ? round16(static_cast<size_t>(split_k) * b * N * 4) : 0;
+    if (ws > 0) {
+        if (!workspace || workspace_bytes < ws) return IQD_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return IQD_ERR_ALIGN;
+    }
+    if (any_overlap({{y_bf16, static_cast<size_t>(b) * N * 2}, {ws ? workspace : nullptr, ws}},
+                    {{q, static_cast<size_t>(b * K)}, {s_a, static_cast<size_t>(b) * 4},
+                     {w, static_cast<size_t>(N) * K}, {s_w, static_cast<size_t>(N) * 4}}))
+        return IQD_ERR_INVALID;
+    clear_stale_error();
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    uint16_t *y = static_cast<uint16_t *>(y_bf16);
+    const int Ni = static_cast<int>(N), Ki = static_cast<int>(K);
+    if (split_k == 1) {
+        // any b: launches of at most 16 tokens (each token's row is independent of its launch)
+        for (int64_t t0 = 0; t0 < b; t0 += 16) {
+            const int bc = static_cast<int>(b - t0 < 16 ? b - t0 : 16);
+            hipError_t e = iqd::launch_fp8_matvec(q + t0 * K, s_a + t0, w, s_w, bc, Ni, Ki, y + t0 * N, 1, nullptr,
+                                                  hs);
+            if (e != hipSuccess) return hip_status(e);
+        }
+        return IQD_OK;
+    }
+    float *part = static_cast<float *>(workspace);
+    const int bi = static_cast<int>(b);
+    hipError_t e = iqd::launch_fp8_matvec(q, s_a, w, s_w, bi, Ni, Ki, nullptr, split_k, part, hs);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(iqd::launch_fp8_combine(part, s_a, s_w, bi, Ni, split_k, y, hs));
 }
 
 int pow2_requantize(const int8_t *w, const float *s_w, int64_t N, int64_t K, int8_t *w_out, float *s_out,

@@ -61,6 +61,15 @@ hipError_t launch_blockq8_combine(const float *part, int b, int N, int split, ui
 int argmax_chunks(int N);
 hipError_t launch_argmax_rows(const uint16_t *logits, int b, int N, int32_t *out, uint64_t *part, hipStream_t st);
 
+// FP8 (E4M3) W8A8: per-token quantizer and the fixed-tree mat-vec (1 <= b <= 16;
+// split > 1 writes fp32 subtree roots [split, b, N] for launch_fp8_combine).
+int64_t fp8_tree_leaves(int K);
+hipError_t launch_quantize_fp8(const uint16_t *x, int b, int K, uint8_t *q, float *s, hipStream_t st);
+hipError_t launch_fp8_matvec(const uint8_t *q, const float *s_a, const uint8_t *w, const float *s_w, int b, int N,
+                             int K, uint16_t *y, int split, float *part, hipStream_t st);
+hipError_t launch_fp8_combine(const float *part, const float *s_a, const float *s_w, int b, int N, int split,
+                              uint16_t *y, hipStream_t st);
+
 // Decode attention in fixed 256-cell chunks (D = 128, Hq / Hkv <= 16).
 // Workspace: attn_workspace_bytes(b, Hq, pos0) bytes of chunk partials.
 int64_t attn_chunks(int64_t b, int64_t pos0);

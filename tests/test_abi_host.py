@@ -19,7 +19,7 @@ def test_exports_every_declared_function(lib):
     names = iqd.header_functions()
     assert set(names) == {"quantize_activations", "w8a8_linear", "w8a8_linear_bf16", "blockq8_linear", "lm_head_argmax",
                           "pow2_requantize", "iqd_workspace_bytes", "iqd_status_str", "iqd_last_hip_error",
-                          "attn_decode", "attn_workspace_bytes"}
+                          "attn_decode", "attn_workspace_bytes", "quantize_fp8", "fp8_linear"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -160,3 +160,22 @@ def test_attn_validation(lib):
     assert attn(lib, out=A + 64) == L.IQD_ERR_INVALID          # output overlaps q
     assert iqd.attn_workspace_bytes(2, 32, 8, 128, 10) == 0    # one chunk: the fast path
     assert iqd.attn_workspace_bytes(2, 32, 8, 64, 300) == 0    # rejected shape
+
+
+def fp8(lib, b=4, N=64, K=256, split=1, q=A, sa=2 * A, w=3 * A, sw=4 * A, y=5 * A, ws=0, wsb=0):
+    return lib.fp8_linear(ptr(q), ptr(sa), ptr(w), ptr(sw), b, N, K, ptr(y), split, ptr(ws), wsb, None)
+
+
+def test_fp8_validation(lib):
+    assert fp8(lib, q=0) == L.IQD_ERR_INVALID
+    assert fp8(lib, K=40) == L.IQD_ERR_INVALID                # K % 16
+    assert fp8(lib, K=131072) == L.IQD_ERR_RANGE
+    assert fp8(lib, split=3) == L.IQD_ERR_UNSUPPORTED
+    assert fp8(lib, K=1024, split=2) == L.IQD_ERR_UNSUPPORTED  # 64 leaves: one chunk, no split
+    assert fp8(lib, K=2048, split=2) == L.IQD_ERR_WORKSPACE
+    assert fp8(lib, b=17, K=2048, split=2) == L.IQD_ERR_UNSUPPORTED
+    assert fp8(lib, q=A + 8) == L.IQD_ERR_ALIGN
+    assert iqd.workspace_bytes(L.IQD_OP_FP8, 4, 64, 2048, 2) == 2 * 4 * 64 * 4
+    assert iqd.workspace_bytes(L.IQD_OP_FP8, 4, 64, 2048, 1) == 0
+    assert lib.quantize_fp8(ptr(A), 2, 40, ptr(2 * A), ptr(3 * A), None) == L.IQD_ERR_INVALID
+    assert lib.quantize_fp8(ptr(A), 2, 64, ptr(A + 32), ptr(3 * A), None) == L.IQD_ERR_INVALID  # q overlaps x
