@@ -64,7 +64,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--detail", action="store_true", help="per-(layer, b) kernel timings")
     p.add_argument("--no-prefill", action="store_true", help="skip timing the b=512 prefill pass")
-    p.add_argument("--extra", action="store_true", help="also time the block-q8, LM-head and attention paths")
+    p.add_argument("--extra", action="store_true", help="also time the block-q8, LM-head, FP8 and attention paths")
     p.add_argument("--calib", action="store_true",
                    help="end with one 256 MiB device-to-device copy (a known-size kernel for HBM counter scaling)")
     return p.parse_args()
@@ -306,6 +306,26 @@ def main():
             by = Ll.N * Ll.K + 4 * Ll.N
             ext.append({"op": "lm_head_argmax", "K": Ll.K, "N": Ll.N, "b": b, "us": round(us, 2),
                         "weight_GBs": round(by / (us * 1e-6) / 1e9, 1)})
+        # FP8 (E4M3) W8A8 on the Qwen3-8B layers (weights 1 byte each, as int8)
+        for li in range(4):
+            Lf = W.fp8_layer(li, tokens=8)
+            wf0 = torch.from_numpy(Lf.w).to(dev)
+            wfs = [wf0] + [wf0.clone() for _ in range(COPIES - 1)]
+            swf = torch.from_numpy(Lf.s_w).to(dev)
+            qf, sf = iqd.quantize_fp8(torch.from_numpy(Lf.x.view(np.int16)).view(torch.bfloat16).to(dev))
+            for b in (1, 4, 8):
+                yf = torch.empty((b, Lf.N), dtype=torch.bfloat16, device=dev)
+
+                def f8(b=b, yf=yf):
+                    for c in range(COPIES):
+                        iqd.fp8_linear(qf[:b], sf[:b], wfs[c], swf, y=yf)
+                g = capture(f8)
+                g.replay()
+                us = time_graph(g, 10) * 1e3 / COPIES
+                by = Lf.N * Lf.K + 4 * Lf.N
+                ext.append({"op": "fp8_linear", "layer": Lf.name, "K": Lf.K, "N": Lf.N, "b": b, "us": round(us, 2),
+                            "weight_GBs": round(by / (us * 1e-6) / 1e9, 1)})
+            del wfs, wf0
         # decode attention, Qwen3-8B heads (32 query, 8 kv, D = 128): enough cache
         # copies in rotation to exceed the 256 MB Infinity Cache
         name, Hq, Hkv, D = W.QWEN3_8B_ATTN

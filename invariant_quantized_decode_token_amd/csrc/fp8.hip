@@ -151,17 +151,18 @@ __global__ __launch_bounds__(kF8Threads) void k_fp8_matvec(F8Args a) {
                     float v[NP];
 #pragma unroll
                     for (int i = 0; i < NP; ++i) v[i] = 0.0f;
+                    float wf[RS][16];  // each weight vector decoded once, used by every token
+#pragma unroll
+                    for (int r = 0; r < RS; ++r) decode16(wv[u][r], wf[r]);
 #pragma unroll
                     for (int t = 0; t < B; ++t) {
                         float af[16];
                         decode16(av[u][t], af);
 #pragma unroll
                         for (int r = 0; r < RS; ++r) {
-                            float wf[16];
-                            decode16(wv[u][r], wf);
-                            float acc = __builtin_fmaf(af[0], wf[0], 0.0f);
+                            float acc = __builtin_fmaf(af[0], wf[r][0], 0.0f);
 #pragma unroll
-                            for (int i = 1; i < 16; ++i) acc = __builtin_fmaf(af[i], wf[i], acc);
+                            for (int i = 1; i < 16; ++i) acc = __builtin_fmaf(af[i], wf[r][i], acc);
                             v[r * B + t] = acc;
                         }
                     }
