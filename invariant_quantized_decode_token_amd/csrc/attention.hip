@@ -27,9 +27,9 @@
 // polynomial, all in binary32 operations.  With one chunk the merge returns
 // o_0 / l_0 exactly, so the chunk kernel writes that directly.
 //
-// Layout: one workgroup per (chunk, kv head, group of up to 4 or 16 query rows);
-// a row is (query token, query head) with the query heads of one kv head
-// adjacent.  Wave w of the workgroup owns part w of the chunk (64 cells) and
+// Layout: one workgroup per (chunk, kv head, group of up to 1, 2, 4 or 16
+// query rows); a row is (query token, query head) with the query heads of one
+// kv head adjacent.  Wave w of the workgroup owns part w of the chunk (64 cells) and
 // issues all of that part's key and value loads before computing; the K and
 // V chunk rows are read once per workgroup.
 #include "device.hpp"
@@ -86,24 +86,24 @@ struct AttnArgs {
     int nc;             // chunks of the longest row
 };
 
-// RM: the most query rows a workgroup holds (4 for single-token decode with
-// up to 4 query heads per kv head, 16 otherwise).
+// RM: the most query rows a workgroup holds.  The rows of one kv head are
+// numbered t * G + g (token t, its query head hk * G + g); a workgroup takes
+// RM consecutive ones, so a token's heads may span workgroups.
 template <int RM>
 __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
     // Workgroups are dealt to the XCDs in turn; the row groups of one
     // (chunk, kv head) take consecutive slots of one XCD, so its K and V rows
     // come from that XCD's L2 after the first read.
-    const int bq = RM / a.G;                    // query tokens per workgroup
-    const int nrg = (a.b + bq - 1) / bq;        // row groups
+    const int nrows = a.b * a.G;                // rows of one kv head
+    const int nrg = (nrows + RM - 1) / RM;      // row groups
     const int id = blockIdx.x, xcd = id % kXcds, slot = id / kXcds;
     const int tile = (slot / nrg) * kXcds + xcd, rg = slot % nrg;
     if (tile >= a.nc * a.Hkv) return;           // padding slots of the last round
     const int c = tile / a.Hkv, hk = tile % a.Hkv;
-    const int t0 = rg * bq;
-    const int nq = min(bq, a.b - t0);
-    const int R = nq * a.G;                     // rows of this workgroup
+    const int rb = rg * RM;                     // first row of this workgroup
+    const int R = min(RM, nrows - rb);          // rows of this workgroup
     const int j0 = c * kChunk;
-    const int pmax = a.pos0 + t0 + nq - 1;      // the last row's position
+    const int pmax = a.pos0 + (rb + R - 1) / a.G;  // the last row's position
     if (pmax < j0) return;                      // no row reaches this chunk
     const int ncell = min(kChunk, pmax + 1 - j0);
     const int tid = static_cast<int>(threadIdx.x);
@@ -114,9 +114,9 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) float op[kParts][RM][kD];
     __shared__ float lp[kParts][RM];
     __shared__ float mrow[RM];
-    // RM == 4: each part's values staged in LDS as [cell][64 words] (16-byte
+    // RM <= 4: each part's values staged in LDS as [cell][64 words] (16-byte
     // direct-to-LDS loads: a quarter of the load instructions of 4-byte ones)
-    constexpr bool kStageV = RM == 4;
+    constexpr bool kStageV = RM <= 4;
     __shared__ __attribute__((aligned(16))) uint32_t vst[kStageV ? kParts * kPart * (kD / 2) : 1];
 
     // Wave w owns part w: cells 64 w .. 64 w + 63 of the chunk, for the scores
@@ -159,10 +159,10 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
         for (int i = 0; i < 4; ++i) kw[st][i] = kp[i];
     }
 
-    // Row r: token t0 + r / G, query head hk * G + r % G.
+    // Row r: token (rb + r) / G, query head hk * G + (rb + r) % G.
     for (int i = tid; i < R * kD; i += kThreads) {
         const int r = i / kD, d = i % kD;
-        const int t = t0 + r / a.G, hq = hk * a.G + r % a.G;
+        const int t = (rb + r) / a.G, hq = hk * a.G + (rb + r) % a.G;
         qs[r][d] = bf16_to_f32(a.q[(static_cast<int64_t>(t) * a.Hq + hq) * kD + d]) * a.scale;
     }
     __syncthreads();
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
     // Per row: the chunk maximum over its own cells, then e_j (+0 past them,
     // to the end of the chunk; +0 for rows the workgroup does not hold).
     for (int r = wave; r < RM; r += kParts) {
-        const int p = a.pos0 + t0 + r / a.G;
+        const int p = a.pos0 + (rb + r) / a.G;
         const int ncr = r < R ? min(ncell, p + 1 - j0) : 0;  // wave-uniform
         float m = -__builtin_inff();
         for (int i = lane; i < ncr; i += kWave) m = fmaxf(m, sc[i][r]);
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
         int n[RM];
 #pragma unroll
         for (int r = 0; r < RM; ++r)
-            n[r] = r < R ? min(kPart, min(ncell, a.pos0 + t0 + r / a.G + 1 - j0) - pbase) : kPart;
+            n[r] = r < R ? min(kPart, min(ncell, a.pos0 + (rb + r) / a.G + 1 - j0) - pbase) : kPart;
         int nmin = kPart;
 #pragma unroll
         for (int r = 0; r < RM; ++r) nmin = min(nmin, n[r]);
@@ -247,23 +247,34 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
             else
                 return vw[i];
         };
+        // e of cell i for all RM rows (16-byte reads when RM is a multiple of 4)
+        auto erow = [&](int i, float (&ev)[RM]) __attribute__((always_inline)) {
+            if constexpr (RM % 4 == 0) {
+                const float4 *e4 = reinterpret_cast<const float4 *>(&sc[pbase + i][0]);
+#pragma unroll
+                for (int q4 = 0; q4 < RM / 4; ++q4) {
+                    const float4 e = e4[q4];
+                    ev[4 * q4 + 0] = e.x;
+                    ev[4 * q4 + 1] = e.y;
+                    ev[4 * q4 + 2] = e.z;
+                    ev[4 * q4 + 3] = e.w;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < RM; ++r) ev[r] = sc[pbase + i][r];
+            }
+        };
         if (nmin == kPart) {
 #pragma unroll
             for (int i = 0; i < kPart; ++i) {
                 const uint32_t w = vword(i);
                 const float v0 = bf16_to_f32(w & 0xFFFFu), v1 = __uint_as_float(w & 0xFFFF0000u);
-                const float4 *e4 = reinterpret_cast<const float4 *>(&sc[pbase + i][0]);
+                float ev[RM];
+                erow(i, ev);
 #pragma unroll
-                for (int q4 = 0; q4 < RM / 4; ++q4) {
-                    const float4 e = e4[q4];
-                    o[4 * q4 + 0][0] = __builtin_fmaf(e.x, v0, o[4 * q4 + 0][0]);
-                    o[4 * q4 + 0][1] = __builtin_fmaf(e.x, v1, o[4 * q4 + 0][1]);
-                    o[4 * q4 + 1][0] = __builtin_fmaf(e.y, v0, o[4 * q4 + 1][0]);
-                    o[4 * q4 + 1][1] = __builtin_fmaf(e.y, v1, o[4 * q4 + 1][1]);
-                    o[4 * q4 + 2][0] = __builtin_fmaf(e.z, v0, o[4 * q4 + 2][0]);
-                    o[4 * q4 + 2][1] = __builtin_fmaf(e.z, v1, o[4 * q4 + 2][1]);
-                    o[4 * q4 + 3][0] = __builtin_fmaf(e.w, v0, o[4 * q4 + 3][0]);
-                    o[4 * q4 + 3][1] = __builtin_fmaf(e.w, v1, o[4 * q4 + 3][1]);
+                for (int r = 0; r < RM; ++r) {
+                    o[r][0] = __builtin_fmaf(ev[r], v0, o[r][0]);
+                    o[r][1] = __builtin_fmaf(ev[r], v1, o[r][1]);
                 }
             }
         } else if (nmin < kPart) {
@@ -271,19 +282,14 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
             for (int i = 0; i < kPart; ++i) {
                 const uint32_t w = vword(i);
                 const float v0 = bf16_to_f32(w & 0xFFFFu), v1 = __uint_as_float(w & 0xFFFF0000u);
-                const float4 *e4 = reinterpret_cast<const float4 *>(&sc[pbase + i][0]);
+                float ev[RM];
+                erow(i, ev);
 #pragma unroll
-                for (int q4 = 0; q4 < RM / 4; ++q4) {
-                    const float4 e = e4[q4];
-                    const float ev[4] = {e.x, e.y, e.z, e.w};
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int r = 4 * q4 + u;
-                        const float x0 = __builtin_fmaf(ev[u], v0, o[r][0]);
-                        const float x1 = __builtin_fmaf(ev[u], v1, o[r][1]);
-                        o[r][0] = i < n[r] ? x0 : o[r][0];
-                        o[r][1] = i < n[r] ? x1 : o[r][1];
-                    }
+                for (int r = 0; r < RM; ++r) {
+                    const float x0 = __builtin_fmaf(ev[r], v0, o[r][0]);
+                    const float x1 = __builtin_fmaf(ev[r], v1, o[r][1]);
+                    o[r][0] = i < n[r] ? x0 : o[r][0];
+                    o[r][1] = i < n[r] ? x1 : o[r][1];
                 }
             }
         }
@@ -305,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
     // row has one chunk (what the merge would give), else the chunk partial.
     for (int i = tid; i < R * (kD / 2); i += kThreads) {
         const int r = i / (kD / 2), dp = i % (kD / 2);
-        const int t = t0 + r / a.G, hq = hk * a.G + r % a.G;
+        const int t = (rb + r) / a.G, hq = hk * a.G + (rb + r) % a.G;
         const int p = a.pos0 + t;
         if (p < j0) continue;  // the row does not reach this chunk
         const float2 o0 = reinterpret_cast<const float2 *>(&op[0][r][0])[dp];
@@ -433,17 +439,27 @@ hipError_t launch_attn_decode(const uint16_t *q, const uint16_t *k, const uint16
     const size_t mlb = static_cast<size_t>(b) * Hq * a.nc * 2 * sizeof(float);
     a.ml = merge ? static_cast<float *>(ws) : nullptr;
     a.o = merge ? reinterpret_cast<float *>(static_cast<char *>(ws) + (mlb + 255) / 256 * 256) : nullptr;
-    // rows per workgroup: 4 when every kv head's rows fit in 4, else 16
-    const bool small = a.G * b <= 4;
-    const int rm = small ? 4 : 16;
-    const int bq = rm / a.G;
-    const int64_t nrg = (b + bq - 1) / bq;
+    // Rows per workgroup.  Single-token decode (a kv head's rows fit in 4):
+    // split them over 2 or 4 workgroups while that still leaves no more
+    // workgroups than CUs (measured at Qwen3-8B shapes: 1024 cells 13.7 ->
+    // 10.1 us with 1 row, 4096 cells 16.9 -> 14.5 us with 2, 32768 cells best
+    // with 4).  Verify batches: 16 rows.
     const int64_t tiles = static_cast<int64_t>(a.nc) * Hkv;
+    const int64_t nr = static_cast<int64_t>(b) * a.G;  // rows of one kv head
+    int rm = 16;
+    if (nr <= 4) {
+        rm = 4;
+        while (rm > 1 && tiles * ((nr + rm / 2 - 1) / (rm / 2)) <= device_info().cus) rm /= 2;
+    }
+    const int64_t nrg = (nr + rm - 1) / rm;
     const int64_t wgs = (tiles + kXcds - 1) / kXcds * kXcds * nrg;  // every XCD gets whole tiles
-    if (small)
-        hipLaunchKernelGGL(k_attn_chunk<4>, dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL(k_attn_chunk<16>, dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, st, a);
+    const dim3 grid(static_cast<unsigned>(wgs));
+    switch (rm) {
+        case 1: hipLaunchKernelGGL(k_attn_chunk<1>, grid, dim3(kThreads), 0, st, a); break;
+        case 2: hipLaunchKernelGGL(k_attn_chunk<2>, grid, dim3(kThreads), 0, st, a); break;
+        case 4: hipLaunchKernelGGL(k_attn_chunk<4>, grid, dim3(kThreads), 0, st, a); break;
+        default: hipLaunchKernelGGL(k_attn_chunk<16>, grid, dim3(kThreads), 0, st, a); break;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !merge) return e;
     hipLaunchKernelGGL(k_attn_merge, dim3(static_cast<unsigned>(b) * Hq), dim3(kWave), 0, st, a);
