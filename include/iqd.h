@@ -280,8 +280,9 @@ int fp8_linear(const uint8_t *q, const float *s_a, const uint8_t *w, const float
  *   k_cache  in  bf16; the element (cell j, kv head h, dim d) is at
  *   v_cache      cache + j * cell_stride + h * head_stride + d (strides in
  *                elements, multiples of 8, so every 16-byte row piece is
- *                aligned); both must hold cells 0 .. pos0 + b - 1, which are
- *                the only cells read; 16-byte aligned
+ *                aligned; cell_stride >= D, or IQD_ERR_INVALID); both must
+ *                hold cells 0 .. pos0 + b - 1, which are the only cells read;
+ *                16-byte aligned
  *   out_bf16 out bf16 [b, Hq, D], contiguous, 16-byte aligned
  *   workspace    attn_workspace_bytes(b, Hq, Hkv, D, pos0) bytes, 16-byte
  *                aligned (none when pos0 + b <= 256): fp32 chunk partials

@@ -371,6 +371,8 @@ int attn_decode(const void *q_bf16, const void *k_cache, const void *v_cache, in
     if (k_cell_stride < 0 || k_head_stride < 0 || v_cell_stride < 0 || v_head_stride < 0 ||
         k_cell_stride > kIntMax || k_head_stride > kIntMax || v_cell_stride > kIntMax || v_head_stride > kIntMax)
         return IQD_ERR_INVALID;
+    // cells hold D elements each and must not overlap
+    if (k_cell_stride < D || v_cell_stride < D) return IQD_ERR_INVALID;
     // a chunk's 256 cells must span less than 2 GB (32-bit buffer offsets)
     if (k_cell_stride >= (int64_t{1} << 22) || v_cell_stride >= (int64_t{1} << 22)) return IQD_ERR_UNSUPPORTED;
     if (!aligned(q_bf16, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out_bf16, 16) ||

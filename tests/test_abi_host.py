@@ -153,6 +153,7 @@ def test_attn_validation(lib):
     assert attn(lib, kc=1020) == L.IQD_ERR_ALIGN               # rows not 16-byte aligned
     assert attn(lib, vh=4) == L.IQD_ERR_ALIGN
     assert attn(lib, vc=1 << 22) == L.IQD_ERR_UNSUPPORTED      # a chunk would span 2 GB
+    assert attn(lib, kc=64) == L.IQD_ERR_INVALID                # cells would overlap
     assert attn(lib, pos0=300) == L.IQD_ERR_WORKSPACE          # two chunks need partials
     need = iqd.attn_workspace_bytes(2, 32, 8, 128, 300)
     assert need == (2 * 32 * 2 * 2 * 4 + 255) // 256 * 256 + 2 * 32 * 2 * 128 * 4
