@@ -35,6 +35,7 @@ METRIC = "W8A8 matvec weight GB/s (% HBM peak) at b=1..8; batch-variant rows = 0
 HBM_PEAK_GBS = 8000.0
 COPIES = 8
 B_LIST = list(range(1, 9))
+PREFILL_SPLITS = (1, 2, 4)  # K splits timed for the b = 512 pass; the fastest is reported
 
 
 def committed_traffic(kernel: str):
@@ -254,16 +255,23 @@ def main():
             xp = torch.from_numpy(Lp.x.view(np.int16)).view(torch.bfloat16).to(dev)
             qp, sp = iqd.quantize_activations(xp)
             yp = torch.empty((T, L.N), dtype=torch.bfloat16, device=dev)
-
-            def pf(li=li):
-                for c in range(COPIES):
-                    iqd.w8a8_linear(qp, sp, wsets[li][c], swsets[li], y=yp)
-            g = capture(pf)
-            g.replay()
-            us = time_graph(g, 5) * 1e3 / COPIES
+            wsp = torch.empty((iqd.workspace_bytes(iqd.IQD_OP_W8A8, T, L.N, L.K, max(PREFILL_SPLITS)),),
+                              dtype=torch.uint8, device=dev)
+            per_split = {}
+            for split in PREFILL_SPLITS:
+                def pf(li=li, split=split):
+                    for c in range(COPIES):
+                        iqd.w8a8_linear(qp, sp, wsets[li][c], swsets[li], split_k=split, y=yp, workspace=wsp)
+                g = capture(pf)
+                g.replay()
+                per_split[split] = time_graph(g, 5) * 1e3 / COPIES
+            best = min(per_split, key=per_split.get)
+            us = per_split[best]
             tops = 2.0 * T * L.N * L.K / (us * 1e-6) / 1e12
-            pre.append({"layer": L.name, "b": T, "us": round(us, 2), "TOPS": round(tops, 1),
-                        "mfma_frac": round(tops / 5000.0, 4)})
+            pre.append({"layer": L.name, "b": T, "split_k": best, "us": round(us, 2), "TOPS": round(tops, 1),
+                        "mfma_frac": round(tops / 5000.0, 4),
+                        "us_by_split": {str(k): round(v, 2) for k, v in per_split.items()}})
+            del wsp
         out["prefill"] = pre
 
     if args.extra:

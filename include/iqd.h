@@ -111,7 +111,9 @@ int quantize_activations(const void *x_bf16, int64_t b, int64_t K, int32_t group
  *              (NULL allowed when that is 0).
  * b <= 16 streams the weights once (packed int8 dot products at b = 1 and
  * on small matrices at b = 2, the int8 matrix cores otherwise); larger b uses
- * the tiled matrix-core path.  All give identical bits.
+ * the tiled matrix-core path, whose split_k divides each output tile's K
+ * stages among split_k workgroups (more workgroups when tiles are few).  All
+ * give identical bits.
  * Errors: IQD_ERR_INVALID, IQD_ERR_ALIGN, IQD_ERR_RANGE, IQD_ERR_UNSUPPORTED
  * (bad split_k), IQD_ERR_WORKSPACE, IQD_ERR_HIP.
  */

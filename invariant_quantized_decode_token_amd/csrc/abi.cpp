@@ -104,9 +104,10 @@ int check_shape(int64_t b, int64_t N, int64_t K) {
     return IQD_OK;
 }
 
-int w8a8_split_ok(int64_t b, int64_t K, int32_t split) {
+// Any b: the int32 partials are exact, so every split gives the same bits.
+int w8a8_split_ok(int64_t, int64_t K, int32_t split) {
     if (split == 1) return IQD_OK;
-    if (b > kMatvecMaxB || !is_pow2(split) || split > IQD_SPLIT_K_MAX || split > K / 16) return IQD_ERR_UNSUPPORTED;
+    if (!is_pow2(split) || split > IQD_SPLIT_K_MAX || split > K / 16) return IQD_ERR_UNSUPPORTED;
     return IQD_OK;
 }
 
@@ -233,10 +234,10 @@ int w8a8_linear(const int8_t *q, const float *s_a, const int8_t *w, const float 
     hipStream_t hs = static_cast<hipStream_t>(stream);
     uint16_t *y = static_cast<uint16_t *>(y_bf16);
     const int bi = static_cast<int>(b), Ni = static_cast<int>(N), Ki = static_cast<int>(K);
-    if (b > kMatvecMaxB) return hip_status(iqd::launch_w8a8_mfma(q, s_a, w, s_w, bi, Ni, Ki, y, hs));
+    int32_t *part = static_cast<int32_t *>(workspace);
+    if (b > kMatvecMaxB) return hip_status(iqd::launch_w8a8_mfma(q, s_a, w, s_w, bi, Ni, Ki, y, split_k, part, hs));
     if (split_k == 1)
         return hip_status(iqd::launch_w8a8_matvec(q, s_a, w, s_w, bi, Ni, Ki, y, 1, nullptr, hs));
-    int32_t *part = static_cast<int32_t *>(workspace);
     hipError_t e = iqd::launch_w8a8_matvec(q, s_a, w, s_w, bi, Ni, Ki, nullptr, split_k, part, hs);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(iqd::launch_w8a8_combine(part, s_a, s_w, bi, Ni, split_k, y, hs));
@@ -273,7 +274,7 @@ int w8a8_linear_bf16(const void *x_bf16, const int8_t *w, const float *s_w, int6
     float *s_a = s_a_out ? s_a_out : reinterpret_cast<float *>(static_cast<char *>(workspace) + round16(qbytes));
     hipError_t e = iqd::launch_quantize_token(x, bi, Ki, q, s_a, hs);
     if (e != hipSuccess) return hip_status(e);
-    if (b > kMatvecMaxB) return hip_status(iqd::launch_w8a8_mfma(q, s_a, w, s_w, bi, Ni, Ki, y, hs));
+    if (b > kMatvecMaxB) return hip_status(iqd::launch_w8a8_mfma(q, s_a, w, s_w, bi, Ni, Ki, y, 1, nullptr, hs));
     return hip_status(iqd::launch_w8a8_matvec(q, s_a, w, s_w, bi, Ni, Ki, y, 1, nullptr, hs));
 }
 

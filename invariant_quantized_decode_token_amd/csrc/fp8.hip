@@ -104,7 +104,6 @@ __global__ __launch_bounds__(kF8Threads) void k_fp8_matvec(F8Args a) {
 
     constexpr int NV = RS * B;
     constexpr int NP = pow2_ceil(NV);
-    constexpr int NPH = NP >= 2 ? NP / 2 : 1;
 
     const __amdgpu_buffer_rsrc_t qr = f8_rsrc(a.q, static_cast<int64_t>(B) * K);
 

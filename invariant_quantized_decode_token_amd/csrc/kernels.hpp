@@ -38,9 +38,11 @@ hipError_t launch_w8a8_mfvec_fused(const uint16_t *x, const int8_t *w, const flo
 hipError_t launch_w8a8_combine(const int32_t *part, const float *s_a, const float *s_w, int b, int N,
                                int split, uint16_t *y, hipStream_t st);
 
-// W8A8 int8 matrix-core GEMM for b > 16 (prefill), same epilogue.
+// W8A8 int8 matrix-core GEMM for b > 16 (prefill), same epilogue.  With
+// split > 1 the K stages are divided among `split` workgroups per tile, which
+// write int32 partial sums part[split, b, N]; the combine then runs too.
 hipError_t launch_w8a8_mfma(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w,
-                            int b, int N, int K, uint16_t *y, hipStream_t st);
+                            int b, int N, int K, uint16_t *y, int split, int32_t *part, hipStream_t st);
 
 // Block-quantized mat-vec, 1 <= b <= 16.  With split > 1, writes fp32 subtree
 // roots part[s, b, N] and needs launch_blockq8_combine afterwards.

@@ -99,7 +99,8 @@ constexpr int out_stride() { return BN + 8; }
 template <int BM, int BN, int S, int GM, int GN>
 __global__ __launch_bounds__(64 * GM * GN) void k_w8a8_mfma(const int8_t *__restrict__ q, const float *__restrict__ s_a,
                                                         const int8_t *__restrict__ w, const float *__restrict__ s_w,
-                                                        int M, int N, int K, uint16_t *__restrict__ y) {
+                                                        int M, int N, int K, uint16_t *__restrict__ y,
+                                                        int32_t *__restrict__ part, int split) {
     constexpr int NWV = GM * GN, NTH = kWave * NWV;  // waves, GM x GN over the tile
     constexpr int WM = BM / GM, WN = BN / GN;        // wave sub-tile
     constexpr int FM = WM / 16, FN = WN / 16;
@@ -124,7 +125,13 @@ __global__ __launch_bounds__(64 * GM * GN) void k_w8a8_mfma(const int8_t *__rest
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int lane = lane_id();
     const int wm = wave / GN, wn = wave % GN;
-    const int nst = (K + kBK - 1) / kBK;
+    // Split s of `split` (blockIdx.y) owns the stages [st0, st1); K bytes at or
+    // past k_hi load as zeros.  A split with no stage writes zero partials.
+    const int nst_all = (K + kBK - 1) / kBK;
+    const int per = (nst_all + split - 1) / split;
+    const int st0 = min(nst_all, static_cast<int>(blockIdx.y) * per);
+    const int nst = min(nst_all, st0 + per) - st0;
+    const int k_hi = min(K, (st0 + nst) * kBK);
     const __amdgpu_buffer_rsrc_t ra = rsrc(q, static_cast<int64_t>(M) * K);
     const __amdgpu_buffer_rsrc_t rb = rsrc(w, static_cast<int64_t>(N) * K);
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_all));
@@ -145,10 +152,10 @@ __global__ __launch_bounds__(64 * GM * GN) void k_w8a8_mfma(const int8_t *__rest
         goff[p] = in ? static_cast<uint32_t>(gr) * static_cast<uint32_t>(K) + 16 * c : kOob;
     }
     auto stage_load = [&](int st, int buf) __attribute__((always_inline)) {
-        const int k0 = st * kBK;  // past K (stages beyond the last) every lane reads zeros
+        const int k0 = (st0 + st) * kBK;  // past k_hi (stages beyond the last) every lane reads zeros
 #pragma unroll
         for (int p = 0; p < PA + PB; ++p) {
-            const bool in = goff[p] != kOob && k0 + gk[p] < K;
+            const bool in = goff[p] != kOob && k0 + gk[p] < k_hi;
             const uint32_t off = in ? goff[p] + static_cast<uint32_t>(k0) : kOob;
             lds_i8 *dst = (lds_i8 *)(lds_all + buf * STAGE + (NWV * p + wave) * 1024);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(p < PA ? ra : rb, dst, 16, off, 0, 0, 0);
@@ -196,6 +203,27 @@ __global__ __launch_bounds__(64 * GM * GN) void k_w8a8_mfma(const int8_t *__rest
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f1[i], f1[FM + j], acc[i][j], 0, 0, 0);
+    }
+
+    if (part) {
+        // Exact int32 partial sums of this split, part[split][M][N]; the
+        // combine adds the splits and applies the epilogue.  Lane l, register
+        // r of fragment (i, j) holds the element named below.
+        wait_vm<0>();
+        int32_t *ps = part + static_cast<int64_t>(blockIdx.y) * M * N;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + wm * WM + i * 16 + fc * 4 + r;
+                if (m >= M) continue;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int n = n0 + wn * WN + j * 16 + fr;
+                    if (n < N) ps[static_cast<int64_t>(m) * N + n] = acc[i][j][r];
+                }
+            }
+        return;
     }
 
     // Scales of the tile, loaded before the first store.  Lane l, register r
@@ -251,7 +279,7 @@ __global__ __launch_bounds__(64 * GM * GN) void k_w8a8_mfma(const int8_t *__rest
 
 template <int BM, int BN, int S, int GM, int GN>
 hipError_t launch_tiles(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int b, int N, int K,
-                        uint16_t *y, hipStream_t st) {
+                        uint16_t *y, int split, int32_t *part, hipStream_t st) {
     const size_t ring = static_cast<size_t>(S) * (BM + BN) * kBK;
     const size_t otile = static_cast<size_t>(BM) * out_stride<BN>() * 2;
     const size_t smem = ring > otile ? ring : otile;
@@ -261,17 +289,18 @@ hipError_t launch_tiles(const int8_t *q, const float *s_a, const int8_t *w, cons
     const int mt = (b + BM - 1) / BM;
     const int nt = (N + BN - 1) / BN;
     const int nt_pad = (nt + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((k_w8a8_mfma<BM, BN, S, GM, GN>), dim3(mt * nt_pad), dim3(kWave * GM * GN), smem, st, q, s_a, w, s_w, b, N, K,
-                       y);
+    hipLaunchKernelGGL((k_w8a8_mfma<BM, BN, S, GM, GN>), dim3(mt * nt_pad, split), dim3(kWave * GM * GN), smem, st, q,
+                       s_a, w, s_w, b, N, K, y, split > 1 ? part : nullptr, split);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_w8a8_mfma(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int b, int N, int K,
-                            uint16_t *y, hipStream_t st) {
+                            uint16_t *y, int split, int32_t *part, hipStream_t st) {
     // Buffer offsets are 32-bit: matrices past 2 GB take token chunks of 16
-    // through the mat-vec instead (same bits, every row is independent).
+    // through the mat-vec instead (same bits, every row is independent, and
+    // the split does not change them).
     if (static_cast<int64_t>(N) * K > 0x7FFF0000ll || static_cast<int64_t>(b) * K > 0x7FFF0000ll) {
         for (int t0 = 0; t0 < b; t0 += 16) {
             const int bc = b - t0 < 16 ? b - t0 : 16;
@@ -284,12 +313,14 @@ hipError_t launch_w8a8_mfma(const int8_t *q, const float *s_a, const int8_t *w, 
     // Tile choice, measured at b = 512 on the Qwen3-8B layers (weights read
     // from HBM) against 64- to 256-token and -row tiles, 4 or 8 waves and
     // rings of 2 to 4 stages: 8 waves and two workgroups per CU throughout;
-    // 128 x 128 tiles with 2 stages while they number at least two per CU,
-    // 128 x 64 tiles with 3 stages below that.
+    // 128 x 128 tiles with 2 stages while they (times the K splits) number
+    // at least two per CU, 128 x 64 tiles with 3 stages below that.
     const int cus = device_info().cus;
-    const int64_t big = static_cast<int64_t>((b + 127) / 128) * ((N + 127) / 128);
-    if (big >= 2 * cus) return launch_tiles<128, 128, 2, 2, 4>(q, s_a, w, s_w, b, N, K, y, st);
-    return launch_tiles<128, 64, 3, 4, 2>(q, s_a, w, s_w, b, N, K, y, st);
+    const int64_t big = static_cast<int64_t>((b + 127) / 128) * ((N + 127) / 128) * split;
+    hipError_t e = big >= 2 * cus ? launch_tiles<128, 128, 2, 2, 4>(q, s_a, w, s_w, b, N, K, y, split, part, st)
+                                  : launch_tiles<128, 64, 3, 4, 2>(q, s_a, w, s_w, b, N, K, y, split, part, st);
+    if (e != hipSuccess || split == 1) return e;
+    return launch_w8a8_combine(part, s_a, s_w, b, N, split, y, st);
 }
 
 }  // namespace iqd

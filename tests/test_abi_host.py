@@ -64,7 +64,7 @@ def test_w8a8_validation(lib):
     assert w8a8(lib, split=3) == L.IQD_ERR_UNSUPPORTED
     assert w8a8(lib, split=128) == L.IQD_ERR_UNSUPPORTED
     assert w8a8(lib, K=32, split=4) == L.IQD_ERR_UNSUPPORTED  # more splits than 16-byte vectors
-    assert w8a8(lib, b=17, split=2) == L.IQD_ERR_UNSUPPORTED
+    assert w8a8(lib, b=17, split=2) == L.IQD_ERR_WORKSPACE  # the tiled path splits K too
     assert w8a8(lib, q=A + 8) == L.IQD_ERR_ALIGN
     assert w8a8(lib, w=3 * A + 4) == L.IQD_ERR_ALIGN
     assert w8a8(lib, sa=2 * A + 2) == L.IQD_ERR_ALIGN

@@ -134,7 +134,9 @@ def test_matrix_core_shape_classes(iqd, N, K):
 # counts that are no multiple of any tile: 128 x 64 tiles (fewer than two
 # 128 x 128 tiles per CU; one and two M tiles, K of 2 and 8 stages plus a
 # ragged one) and 128 x 128 tiles.  Sampled rows against the oracle, every
-# row against the mat-vec over 16-token chunks.
+# row against the mat-vec over 16-token chunks.  Every split of K gives the
+# same bits, including splits left with no stage (K = 272 has three 128-byte
+# stages; splits 4 and 8 leave some workgroups only zero partials).
 @pytest.mark.parametrize("b,N,K", [(100, 20000, 272), (130, 2000, 1040), (300, 33000, 272)])
 def test_prefill_tile_classes_ragged(iqd, b, N, K):
     t = torch()
@@ -153,18 +155,23 @@ def test_prefill_tile_classes_ragged(iqd, b, N, K):
         t1 = min(b, t0 + 16)
         iqd.w8a8_linear(q[t0:t1], sa[t0:t1], wd, swd, y=ref[t0:t1])
     assert_bits_equal(host_bits(y), host_bits(ref), f"b={b} N={N} K={K} vs mat-vec")
+    for split in (2, 4, 8):
+        ys = iqd.w8a8_linear(q, sa, wd, swd, split_k=split)
+        assert_bits_equal(host_bits(ys), host_bits(ref), f"b={b} N={N} K={K} split={split}")
 
 
-def test_max_k_and_extreme_codes(iqd):
+@pytest.mark.parametrize("b", [3, 20])
+def test_max_k_and_extreme_codes(iqd, b):
     """K = 131056 (the largest multiple of 16 under the bound) with every
-    product at (-128)*(-128): acc = 2147287040, close to 2^31."""
-    K, N, b = 131056, 4, 3
+    product at (-128)*(-128): acc = 2147287040, close to 2^31.  b = 3 takes
+    the mat-vec, b = 20 the tiled matrix-core path (and its K splits)."""
+    K, N = 131056, 4
     q = np.full((b, K), -128, np.int8)
-    q[1] = 127
-    q[2, ::2] = 0
+    q[1::3] = 127
+    q[2::3, ::2] = 0
     w = np.full((N, K), -128, np.int8)
     w[1] = 127
-    s_a = np.array([1e-9, 2.5e-3, 1.0], np.float32)
+    s_a = np.resize(np.array([1e-9, 2.5e-3, 1.0], np.float32), b)
     s_w = np.array([1e-3, 3e-2, 0.5, 1e-5], np.float32)
     oy = oracle.w8a8(q, s_a, w, s_w)
     y = iqd.w8a8_linear(dev(q), dev(s_a), dev(w), dev(s_w))
@@ -238,11 +245,15 @@ def test_qwen3_8b_layer_invariance_and_parity(iqd, li):
     for split in (2, 4, 8):
         y = iqd.w8a8_linear(q[:8], sa[:8], w, sw, split_k=split)
         assert_bits_equal(host_bits(y), ref[:8], f"{L.name} split={split}")
-    # prefill: all 512 tokens in one pass, twice (run-to-run bitwise)
+    # prefill: all 512 tokens in one pass, twice (run-to-run bitwise), and
+    # with K split over 2 and 4 workgroups per tile
     y512 = iqd.w8a8_linear(q, sa, w, sw)
     assert_bits_equal(host_bits(y512), ref, f"{L.name} b=512 vs b=1")
     y512b = iqd.w8a8_linear(q, sa, w, sw)
     assert_bits_equal(host_bits(y512b), ref, f"{L.name} b=512 second run")
+    for split in (2, 4):
+        ys = iqd.w8a8_linear(q, sa, w, sw, split_k=split)
+        assert_bits_equal(host_bits(ys), ref, f"{L.name} b=512 split={split}")
 
 
 # ----------------------------------------------------------------------------
