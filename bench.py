@@ -344,7 +344,7 @@ def main():
             ks = [torch.from_numpy(case.k.view(np.int16)).view(torch.bfloat16).to(dev) for _ in range(ncopy)]
             vs = [torch.from_numpy(case.v.view(np.int16)).view(torch.bfloat16).to(dev) for _ in range(ncopy)]
             qa = torch.from_numpy(case.q.view(np.int16)).view(torch.bfloat16).to(dev)
-            for b in (1, 8):
+            for b in (1, 2, 4, 8):
                 oa = torch.empty((b, Hq, D), dtype=torch.bfloat16, device=dev)
                 wsa = torch.empty((max(16, iqd.attn_workspace_bytes(b, Hq, Hkv, D, cells - b)),), dtype=torch.uint8,
                                   device=dev)

@@ -105,6 +105,23 @@ def test_cache_allocation_and_strides_do_not_matter(iqd):
     del t
 
 
+@pytest.mark.parametrize("cells,b", [(2049, 8), (5600, 3), (9000, 2)])
+def test_row_groups_of_eight(iqd, cells, b):
+    """Qwen3-8B heads with more (chunk, kv head) tiles than two per CU take
+    workgroups of up to 8 rows on a 256-CU chip: 32 rows as four full groups,
+    12 rows as a full group and a ragged one of 4, 8 rows as one.  Sampled
+    heads against the oracle; every row equals its token decoded alone."""
+    case = W.attn_case(W.SEED_ATTN + 3 * cells + b, b, cells)
+    kd, vd = dev(case.k), dev(case.v)
+    got = run(iqd, case, k=kd, v=vd)
+    for h in (0, 5, 22, 31):
+        want = oracle.attn_decode(case.q, case.k, case.v, case.pos0, case.scale, heads=(h, h + 1))
+        assert_bits_equal(got[:, h], want[:, h], f"cells={cells} b={b} head={h}")
+    for t in range(b):
+        alone = run(iqd, case, q=case.q[t:t + 1], pos0=case.pos0 + t, k=kd, v=vd)
+        assert_bits_equal(alone[0], got[t], f"cells={cells} b={b} token {t} alone")
+
+
 @pytest.mark.parametrize("cells", [4096, 32768])
 def test_qwen3_8b_long_context_sampled_heads(iqd, cells):
     """Qwen3-8B attention (32 query heads, 8 kv heads, D = 128), b = 8 verify
