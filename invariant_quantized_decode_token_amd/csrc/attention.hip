@@ -65,7 +65,6 @@ __device__ __forceinline__ float attn_exp(float x) {
     return n < -125.0f ? 0.0f : p * two_n;
 }
 
-typedef __attribute__((address_space(3))) int8_t lds_i8;
 
 // Buffer resource over [base, base + bytes): loads past the end read zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void *base, int64_t bytes) {
@@ -114,40 +113,26 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) float op[kParts][RM][kD];
     __shared__ float lp[kParts][RM];
     __shared__ float mrow[RM];
-    // RM <= 4: each part's values staged in LDS as [cell][64 words] (16-byte
-    // direct-to-LDS loads: a quarter of the load instructions of 4-byte ones)
-    constexpr bool kStageV = RM <= 4;
-    __shared__ __attribute__((aligned(16))) uint32_t vst[kStageV ? kParts * kPart * (kD / 2) : 1];
 
     // Wave w owns part w: cells 64 w .. 64 w + 63 of the chunk, for the scores
-    // and for the value sums.  Its loads go out first, all at once: the values
-    // (lane: dims 2 lane, 2 lane + 1 of each cell), then the keys (four lanes
-    // per cell, lane `sub` holding dims 32 sub .. 32 sub + 31).  Cells past
-    // the last one read cell j0 instead (in range, never used).
-    const int pbase = kPart * wave;
-    uint32_t vw[kStageV ? 1 : kPart];
-    if constexpr (kStageV) {
-        // instruction i: lane L loads bytes 16 (L % 16) .. + 15 of cell
-        // 4 i + L / 16 of the part, landing at word 64 (4 i + L / 16) + 4 (L % 16)
-        const __amdgpu_buffer_rsrc_t vr =
-            attn_rsrc(a.v + static_cast<int64_t>(j0) * a.vc + hk * a.vh, static_cast<int64_t>(kChunk) * a.vc * 2);
+    // and for the value sums.  Its loads go out first, all at once, in the
+    // order they are used (they return in issue order): the query rows, the
+    // keys (four lanes per cell, lane `sub` holding dims 32 sub .. 32 sub +
+    // 31), then the values (lane: dims 2 lane, 2 lane + 1 of each cell).  The
+    // scores then run while the values are still arriving.  Cells past the
+    // last one read cell j0 instead (in range, never used).
+    // Query element i = tid + kThreads u is row i / kD, dim i % kD.
+    constexpr int QU = (RM * kD + kThreads - 1) / kThreads;
+    uint16_t qv[QU];
 #pragma unroll
-        for (int i = 0; i < kPart / 4; ++i) {
-            const int jj = pbase + 4 * i + (lane >> 4);
-            const uint32_t off = static_cast<uint32_t>((jj < ncell ? jj : 0) * a.vc * 2 + 16 * (lane & 15));
-            lds_i8 *dst = (lds_i8 *)(vst + (wave * kPart + 4 * i) * (kD / 2));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, dst, 16, off, 0, 0, 0);
-        }
-    } else {
-        const uint32_t *vp = reinterpret_cast<const uint32_t *>(a.v + static_cast<int64_t>(j0) * a.vc + hk * a.vh) +
-                             lane;
-        const int64_t vstep = a.vc / 2;  // in 32-bit words
-#pragma unroll
-        for (int i = 0; i < kPart; ++i) {
-            const int jj = pbase + i;
-            vw[i] = vp[(jj < ncell ? jj : 0) * vstep];
-        }
+    for (int u = 0; u < QU; ++u) {
+        const int i = tid + kThreads * u;
+        const int r = i / kD < R ? i / kD : 0, d = i % kD;  // rows past R load row 0 (unused)
+        const int t = (rb + r) / a.G, hq = hk * a.G + (rb + r) % a.G;
+        qv[u] = a.q[(static_cast<int64_t>(t) * a.Hq + hq) * kD + d];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    const int pbase = kPart * wave;
     const int cs = lane >> 2, sub = lane & 3;
     v4i kw[4][4];
 #pragma unroll
@@ -158,12 +143,26 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) kw[st][i] = kp[i];
     }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // Row r: token (rb + r) / G, query head hk * G + (rb + r) % G.
-    for (int i = tid; i < R * kD; i += kThreads) {
-        const int r = i / kD, d = i % kD;
-        const int t = (rb + r) / a.G, hq = hk * a.G + (rb + r) % a.G;
-        qs[r][d] = bf16_to_f32(a.q[(static_cast<int64_t>(t) * a.Hq + hq) * kD + d]) * a.scale;
+    // 32-bit offsets into a buffer over the chunk's values (cell strides are
+    // below 2^22 elements, so a chunk spans less than 2^31 bytes)
+    uint32_t vw[kPart];
+    {
+        const __amdgpu_buffer_rsrc_t vr =
+            attn_rsrc(a.v + static_cast<int64_t>(j0) * a.vc + hk * a.vh, static_cast<int64_t>(kChunk) * a.vc * 2);
+        const uint32_t vcb = static_cast<uint32_t>(a.vc) * 2;
+#pragma unroll
+        for (int i = 0; i < kPart; ++i) {
+            const int jj = pbase + i;
+            vw[i] = __builtin_amdgcn_raw_buffer_load_b32(vr, static_cast<uint32_t>(jj < ncell ? jj : 0) * vcb + 4 * lane,
+                                                         0, 0);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+        const int i = tid + kThreads * u;
+        if (i < R * kD) qs[i / kD][i % kD] = bf16_to_f32(qv[u]) * a.scale;
     }
     __syncthreads();
 
@@ -241,12 +240,6 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
         float o[RM][2];
 #pragma unroll
         for (int r = 0; r < RM; ++r) o[r][0] = o[r][1] = 0.0f;
-        auto vword = [&](int i) __attribute__((always_inline)) {
-            if constexpr (kStageV)
-                return vst[(wave * kPart + i) * (kD / 2) + lane];
-            else
-                return vw[i];
-        };
         // e of cell i for all RM rows (16-byte reads when RM is a multiple of 4)
         auto erow = [&](int i, float (&ev)[RM]) __attribute__((always_inline)) {
             if constexpr (RM % 4 == 0) {
@@ -267,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
         if (nmin == kPart) {
 #pragma unroll
             for (int i = 0; i < kPart; ++i) {
-                const uint32_t w = vword(i);
+                const uint32_t w = vw[i];
                 const float v0 = bf16_to_f32(w & 0xFFFFu), v1 = __uint_as_float(w & 0xFFFF0000u);
                 float ev[RM];
                 erow(i, ev);
@@ -280,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
         } else if (nmin < kPart) {
 #pragma unroll
             for (int i = 0; i < kPart; ++i) {
-                const uint32_t w = vword(i);
+                const uint32_t w = vw[i];
                 const float v0 = bf16_to_f32(w & 0xFFFFu), v1 = __uint_as_float(w & 0xFFFF0000u);
                 float ev[RM];
                 erow(i, ev);
