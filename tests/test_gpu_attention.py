@@ -122,6 +122,21 @@ def test_row_groups_of_eight(iqd, cells, b):
         assert_bits_equal(alone[0], got[t], f"cells={cells} b={b} token {t} alone")
 
 
+def test_merge_over_many_windows(iqd):
+    """70001 cells: 274 chunks per row, merged in windows of chunks with a
+    ragged last window; two tokens, every head against the oracle, and each
+    row against its token decoded alone."""
+    b, cells = 2, 70001
+    case = W.attn_case(W.SEED_ATTN + cells, b, cells, Hq=8, Hkv=2)
+    kd, vd = dev(case.k), dev(case.v)
+    got = run(iqd, case, k=kd, v=vd)
+    want = oracle.attn_decode(case.q, case.k, case.v, case.pos0, case.scale)
+    assert_bits_equal(got, want, "70001 cells")
+    for t in range(b):
+        alone = run(iqd, case, q=case.q[t:t + 1], pos0=case.pos0 + t, k=kd, v=vd)
+        assert_bits_equal(alone[0], got[t], f"token {t} alone")
+
+
 @pytest.mark.parametrize("cells", [4096, 32768])
 def test_qwen3_8b_long_context_sampled_heads(iqd, cells):
     """Qwen3-8B attention (32 query heads, 8 kv heads, D = 128), b = 8 verify
