@@ -87,6 +87,8 @@ def _load():
         "oracle_f32_to_e4m3": (ctypes.c_uint8, [f32]),
         "oracle_quantize_fp8": (ctypes.c_int, [P, I64, I64, P, P]),
         "oracle_fp8_linear": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, ctypes.c_int]),
+        "oracle_kq6_decode": (ctypes.c_int, [P, P, I64, I64, P]),
+        "oracle_kq6_linear": (ctypes.c_int, [P, P, P, P, P, P, I64, I64, I64, P, ctypes.c_int]),
         "oracle_attn_decode": (ctypes.c_int, [P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, I64, f32, I64, I64,
                                               P, ctypes.c_int]),
     }
@@ -331,4 +333,37 @@ def fp8_linear(q, s_a, w, s_w, nthreads: int = 0) -> np.ndarray:
     y = np.empty((b, N), np.uint16)
     _check(_load().oracle_fp8_linear(_ptr(q), _ptr(s_a), _ptr(w), _ptr(s_w), b, N, K, _ptr(y), nthreads),
            "fp8_linear")
+    return y
+
+
+# --- k-quant-style 6-bit superblocks (kq6) ------------------------------------
+
+def kq6_decode(ql, qh) -> np.ndarray:
+    """Low plane uint8 [N, K/2] and high plane uint8 [N, K/4] -> codes int8 [N, K] in [-32, 31]."""
+    ql = _arr(ql, np.uint8)
+    qh = _arr(qh, np.uint8)
+    N, K2 = ql.shape
+    K = 2 * K2
+    assert qh.shape == (N, K // 4)
+    codes = np.empty((N, K), np.int8)
+    _check(_load().oracle_kq6_decode(_ptr(ql), _ptr(qh), N, K, _ptr(codes)), "kq6_decode")
+    return codes
+
+
+def kq6_linear(q, d_a, ql, qh, sc, d_bits, nthreads: int = 0) -> np.ndarray:
+    """q int8 [b,K], d_a fp32 [b,K/32], ql uint8 [N,K/2], qh uint8 [N,K/4], sc int8 [N,K/16],
+    d fp16 bits [N,K/256] -> y bf16 bits [b,N]."""
+    q = _arr(q, np.int8)
+    d_a = _arr(d_a, np.float32)
+    ql = _arr(ql, np.uint8)
+    qh = _arr(qh, np.uint8)
+    sc = _arr(sc, np.int8)
+    d = _arr(d_bits, np.uint16)
+    b, K = q.shape
+    N = ql.shape[0]
+    assert ql.shape == (N, K // 2) and qh.shape == (N, K // 4) and sc.shape == (N, K // 16)
+    assert d.shape == (N, K // 256) and d_a.shape == (b, K // 32)
+    y = np.empty((b, N), np.uint16)
+    _check(_load().oracle_kq6_linear(_ptr(q), _ptr(d_a), _ptr(ql), _ptr(qh), _ptr(sc), _ptr(d), b, N, K, _ptr(y),
+                                     nthreads), "kq6_linear")
     return y

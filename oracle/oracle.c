@@ -800,3 +800,125 @@ int oracle_fp8_linear(const uint8_t *q, const float *s_a, const uint8_t *w, cons
         if (jobs[i].status != ORACLE_OK) status = jobs[i].status;
     return status;
 }
+
+
+/* ------------------------------------------------------------------------ */
+/* k-quant-style superblocks with 6-bit codes (kq6).                          */
+/* ------------------------------------------------------------------------ */
+/*
+ * [P1 "the mat-vec kernel"]: decoding a q6_k matrix reads each 4096-wide row
+ * as 16 weight blocks of 256 against int8 activations in blocks of 32; the
+ * integer products are exact and each block's integer result is scaled into
+ * an fp32 sum.  [P1 opening]: the pages' own decode workload is Qwen3-8B at
+ * q4_k_m and q6_k.  The pages give no bit layout, so the layout here is this
+ * library's own (not GGUF's), with the same 6.5625 bits per weight:
+ *   - a superblock is 256 consecutive weights of a row, s = k / 256;
+ *   - each weight is a code c in [-32, 31] stored as u = c + 32 in [0, 63];
+ *   - low plane  ql uint8 [N, K/2]: byte s*128 + i holds the low 4 bits of u
+ *     for element s*256 + i (bits 0-3) and s*256 + 128 + i (bits 4-7);
+ *   - high plane qh uint8 [N, K/4]: byte s*64 + i holds the top 2 bits of u
+ *     for element s*256 + 64*g + i in bits 2g, 2g+1 (g = 0..3);
+ *   - sub-scales sc int8 [N, K/16], one per 16 weights;
+ *   - superblock scale d fp16 [N, K/256].
+ * Reading (the pages name only the block scaling): a weight's integer value is
+ * sc[k/16] * c[k]; per 32-block j of activations, isum_j = sum of
+ * (sc * c) * q over its 32 elements, exact in int32 (|isum_j| <= 2^24, so
+ * fl32(isum_j) is exact too); the leaf is the blockq8 leaf with the
+ * superblock scale, p_j = fl(fl(fl32(isum_j) * d_a[t,j]) * fl32(d[n, j/8]));
+ * y = bf16 of the canonical tree over the K/32 leaves.
+ */
+
+/* Codes of an [N, K] kq6 matrix from its two planes, element by element. */
+int oracle_kq6_decode(const uint8_t *ql, const uint8_t *qh, int64_t N, int64_t K, int8_t *codes) {
+    if (!ql || !qh || !codes || N < 1 || K < 256 || K % 256 != 0) return ORACLE_ERR_ARGS;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t s = k / 256, e = k % 256;
+            const uint8_t lob = ql[n * (K / 2) + s * 128 + e % 128];
+            const int lo = e < 128 ? (lob & 15) : (lob >> 4);
+            const uint8_t hib = qh[n * (K / 4) + s * 64 + e % 64];
+            const int hi = (hib >> (2 * (e / 64))) & 3;
+            codes[n * K + k] = (int8_t)((lo | (hi << 4)) - 32);
+        }
+    return ORACLE_OK;
+}
+
+typedef struct {
+    const int8_t *q;
+    const float *da;
+    const int8_t *codes;
+    const int8_t *sc;
+    const uint16_t *d;
+    int64_t b, N, K;
+    uint16_t *y;
+    int64_t n0, n1;
+    int status;
+} kq6_job;
+
+static void *kq6_worker(void *arg) {
+    kq6_job *j = (kq6_job *)arg;
+    const int64_t K = j->K, m = K / 32;
+    float *leaf = (float *)malloc(sizeof(float) * (size_t)m);
+    if (!leaf) {
+        j->status = ORACLE_ERR_ARGS;
+        return NULL;
+    }
+    for (int64_t n = j->n0; n < j->n1; ++n)
+        for (int64_t t = 0; t < j->b; ++t) {
+            for (int64_t i = 0; i < m; ++i) {
+                int32_t isum = 0;
+                int64_t shadow = 0;
+                for (int64_t k = 32 * i; k < 32 * i + 32; ++k) {
+                    const int32_t wv = (int32_t)j->sc[n * (K / 16) + k / 16] * (int32_t)j->codes[n * K + k];
+                    isum += wv * (int32_t)j->q[t * K + k];
+                    shadow += (int64_t)wv * (int64_t)j->q[t * K + k];
+                }
+                if ((int64_t)isum != shadow) j->status = ORACLE_ERR_OVERFLOW;
+                leaf[i] = oracle_block_partial(isum, j->da[t * m + i], j->d[n * (K / 256) + i / 8]);
+            }
+            const float root = oracle_tree_sum(leaf, m);
+            j->y[t * j->N + n] = oracle_bf16_rne(f32_bits(root));
+        }
+    free(leaf);
+    return NULL;
+}
+
+/* q int8 [b, K], d_a fp32 [b, K/32], a kq6 matrix (ql, qh, sc, d as above)
+ * -> y bf16 [b, N]; K a multiple of 256.  Threads split output rows only. */
+int oracle_kq6_linear(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8_t *qh, const int8_t *sc,
+                      const uint16_t *d, int64_t b, int64_t N, int64_t K, uint16_t *y, int nthreads) {
+    if (!q || !d_a || !ql || !qh || !sc || !d || !y || b < 1 || N < 1 || K < 256 || K % 256 != 0)
+        return ORACLE_ERR_ARGS;
+    int8_t *codes = (int8_t *)malloc((size_t)(N * K));
+    if (!codes) return ORACLE_ERR_ARGS;
+    int status = oracle_kq6_decode(ql, qh, N, K, codes);
+    if (status != ORACLE_OK) {
+        free(codes);
+        return status;
+    }
+    if (nthreads <= 0) nthreads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > N) nthreads = (int)N;
+    kq6_job jobs[256];
+    pthread_t th[256];
+    int started[256];
+    for (int i = 0; i < nthreads; ++i) {
+        kq6_job jb = {q, d_a, codes, sc, d, b, N, K, y, N * i / nthreads, N * (i + 1) / nthreads, ORACLE_OK};
+        jobs[i] = jb;
+        started[i] = 0;
+    }
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, kq6_worker, &jobs[i]) == 0)
+            started[i] = 1;
+        else
+            kq6_worker(&jobs[i]);
+    }
+    kq6_worker(&jobs[0]);
+    for (int i = 1; i < nthreads; ++i)
+        if (started[i]) pthread_join(th[i], NULL);
+    for (int i = 0; i < nthreads; ++i)
+        if (jobs[i].status != ORACLE_OK) status = jobs[i].status;
+    free(codes);
+    return status;
+}

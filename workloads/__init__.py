@@ -27,7 +27,11 @@ Recipes (numpy ``Generator(PCG64(seed))``; draws happen in the order listed):
   * q8_0-style block weights: real weights ``standard_normal``, per aligned
     32-block an fp16 scale ``d = fp16(amax / 127)`` and int8 codes
     ``clamp(rint(w / d), -127, 127)`` (0 where d == 0).  This is the
-    preparation of a weight file, not a step of the linear layer.
+    preparation of a weight file, not a step of the linear layer;
+  * kq6 superblock weights (256 weights per superblock, this library's own
+    layout): codes uniform on [-32, 31], int8 sub-scales (one per 16
+    weights) uniform on [-127, 127], fp16 superblock scales log-uniform on
+    [1e-6, 1e-4]; the codes are then laid out in the two bit planes.
 
 The layer shapes follow Qwen3 models (hidden size, intermediate size and the
 packed qkv / gate_up projections); no model weights are used or needed.
@@ -294,3 +298,58 @@ def fp8_layer(i: int, tokens: int = 16) -> FP8Layer:
     x = normal_bf16(g, tokens, K)
     x, _ = add_outlier_channels(g, x)
     return FP8Layer(name, K, N, w, s_w, x)
+
+
+# -- kq6: k-quant-style superblocks of 256 weights with 6-bit codes ------------------
+#
+# Layout (this library's own; the pages give none): code c in [-32, 31] kept as
+# u = c + 32.  Superblock s holds weights 256 s .. 256 s + 255 of a row.
+#   low plane  [N, K/2]: byte 128 s + i = (u[i] & 15) | (u[128 + i] & 15) << 4
+#   high plane [N, K/4]: byte  64 s + i = sum over g of ((u[64 g + i] >> 4) & 3) << 2 g
+# with u indexed within the superblock.
+
+KQ6_SHAPES = [("o", 4096, 4096), ("down", 12288, 4096)]
+SEED_KQ6 = 8001
+
+
+def kq6_pack(codes: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """codes int8 [N, K] in [-32, 31] -> (low plane uint8 [N, K/2], high plane uint8 [N, K/4])."""
+    N, K = codes.shape
+    assert K % 256 == 0 and codes.min() >= -32 and codes.max() <= 31
+    u = (codes.astype(np.int16) + 32).astype(np.uint8).reshape(N, K // 256, 256)
+    lo = u & 15
+    ql = lo[:, :, :128] | (lo[:, :, 128:] << 4)
+    hi = (u >> 4) & 3
+    qh = hi[:, :, 0:64] | (hi[:, :, 64:128] << 2) | (hi[:, :, 128:192] << 4) | (hi[:, :, 192:256] << 6)
+    return ql.reshape(N, K // 2).astype(np.uint8), qh.reshape(N, K // 4).astype(np.uint8)
+
+
+def kq6_weights(g: np.random.Generator, N: int, K: int):
+    """-> (codes int8 [N, K], sub-scales int8 [N, K/16], superblock scales fp16 bits [N, K/256])."""
+    codes = g.integers(-32, 32, (N, K), dtype=np.int8)
+    sc = g.integers(-127, 128, (N, K // 16), dtype=np.int8)
+    d = np.exp(g.uniform(np.log(1e-6), np.log(1e-4), (N, K // 256))).astype(np.float32)
+    return codes, sc, d.astype(np.float16).view(np.uint16)
+
+
+@dataclass
+class KQ6Layer:
+    name: str
+    K: int
+    N: int
+    codes: np.ndarray    # int8 [N, K]
+    ql: np.ndarray       # uint8 [N, K/2]
+    qh: np.ndarray       # uint8 [N, K/4]
+    sc: np.ndarray       # int8 [N, K/16]
+    d: np.ndarray        # fp16 bits [N, K/256]
+    x: np.ndarray        # bf16 bits [T, K]
+
+
+def kq6_layer(i: int, tokens: int = 16) -> KQ6Layer:
+    """Qwen3-8B o (4096 -> 4096) or down (12288 -> 4096) projection as kq6 weights."""
+    name, K, N = KQ6_SHAPES[i]
+    g = rng(SEED_KQ6 + i)
+    codes, sc, d = kq6_weights(g, N, K)
+    ql, qh = kq6_pack(codes)
+    x = normal_bf16(g, tokens, K)
+    return KQ6Layer(name, K, N, codes, ql, qh, sc, d, x)
