@@ -276,10 +276,15 @@ def main():
 
     if args.extra:
         ext = []
+        def copies_past_cache(nbytes):  # weight copies in rotation: more than 512 MB, past the 256 MB cache
+            return max(2, -(-512 * 2 ** 20 // int(nbytes)))
+
         for i in range(2):
             Lb = W.blockq8_layer(i, tokens=16)
+            by = Lb.N * Lb.K * (1 + 2 / 32)
+            nc = copies_past_cache(by)
             wq = torch.from_numpy(Lb.w).to(dev)
-            wqs = [wq] + [wq.clone() for _ in range(3)]
+            wqs = [wq] + [wq.clone() for _ in range(nc - 1)]
             dw = torch.from_numpy(Lb.d_w.view(np.int16)).view(torch.float16).to(dev)
             xb = torch.from_numpy(Lb.x.view(np.int16)).view(torch.bfloat16).to(dev)
             qb, db = iqd.quantize_activations(xb, group=32)
@@ -287,15 +292,36 @@ def main():
                 yb = torch.empty((b, Lb.N), dtype=torch.bfloat16, device=dev)
 
                 def bq(b=b, yb=yb):
-                    for c in range(4):
+                    for c in range(nc):
                         iqd.blockq8_linear(qb[:b], db[:b], wqs[c], dw, y=yb)
                 g = capture(bq)
                 g.replay()
-                us = time_graph(g, 10) * 1e3 / 4
-                by = Lb.N * Lb.K * (1 + 2 / 32)
+                us = time_graph(g, 10) * 1e3 / nc
                 ext.append({"op": "blockq8_linear", "K": Lb.K, "N": Lb.N, "b": b, "us": round(us, 2),
                             "weight_GBs": round(by / (us * 1e-6) / 1e9, 1)})
             del wqs, wq
+        # kq6 superblocks (6.5625 bits per weight) on the Qwen3-8B o and down shapes
+        for i in range(len(W.KQ6_SHAPES)):
+            Lk = W.kq6_layer(i, tokens=16)
+            by = Lk.N * Lk.K * (0.5 + 0.25 + 1 / 16) + Lk.N * (Lk.K // 256) * 2
+            nc = copies_past_cache(by)
+            planes = [(torch.from_numpy(Lk.ql).to(dev), torch.from_numpy(Lk.qh).to(dev), torch.from_numpy(Lk.sc).to(dev))]
+            planes += [tuple(p.clone() for p in planes[0]) for _ in range(nc - 1)]
+            dk = torch.from_numpy(Lk.d.view(np.int16)).view(torch.float16).to(dev)
+            xk = torch.from_numpy(Lk.x.view(np.int16)).view(torch.bfloat16).to(dev)
+            qk, dak = iqd.quantize_activations(xk, group=32)
+            for b in (1, 4, 8):
+                yk = torch.empty((b, Lk.N), dtype=torch.bfloat16, device=dev)
+
+                def kq(b=b, yk=yk):
+                    for c in range(nc):
+                        iqd.kq6_linear(qk[:b], dak[:b], *planes[c], dk, y=yk)
+                g = capture(kq)
+                g.replay()
+                us = time_graph(g, 10) * 1e3 / nc
+                ext.append({"op": "kq6_linear", "K": Lk.K, "N": Lk.N, "b": b, "us": round(us, 2),
+                            "weight_GBs": round(by / (us * 1e-6) / 1e9, 1)})
+            del planes
         Ll = W.lm_head_layer(tokens=8)
         wl = torch.from_numpy(Ll.w).to(dev)
         swl = torch.from_numpy(Ll.s_w).to(dev)

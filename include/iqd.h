@@ -67,7 +67,7 @@ typedef enum {
 } iqd_status;
 
 /* Operation codes for iqd_workspace_bytes. */
-enum { IQD_OP_W8A8 = 1, IQD_OP_BLOCKQ8 = 2, IQD_OP_LM_HEAD = 3, IQD_OP_W8A8_BF16 = 4, IQD_OP_FP8 = 5 };
+enum { IQD_OP_W8A8 = 1, IQD_OP_BLOCKQ8 = 2, IQD_OP_LM_HEAD = 3, IQD_OP_W8A8_BF16 = 4, IQD_OP_FP8 = 5, IQD_OP_KQ6 = 6 };
 
 #define IQD_K_MAX 131071
 #define IQD_SPLIT_K_MAX 64
@@ -173,6 +173,38 @@ int w8a8_linear_bf16(const void *x_bf16, const int8_t *w, const float *s_w, int6
 int blockq8_linear(const int8_t *q, const float *d_a, const int8_t *w, const void *d_w_fp16,
                    int64_t b, int64_t N, int64_t K, void *y_bf16, int32_t split_k, void *workspace,
                    size_t workspace_bytes, void *stream);
+
+/*
+ * kq6_linear - linear layer over k-quant-style superblocks of 256 weights
+ * with 6-bit codes.
+ *
+ * [P1 "the mat-vec kernel"]: a q6_k row is read as weight blocks of 256
+ * against int8 activations in blocks of 32; each block's exact integer
+ * result is scaled into fp32.  The pages give no bit layout; this one is the
+ * library's own (6.5625 bits per weight, the same as q6_k's), packed in
+ * weight order so that 16 consecutive weights are 8 + 4 contiguous bytes:
+ *   weight k of a row has a code c in [-32, 31] kept as u = c + 32, a
+ *   sub-scale sc[k / 16] and the scale d[k / 256] of its superblock;
+ *   ql  in  uint8 [N, K/2]:  u & 15 of weight k in bits 4 (k%2) .. +3 of byte k/2
+ *   qh  in  uint8 [N, K/4]:  u >> 4 of weight k in bits 2 (k%4) .. +1 of byte k/4
+ *   sc  in  int8  [N, K/16]  sub-scales, one per 16 weights
+ *   d_fp16 in fp16 [N, K/256] superblock scales
+ * The result is the blockq8_linear tree with integer weights sc * c and the
+ * superblock's scale as every block's weight scale:
+ *     isum_j = sum over block j of (sc[k/16] * c[k]) * q[t,k]   (exact int32)
+ *     p_j    = fl( fl( fl32(isum_j) * d_a[t,j] ) * fl32(d[n, j/8]) )
+ *     y      = bf16(canonical tree over the K/32 leaves)
+ * |isum_j| <= 2^24, so fl32(isum_j) is exact.
+ *
+ *   q      in  int8 [b, K]       d_a  in  fp32 [b, K/32]
+ *   y_bf16 out bf16 [b, N]
+ *   split_k    as blockq8_linear (aligned subtrees of the same tree).
+ * K must be a multiple of 256.  q, ql and qh 16-byte aligned.
+ * Errors: as blockq8_linear.
+ */
+int kq6_linear(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8_t *qh, const int8_t *sc,
+               const void *d_fp16, int64_t b, int64_t N, int64_t K, void *y_bf16, int32_t split_k,
+               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * lm_head_argmax - W8A8 vocab projection and the winning token per row.

@@ -51,8 +51,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int
 struct BqArgs {
     const int8_t *q;
     const float *d_a;
-    const int8_t *w;
-    const uint16_t *d_w;
+    const int8_t *w;       // q8_0: int8 weights [N, K]
+    const uint16_t *d_w;   // q8_0: fp16 [N, K/32]; kq6: superblock scales fp16 [N, K/256]
+    const uint8_t *ql;     // kq6: low plane [N, K/2]
+    const uint8_t *qh;     // kq6: high plane [N, K/4]
+    const int8_t *sc;      // kq6: sub-scales [N, K/16]
     int N, K, m, L;
     uint16_t *y;
     float *part;  // [split, B, N] subtree roots when split > 1
@@ -81,6 +84,29 @@ __device__ __forceinline__ float carry_insert(float (&stk)[kMaxLevels], int i, f
     return v;
 }
 
+// kq6: the 16 codes of one sub-block from its 8 bytes of the low plane (lo0,
+// lo1: nibble i is weight i) and 4 bytes of the high plane (hi: 2-bit field i
+// is weight i).  Output word w holds weights 4w .. 4w+3, one per byte:
+// nibbles spread to bytes by two shift-or-mask steps, 2-bit fields likewise,
+// u = lo | hi << 4 in [0, 63], and the int8 code u - 32 for four bytes at
+// once: (u | 0x80) - 0x20 = u + 0x60 borrows nothing from the next byte, and
+// flipping bit 7 back gives u - 32 in two's complement.
+__device__ __forceinline__ v4i kq6_codes(uint32_t lo0, uint32_t lo1, uint32_t hi) {
+    v4i c;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t v = ((w < 2 ? lo0 : lo1) >> (16 * (w & 1))) & 0xFFFFu;
+        const uint32_t t = (v | (v << 8)) & 0x00FF00FFu;
+        const uint32_t l = (t | (t << 4)) & 0x0F0F0F0Fu;
+        const uint32_t hb = (hi >> (8 * w)) & 0xFFu;
+        const uint32_t s = (hb | (hb << 12)) & 0x000F000Fu;
+        const uint32_t h = (s | (s << 6)) & 0x03030303u;
+        const uint32_t u = l | (h << 4);
+        c[w] = static_cast<int32_t>(((u | 0x80808080u) - 0x20202020u) ^ 0x80808080u);
+    }
+    return c;
+}
+
 struct AddI {
     __device__ int32_t operator()(int32_t a, int32_t b) const { return a + b; }
 };
@@ -88,7 +114,13 @@ struct AddF {
     __device__ float operator()(float a, float b) const { return a + b; }
 };
 
-template <int B, int RS, int U>
+// KQ: the weights are kq6 superblocks (two bit planes, a sub-scale per 16
+// weights, an fp16 scale per 256) instead of q8_0 blocks.  The lane's 16
+// weights are then one sub-block; its integer dot is multiplied by the
+// sub-scale before the lane pair adds its halves, so the pair forms
+// isum_j = sum of (sc * c) * q over the block, and the block's weight scale is
+// its superblock's.
+template <int B, int RS, int U, bool KQ>
 __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
     __shared__ float red[kBqWaves][kWave];
     const int lane = lane_id();
@@ -120,9 +152,16 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
         const int rfirst = min(row0, N - 1);
         const int rlast = min(row0 + RS - 1, N - 1);
         const int nrows = rlast - rfirst + 1;
-        const __amdgpu_buffer_rsrc_t wr = buf_rsrc(a.w + static_cast<int64_t>(rfirst) * K, static_cast<int64_t>(nrows) * K);
+        const int dstride = KQ ? K / 256 : m;  // weight scales per row
+        const __amdgpu_buffer_rsrc_t wr =
+            KQ ? buf_rsrc(a.ql + static_cast<int64_t>(rfirst) * (K / 2), static_cast<int64_t>(nrows) * (K / 2))
+               : buf_rsrc(a.w + static_cast<int64_t>(rfirst) * K, static_cast<int64_t>(nrows) * K);
+        const __amdgpu_buffer_rsrc_t hr =
+            buf_rsrc(KQ ? a.qh + static_cast<int64_t>(rfirst) * (K / 4) : nullptr, KQ ? static_cast<int64_t>(nrows) * (K / 4) : 0);
+        const __amdgpu_buffer_rsrc_t scr =
+            buf_rsrc(KQ ? a.sc + static_cast<int64_t>(rfirst) * (K / 16) : nullptr, KQ ? static_cast<int64_t>(nrows) * (K / 16) : 0);
         const __amdgpu_buffer_rsrc_t dwr =
-            buf_rsrc(a.d_w + static_cast<int64_t>(rfirst) * m, static_cast<int64_t>(nrows) * m * 2);
+            buf_rsrc(a.d_w + static_cast<int64_t>(rfirst) * dstride, static_cast<int64_t>(nrows) * dstride * 2);
         int roff[RS];
 #pragma unroll
         for (int r = 0; r < RS; ++r) roff[r] = min(row0 + r, N - 1) - rfirst;
@@ -134,8 +173,8 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
             // All loads of U slots go out before any is used, and no branch
             // surrounds them: blocks past m (or slots past the wave's range)
             // read zeros from out-of-range offsets.
-            v4i wv[U][RS], av[U][B];
-            uint32_t dwb[U][RS];
+            v4i wv[U][RS], av[U][B];  // kq6: low plane in words 0-1, high plane in word 2
+            uint32_t dwb[U][RS], scb[KQ ? U : 1][RS];
             float dav[U][B];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -144,8 +183,24 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
                 const int kb = j * 32 + 16 * half;
 #pragma unroll
                 for (int r = 0; r < RS; ++r) {
-                    wv[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wr, live ? roff[r] * K + kb : kBqOob, 0, 2);
-                    dwb[u][r] = __builtin_amdgcn_raw_buffer_load_b16(dwr, live ? 2 * (roff[r] * m + j) : kBqOob, 0, 0);
+                    if constexpr (KQ) {
+                        // weights kb .. kb + 15: 8 bytes of the low plane, 4 of the high
+                        const auto lo = __builtin_amdgcn_raw_buffer_load_b64(
+                            wr, live ? roff[r] * (K / 2) + kb / 2 : kBqOob, 0, 2);
+                        wv[u][r][0] = static_cast<int32_t>(lo[0]);
+                        wv[u][r][1] = static_cast<int32_t>(lo[1]);
+                        wv[u][r][2] = static_cast<int32_t>(
+                            __builtin_amdgcn_raw_buffer_load_b32(hr, live ? roff[r] * (K / 4) + kb / 4 : kBqOob, 0, 2));
+                        wv[u][r][3] = 0;
+                        scb[u][r] = __builtin_amdgcn_raw_buffer_load_b8(scr, live ? roff[r] * (K / 16) + 2 * j + half : kBqOob,
+                                                                        0, 0);
+                        dwb[u][r] =
+                            __builtin_amdgcn_raw_buffer_load_b16(dwr, live ? 2 * (roff[r] * dstride + (j >> 3)) : kBqOob, 0, 0);
+                    } else {
+                        wv[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wr, live ? roff[r] * K + kb : kBqOob, 0, 2);
+                        dwb[u][r] =
+                            __builtin_amdgcn_raw_buffer_load_b16(dwr, live ? 2 * (roff[r] * dstride + j) : kBqOob, 0, 0);
+                    }
                 }
 #pragma unroll
                 for (int t = 0; t < B; ++t) {
@@ -165,10 +220,21 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
                     int32_t isum[NP];
 #pragma unroll
                     for (int v = 0; v < NP; ++v) isum[v] = 0;
+                    if constexpr (KQ) {
 #pragma unroll
-                    for (int t = 0; t < B; ++t)
+                        for (int r = 0; r < RS; ++r) {
+                            const v4i c = kq6_codes(static_cast<uint32_t>(wv[u][r][0]), static_cast<uint32_t>(wv[u][r][1]),
+                                                    static_cast<uint32_t>(wv[u][r][2]));
+                            const int32_t scv = static_cast<int8_t>(scb[u][r]);
 #pragma unroll
-                        for (int r = 0; r < RS; ++r) isum[r * B + t] = dot16(wv[u][r], av[u][t], isum[r * B + t]);
+                            for (int t = 0; t < B; ++t) isum[r * B + t] = dot16(c, av[u][t], 0) * scv;
+                        }
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < B; ++t)
+#pragma unroll
+                            for (int r = 0; r < RS; ++r) isum[r * B + t] = dot16(wv[u][r], av[u][t], isum[r * B + t]);
+                    }
                     float dwv[RS];
 #pragma unroll
                     for (int r = 0; r < RS; ++r) dwv[r] = fp16_to_f32(static_cast<uint16_t>(dwb[u][r]));
@@ -240,16 +306,16 @@ __global__ __launch_bounds__(256) void k_blockq8_combine(const float *__restrict
     y[i] = bf16_rne(root);
 }
 
-template <int B, int RS, int U>
+template <int B, int RS, int U, bool KQ>
 hipError_t launch_rs(const BqArgs &a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((k_blockq8_matvec<B, RS, U>), dim3(grid, a.split), dim3(kBqThreads), 0, st, a);
+    hipLaunchKernelGGL((k_blockq8_matvec<B, RS, U, KQ>), dim3(grid, a.split), dim3(kBqThreads), 0, st, a);
     return hipGetLastError();
 }
 
 // Four rows per wave: each activation load serves four weight rows (measured
 // on MI355X at 4096 -> 4096 and 12288 -> 4096 against 1, 2 and 8 rows).  At
 // b = 1 a wave with at least four slots keeps two slots of loads in flight.
-template <int B>
+template <int B, bool KQ>
 hipError_t launch_b(const BqArgs &base, hipStream_t st) {
     constexpr int RS = 4;
     BqArgs a = base;
@@ -264,9 +330,49 @@ hipError_t launch_b(const BqArgs &base, hipStream_t st) {
     int grid = device_info().cus * 8;
     if (grid > a.nsteps) grid = a.nsteps;
     if constexpr (B == 1) {
-        if (nss / ks >= 4) return launch_rs<B, RS, 2>(a, grid, st);
+        if (nss / ks >= 4) return launch_rs<B, RS, 2, KQ>(a, grid, st);
     }
-    return launch_rs<B, RS, 1>(a, grid, st);
+    return launch_rs<B, RS, 1, KQ>(a, grid, st);
+}
+
+template <bool KQ>
+hipError_t launch_any_b(const BqArgs &a, int b, hipStream_t st) {
+    switch (b) {
+        case 1: return launch_b<1, KQ>(a, st);
+        case 2: return launch_b<2, KQ>(a, st);
+        case 3: return launch_b<3, KQ>(a, st);
+        case 4: return launch_b<4, KQ>(a, st);
+        case 5: return launch_b<5, KQ>(a, st);
+        case 6: return launch_b<6, KQ>(a, st);
+        case 7: return launch_b<7, KQ>(a, st);
+        case 8: return launch_b<8, KQ>(a, st);
+        case 9: return launch_b<9, KQ>(a, st);
+        case 10: return launch_b<10, KQ>(a, st);
+        case 11: return launch_b<11, KQ>(a, st);
+        case 12: return launch_b<12, KQ>(a, st);
+        case 13: return launch_b<13, KQ>(a, st);
+        case 14: return launch_b<14, KQ>(a, st);
+        case 15: return launch_b<15, KQ>(a, st);
+        case 16: return launch_b<16, KQ>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+BqArgs bq_args(int N, int K, uint16_t *y, int split, float *part) {
+    const int m = K / 32;
+    int L = 1;
+    while (L < m) L *= 2;
+    BqArgs a{};
+    a.N = N;
+    a.K = K;
+    a.m = m;
+    a.L = L;
+    a.y = y;
+    a.part = part;
+    a.split = split;
+    a.nslots = L >= 32 ? L / 32 : 1;
+    a.ks = 1;
+    return a;
 }
 
 }  // namespace
@@ -280,30 +386,25 @@ hipError_t launch_blockq8_matvec(const int8_t *q, const float *d_a, const int8_t
     // b = 9 on, where its activations fit in LDS.
     if (b >= 9 && blockq8_mfvec_fits(b, N, K, split))
         return launch_blockq8_mfvec(q, d_a, w, d_w, b, N, K, y, split, part, st);
-    const int m = K / 32;
-    int L = 1;
-    while (L < m) L *= 2;
-    const int nslots = L >= 32 ? L / 32 : 1;
-    BqArgs a{q, d_a, w, d_w, N, K, m, L, y, part, split, nslots, 1, 0};
-    switch (b) {
-        case 1: return launch_b<1>(a, st);
-        case 2: return launch_b<2>(a, st);
-        case 3: return launch_b<3>(a, st);
-        case 4: return launch_b<4>(a, st);
-        case 5: return launch_b<5>(a, st);
-        case 6: return launch_b<6>(a, st);
-        case 7: return launch_b<7>(a, st);
-        case 8: return launch_b<8>(a, st);
-        case 9: return launch_b<9>(a, st);
-        case 10: return launch_b<10>(a, st);
-        case 11: return launch_b<11>(a, st);
-        case 12: return launch_b<12>(a, st);
-        case 13: return launch_b<13>(a, st);
-        case 14: return launch_b<14>(a, st);
-        case 15: return launch_b<15>(a, st);
-        case 16: return launch_b<16>(a, st);
-        default: return hipErrorInvalidValue;
-    }
+    BqArgs a = bq_args(N, K, y, split, part);
+    a.q = q;
+    a.d_a = d_a;
+    a.w = w;
+    a.d_w = d_w;
+    return launch_any_b<false>(a, b, st);
+}
+
+hipError_t launch_kq6_matvec(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8_t *qh, const int8_t *sc,
+                             const uint16_t *d, int b, int N, int K, uint16_t *y, int split, float *part,
+                             hipStream_t st) {
+    BqArgs a = bq_args(N, K, y, split, part);
+    a.q = q;
+    a.d_a = d_a;
+    a.ql = ql;
+    a.qh = qh;
+    a.sc = sc;
+    a.d_w = d;
+    return launch_any_b<true>(a, b, st);
 }
 
 hipError_t launch_blockq8_combine(const float *part, int b, int N, int split, uint16_t *y,

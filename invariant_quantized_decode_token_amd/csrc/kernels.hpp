@@ -57,6 +57,11 @@ hipError_t launch_blockq8_mfvec(const int8_t *q, const float *d_a, const int8_t 
                                 int N, int K, uint16_t *y, int split, float *part, hipStream_t st);
 hipError_t launch_blockq8_combine(const float *part, int b, int N, int split, uint16_t *y,
                                   hipStream_t st);
+// The same block mat-vec over kq6 superblocks (1 <= b <= 16; split as above,
+// finished by launch_blockq8_combine).
+hipError_t launch_kq6_matvec(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8_t *qh, const int8_t *sc,
+                             const uint16_t *d, int b, int N, int K, uint16_t *y, int split, float *part,
+                             hipStream_t st);
 
 // Argmax over bf16 logits [b, N]: smallest index of the row maximum.  part is
 // scratch for argmax_chunks(N) 64-bit keys per row.

@@ -814,10 +814,10 @@ int oracle_fp8_linear(const uint8_t *q, const float *s_a, const uint8_t *w, cons
  * library's own (not GGUF's), with the same 6.5625 bits per weight:
  *   - a superblock is 256 consecutive weights of a row, s = k / 256;
  *   - each weight is a code c in [-32, 31] stored as u = c + 32 in [0, 63];
- *   - low plane  ql uint8 [N, K/2]: byte s*128 + i holds the low 4 bits of u
- *     for element s*256 + i (bits 0-3) and s*256 + 128 + i (bits 4-7);
- *   - high plane qh uint8 [N, K/4]: byte s*64 + i holds the top 2 bits of u
- *     for element s*256 + 64*g + i in bits 2g, 2g+1 (g = 0..3);
+ *   - low plane  ql uint8 [N, K/2]: the low 4 bits of u for weight k are
+ *     bits 4*(k%2) .. 4*(k%2)+3 of byte k/2;
+ *   - high plane qh uint8 [N, K/4]: the top 2 bits of u for weight k are
+ *     bits 2*(k%4), 2*(k%4)+1 of byte k/4;
  *   - sub-scales sc int8 [N, K/16], one per 16 weights;
  *   - superblock scale d fp16 [N, K/256].
  * Reading (the pages name only the block scaling): a weight's integer value is
@@ -833,11 +833,8 @@ int oracle_kq6_decode(const uint8_t *ql, const uint8_t *qh, int64_t N, int64_t K
     if (!ql || !qh || !codes || N < 1 || K < 256 || K % 256 != 0) return ORACLE_ERR_ARGS;
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k) {
-            const int64_t s = k / 256, e = k % 256;
-            const uint8_t lob = ql[n * (K / 2) + s * 128 + e % 128];
-            const int lo = e < 128 ? (lob & 15) : (lob >> 4);
-            const uint8_t hib = qh[n * (K / 4) + s * 64 + e % 64];
-            const int hi = (hib >> (2 * (e / 64))) & 3;
+            const int lo = (ql[n * (K / 2) + k / 2] >> (4 * (k % 2))) & 15;
+            const int hi = (qh[n * (K / 4) + k / 4] >> (2 * (k % 4))) & 3;
             codes[n * K + k] = (int8_t)((lo | (hi << 4)) - 32);
         }
     return ORACLE_OK;

@@ -28,22 +28,22 @@ def planes(codes):
 
 def test_planes_match_bytes_worked_by_hand():
     """All codes 0 (u = 32 = 0b10_0000): every low byte 0x00, every high byte
-    0b10101010.  Then element 130 of superblock 0 set to 31 (u = 63): low
-    byte 130 - 128 = 2 gets 0xF in its upper nibble; high byte 130 - 128 = 2
-    gets 0b11 in bits 4-5 (element 130 = 64 * 2 + 2).  Element 256 + 5 set to
-    -32 (u = 0): low byte 128 + 5 loses nothing (already 0), high byte
-    64 + 5 gets 0b00 in bits 0-1."""
+    0b10101010.  Then weight 131 set to 31 (u = 63 = 0b11_1111): low byte
+    131 / 2 = 65 gets 0xF in its upper nibble (131 is odd); high byte
+    131 / 4 = 32 gets 0b11 in bits 6-7 (131 % 4 = 3).  Weight 256 + 5 = 261
+    set to -32 (u = 0): low byte 130 keeps 0x00, high byte 65 gets 0b00 in
+    bits 2-3 (261 % 4 = 1)."""
     c = np.zeros((1, 512), np.int8)
     ql, qh = planes(c)
     assert (ql == 0x00).all() and (qh == 0xAA).all()
-    c[0, 130] = 31
-    c[0, 256 + 5] = -32
+    c[0, 131] = 31
+    c[0, 261] = -32
     ql, qh = planes(c)
     want_ql = np.zeros(256, np.uint8)
-    want_ql[2] = 0xF0
+    want_ql[65] = 0xF0
     want_qh = np.full(128, 0xAA, np.uint8)
-    want_qh[2] = 0xBA                      # 0b10_11_10_10
-    want_qh[64 + 5] = 0xA8                 # 0b10_10_10_00
+    want_qh[32] = 0xEA                     # 0b11_10_10_10
+    want_qh[65] = 0xA2                     # 0b10_10_00_10
     assert np.array_equal(ql[0], want_ql)
     assert np.array_equal(qh[0], want_qh)
     assert np.array_equal(oracle.kq6_decode(ql, qh), c)

@@ -303,10 +303,9 @@ def fp8_layer(i: int, tokens: int = 16) -> FP8Layer:
 # -- kq6: k-quant-style superblocks of 256 weights with 6-bit codes ------------------
 #
 # Layout (this library's own; the pages give none): code c in [-32, 31] kept as
-# u = c + 32.  Superblock s holds weights 256 s .. 256 s + 255 of a row.
-#   low plane  [N, K/2]: byte 128 s + i = (u[i] & 15) | (u[128 + i] & 15) << 4
-#   high plane [N, K/4]: byte  64 s + i = sum over g of ((u[64 g + i] >> 4) & 3) << 2 g
-# with u indexed within the superblock.
+# u = c + 32, packed in weight order within each row.
+#   low plane  [N, K/2]: byte i = (u[2 i] & 15) | (u[2 i + 1] & 15) << 4
+#   high plane [N, K/4]: byte i = sum over g < 4 of (u[4 i + g] >> 4) << 2 g
 
 KQ6_SHAPES = [("o", 4096, 4096), ("down", 12288, 4096)]
 SEED_KQ6 = 8001
@@ -316,12 +315,12 @@ def kq6_pack(codes: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """codes int8 [N, K] in [-32, 31] -> (low plane uint8 [N, K/2], high plane uint8 [N, K/4])."""
     N, K = codes.shape
     assert K % 256 == 0 and codes.min() >= -32 and codes.max() <= 31
-    u = (codes.astype(np.int16) + 32).astype(np.uint8).reshape(N, K // 256, 256)
+    u = (codes.astype(np.int16) + 32).astype(np.uint8)
     lo = u & 15
-    ql = lo[:, :, :128] | (lo[:, :, 128:] << 4)
-    hi = (u >> 4) & 3
-    qh = hi[:, :, 0:64] | (hi[:, :, 64:128] << 2) | (hi[:, :, 128:192] << 4) | (hi[:, :, 192:256] << 6)
-    return ql.reshape(N, K // 2).astype(np.uint8), qh.reshape(N, K // 4).astype(np.uint8)
+    ql = lo[:, 0::2] | (lo[:, 1::2] << 4)
+    hi = u >> 4
+    qh = hi[:, 0::4] | (hi[:, 1::4] << 2) | (hi[:, 2::4] << 4) | (hi[:, 3::4] << 6)
+    return ql.astype(np.uint8), qh.astype(np.uint8)
 
 
 def kq6_weights(g: np.random.Generator, N: int, K: int):
