@@ -89,6 +89,7 @@ def _load():
         "oracle_fp8_linear": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, ctypes.c_int]),
         "oracle_kq6_decode": (ctypes.c_int, [P, P, I64, I64, P]),
         "oracle_kq6_linear": (ctypes.c_int, [P, P, P, P, P, P, I64, I64, I64, P, ctypes.c_int]),
+        "oracle_kq4_linear": (ctypes.c_int, [P, P, P, P, P, I64, I64, I64, P, ctypes.c_int]),
         "oracle_attn_decode": (ctypes.c_int, [P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, I64, f32, I64, I64,
                                               P, ctypes.c_int]),
     }
@@ -366,4 +367,22 @@ def kq6_linear(q, d_a, ql, qh, sc, d_bits, nthreads: int = 0) -> np.ndarray:
     y = np.empty((b, N), np.uint16)
     _check(_load().oracle_kq6_linear(_ptr(q), _ptr(d_a), _ptr(ql), _ptr(qh), _ptr(sc), _ptr(d), b, N, K, _ptr(y),
                                      nthreads), "kq6_linear")
+    return y
+
+
+def kq4_linear(q, d_a, ql, scm, dm_bits, nthreads: int = 0) -> np.ndarray:
+    """q int8 [b,K], d_a fp32 [b,K/32], ql uint8 [N,K/2], scm uint8 [N,K/32,2] (sub-scale, minimum),
+    dm fp16 bits [N,K/256,2] (d, dmin) -> y bf16 bits [b,N]."""
+    q = _arr(q, np.int8)
+    d_a = _arr(d_a, np.float32)
+    ql = _arr(ql, np.uint8)
+    scm = _arr(scm, np.uint8)
+    dm = _arr(dm_bits, np.uint16)
+    b, K = q.shape
+    N = ql.shape[0]
+    assert ql.shape == (N, K // 2) and scm.shape == (N, K // 32, 2) and dm.shape == (N, K // 256, 2)
+    assert d_a.shape == (b, K // 32)
+    y = np.empty((b, N), np.uint16)
+    _check(_load().oracle_kq4_linear(_ptr(q), _ptr(d_a), _ptr(ql), _ptr(scm), _ptr(dm), b, N, K, _ptr(y), nthreads),
+           "kq4_linear")
     return y

@@ -919,3 +919,104 @@ int oracle_kq6_linear(const int8_t *q, const float *d_a, const uint8_t *ql, cons
     free(codes);
     return status;
 }
+
+
+/* ------------------------------------------------------------------------ */
+/* k-quant-style superblocks with 4-bit codes and minimums (kq4).             */
+/* ------------------------------------------------------------------------ */
+/*
+ * [P1 opening]: the pages' decode workload is Qwen3-8B at q4_k_m; [P1 "the
+ * mat-vec kernel"] fixes the integer-then-scale structure per activation block
+ * of 32.  The 4-bit form subtracts a per-sub-block minimum.  Layout (this
+ * library's own):
+ *   - weight k has a code q in [0, 15]; low plane ql uint8 [N, K/2] as kq6:
+ *     q of weight k in bits 4*(k%2) .. +3 of byte k/2;
+ *   - per 32 weights (one activation block) j: a sub-scale sc_j and a minimum
+ *     m_j, both in [0, 63], as the byte pair scm[n, j] = (sc_j, m_j),
+ *     uint8 [N, K/32, 2];
+ *   - per superblock of 256: the fp16 pair dm[n, s] = (d, dmin), [N, K/256, 2].
+ * Reading: weight k stands for d * sc_j * q_k - dmin * m_j.  Per block both
+ * integer sums are exact,
+ *   isum_j = sc_j * sum q*a  (|isum_j| <= 63 * 32 * 15 * 128 < 2^22),
+ *   msum_j = m_j * sum a     (|msum_j| <= 63 * 32 * 128 < 2^18),
+ * and each is scaled as the blockq8 leaf is, then subtracted:
+ *   p_j = fl( fl(fl(fl32(isum_j) * d_a) * fl32(d)) - fl(fl(fl32(msum_j) * d_a) * fl32(dmin)) );
+ * y = bf16 of the canonical tree over the K/32 leaves.
+ */
+
+typedef struct {
+    const int8_t *q;
+    const float *da;
+    const uint8_t *ql, *scm;
+    const uint16_t *dm;
+    int64_t b, N, K;
+    uint16_t *y;
+    int64_t n0, n1;
+    int status;
+} kq4_job;
+
+static void *kq4_worker(void *arg) {
+    kq4_job *j = (kq4_job *)arg;
+    const int64_t K = j->K, m = K / 32;
+    float *leaf = (float *)malloc(sizeof(float) * (size_t)m);
+    if (!leaf) {
+        j->status = ORACLE_ERR_ARGS;
+        return NULL;
+    }
+    for (int64_t n = j->n0; n < j->n1; ++n)
+        for (int64_t t = 0; t < j->b; ++t) {
+            for (int64_t i = 0; i < m; ++i) {
+                const int32_t sc = j->scm[(n * m + i) * 2], mn = j->scm[(n * m + i) * 2 + 1];
+                if (sc > 63 || mn > 63) j->status = ORACLE_ERR_ARGS;
+                int32_t qa = 0, asum = 0;
+                for (int64_t k = 32 * i; k < 32 * i + 32; ++k) {
+                    const int32_t code = (j->ql[n * (K / 2) + k / 2] >> (4 * (k % 2))) & 15;
+                    qa += code * (int32_t)j->q[t * K + k];
+                    asum += (int32_t)j->q[t * K + k];
+                }
+                const int32_t isum = sc * qa, msum = mn * asum;
+                const float da = j->da[t * m + i];
+                const uint16_t d = j->dm[(n * (K / 256) + i / 8) * 2], dmin = j->dm[(n * (K / 256) + i / 8) * 2 + 1];
+                const float a = oracle_f32_mul(oracle_f32_mul(oracle_i32_to_f32(isum), da), oracle_fp16_to_f32(d));
+                const float c = oracle_f32_mul(oracle_f32_mul(oracle_i32_to_f32(msum), da), oracle_fp16_to_f32(dmin));
+                leaf[i] = oracle_f32_sub(a, c);
+            }
+            const float root = oracle_tree_sum(leaf, m);
+            j->y[t * j->N + n] = oracle_bf16_rne(f32_bits(root));
+        }
+    free(leaf);
+    return NULL;
+}
+
+/* q int8 [b, K], d_a fp32 [b, K/32], a kq4 matrix (ql, scm, dm as above)
+ * -> y bf16 [b, N]; K a multiple of 256.  Threads split output rows only.
+ * Sub-scales or minimums above 63 give ORACLE_ERR_ARGS. */
+int oracle_kq4_linear(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8_t *scm, const uint16_t *dm,
+                      int64_t b, int64_t N, int64_t K, uint16_t *y, int nthreads) {
+    if (!q || !d_a || !ql || !scm || !dm || !y || b < 1 || N < 1 || K < 256 || K % 256 != 0) return ORACLE_ERR_ARGS;
+    if (nthreads <= 0) nthreads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > N) nthreads = (int)N;
+    kq4_job jobs[256];
+    pthread_t th[256];
+    int started[256];
+    for (int i = 0; i < nthreads; ++i) {
+        kq4_job jb = {q, d_a, ql, scm, dm, b, N, K, y, N * i / nthreads, N * (i + 1) / nthreads, ORACLE_OK};
+        jobs[i] = jb;
+        started[i] = 0;
+    }
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, kq4_worker, &jobs[i]) == 0)
+            started[i] = 1;
+        else
+            kq4_worker(&jobs[i]);
+    }
+    kq4_worker(&jobs[0]);
+    int status = ORACLE_OK;
+    for (int i = 1; i < nthreads; ++i)
+        if (started[i]) pthread_join(th[i], NULL);
+    for (int i = 0; i < nthreads; ++i)
+        if (jobs[i].status != ORACLE_OK) status = jobs[i].status;
+    return status;
+}

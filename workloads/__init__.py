@@ -31,7 +31,10 @@ Recipes (numpy ``Generator(PCG64(seed))``; draws happen in the order listed):
   * kq6 superblock weights (256 weights per superblock, this library's own
     layout): codes uniform on [-32, 31], int8 sub-scales (one per 16
     weights) uniform on [-127, 127], fp16 superblock scales log-uniform on
-    [1e-6, 1e-4]; the codes are then laid out in the two bit planes.
+    [1e-6, 1e-4]; the codes are then laid out in the two bit planes;
+  * kq4 superblock weights: codes uniform on [0, 15], per 32 weights a
+    sub-scale and a minimum uniform on [0, 63], per superblock fp16 d
+    log-uniform on [1e-5, 1e-3] and dmin log-uniform on [1e-4, 1e-2].
 
 The layer shapes follow Qwen3 models (hidden size, intermediate size and the
 packed qkv / gate_up projections); no model weights are used or needed.
@@ -352,3 +355,50 @@ def kq6_layer(i: int, tokens: int = 16) -> KQ6Layer:
     ql, qh = kq6_pack(codes)
     x = normal_bf16(g, tokens, K)
     return KQ6Layer(name, K, N, codes, ql, qh, sc, d, x)
+
+
+# -- kq4: 4-bit codes with a sub-scale and a minimum per 32 weights --------------------
+#
+# Layout (this library's own): codes q in [0, 15] packed two per byte in weight
+# order (the kq6 low plane); scm [N, K/32, 2] uint8 = (sub-scale, minimum) per 32
+# weights, both in [0, 63]; dm [N, K/256, 2] fp16 = (d, dmin) per superblock.
+
+def kq4_pack(codes: np.ndarray) -> np.ndarray:
+    """codes uint8 [N, K] in [0, 15] -> low plane uint8 [N, K/2]."""
+    assert codes.min() >= 0 and codes.max() <= 15
+    c = codes.astype(np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def kq4_weights(g: np.random.Generator, N: int, K: int):
+    """-> (codes uint8 [N, K], scm uint8 [N, K/32, 2], dm fp16 bits [N, K/256, 2])."""
+    codes = g.integers(0, 16, (N, K), dtype=np.uint8)
+    scm = g.integers(0, 64, (N, K // 32, 2), dtype=np.uint8)
+    d = np.exp(g.uniform(np.log(1e-5), np.log(1e-3), (N, K // 256)))
+    dmin = np.exp(g.uniform(np.log(1e-4), np.log(1e-2), (N, K // 256)))
+    dm = np.stack([d, dmin], axis=-1).astype(np.float32).astype(np.float16).view(np.uint16)
+    return codes, scm, dm
+
+
+@dataclass
+class KQ4Layer:
+    name: str
+    K: int
+    N: int
+    codes: np.ndarray    # uint8 [N, K]
+    ql: np.ndarray       # uint8 [N, K/2]
+    scm: np.ndarray      # uint8 [N, K/32, 2]
+    dm: np.ndarray       # fp16 bits [N, K/256, 2]
+    x: np.ndarray        # bf16 bits [T, K]
+
+
+SEED_KQ4 = 9001
+
+
+def kq4_layer(i: int, tokens: int = 16) -> KQ4Layer:
+    """Qwen3-8B o (4096 -> 4096) or down (12288 -> 4096) projection as kq4 weights."""
+    name, K, N = KQ6_SHAPES[i]
+    g = rng(SEED_KQ4 + i)
+    codes, scm, dm = kq4_weights(g, N, K)
+    x = normal_bf16(g, tokens, K)
+    return KQ4Layer(name, K, N, codes, kq4_pack(codes), scm, dm, x)
