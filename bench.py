@@ -322,6 +322,28 @@ def main():
                 ext.append({"op": "kq6_linear", "K": Lk.K, "N": Lk.N, "b": b, "us": round(us, 2),
                             "weight_GBs": round(by / (us * 1e-6) / 1e9, 1)})
             del planes
+        # kq4 superblocks (4.625 bits per weight) on the same shapes
+        for i in range(len(W.KQ6_SHAPES)):
+            L4 = W.kq4_layer(i, tokens=16)
+            by = L4.N * L4.K * (0.5 + 1 / 16) + L4.N * (L4.K // 256) * 4
+            nc = copies_past_cache(by)
+            planes = [(torch.from_numpy(L4.ql).to(dev), torch.from_numpy(L4.scm).to(dev))]
+            planes += [tuple(p.clone() for p in planes[0]) for _ in range(nc - 1)]
+            dm4 = torch.from_numpy(L4.dm.view(np.int16)).view(torch.float16).to(dev)
+            x4 = torch.from_numpy(L4.x.view(np.int16)).view(torch.bfloat16).to(dev)
+            q4, da4 = iqd.quantize_activations(x4, group=32)
+            for b in (1, 4, 8):
+                y4 = torch.empty((b, L4.N), dtype=torch.bfloat16, device=dev)
+
+                def k4(b=b, y4=y4):
+                    for c in range(nc):
+                        iqd.kq4_linear(q4[:b], da4[:b], planes[c][0], planes[c][1], dm4, y=y4)
+                g = capture(k4)
+                g.replay()
+                us = time_graph(g, 10) * 1e3 / nc
+                ext.append({"op": "kq4_linear", "K": L4.K, "N": L4.N, "b": b, "us": round(us, 2),
+                            "weight_GBs": round(by / (us * 1e-6) / 1e9, 1)})
+            del planes
         Ll = W.lm_head_layer(tokens=8)
         wl = torch.from_numpy(Ll.w).to(dev)
         swl = torch.from_numpy(Ll.s_w).to(dev)

@@ -67,7 +67,8 @@ typedef enum {
 } iqd_status;
 
 /* Operation codes for iqd_workspace_bytes. */
-enum { IQD_OP_W8A8 = 1, IQD_OP_BLOCKQ8 = 2, IQD_OP_LM_HEAD = 3, IQD_OP_W8A8_BF16 = 4, IQD_OP_FP8 = 5, IQD_OP_KQ6 = 6 };
+enum { IQD_OP_W8A8 = 1, IQD_OP_BLOCKQ8 = 2, IQD_OP_LM_HEAD = 3, IQD_OP_W8A8_BF16 = 4, IQD_OP_FP8 = 5, IQD_OP_KQ6 = 6,
+       IQD_OP_KQ4 = 7 };
 
 #define IQD_K_MAX 131071
 #define IQD_SPLIT_K_MAX 64
@@ -205,6 +206,33 @@ int blockq8_linear(const int8_t *q, const float *d_a, const int8_t *w, const voi
 int kq6_linear(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8_t *qh, const int8_t *sc,
                const void *d_fp16, int64_t b, int64_t N, int64_t K, void *y_bf16, int32_t split_k,
                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kq4_linear - linear layer over k-quant-style superblocks of 256 weights
+ * with 4-bit codes and a minimum per 32 weights.
+ *
+ * [P1 opening]: the pages' decode workload is Qwen3-8B at q4_k_m; [P1 "the
+ * mat-vec kernel"]: exact integer sums per activation block of 32, each
+ * scaled into fp32.  Layout (the library's own; 4.625 bits per weight):
+ *   ql  in  uint8 [N, K/2]     code q in [0, 15] of weight k in bits
+ *                              4 (k%2) .. +3 of byte k/2
+ *   scm in  uint8 [N, K/32, 2] (sub-scale sc_j, minimum m_j) per 32 weights,
+ *                              both in [0, 63] (not checked)
+ *   dm  in  fp16  [N, K/256, 2] (d, dmin) per superblock
+ * Weight k of block j stands for d sc_j q_k - dmin m_j.  Per block:
+ *     isum_j = sc_j * sum q[t,k] * code_k,  msum_j = m_j * sum q[t,k]  (exact)
+ *     p_j = fl( fl(fl(fl32(isum_j) * d_a[t,j]) * fl32(d)) - fl(fl(fl32(msum_j) * d_a[t,j]) * fl32(dmin)) )
+ *     y   = bf16(canonical tree over the K/32 leaves)
+ *
+ *   q      in  int8 [b, K]       d_a  in  fp32 [b, K/32]
+ *   y_bf16 out bf16 [b, N]
+ *   split_k    as blockq8_linear.
+ * K must be a multiple of 256.  q and ql 16-byte aligned, scm 2, dm 4.
+ * Errors: as blockq8_linear.
+ */
+int kq4_linear(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8_t *scm, const void *dm_fp16,
+               int64_t b, int64_t N, int64_t K, void *y_bf16, int32_t split_k, void *workspace,
+               size_t workspace_bytes, void *stream);
 
 /*
  * lm_head_argmax - W8A8 vocab projection and the winning token per row.

@@ -29,6 +29,7 @@ IQD_OP_LM_HEAD = 3
 IQD_OP_W8A8_BF16 = 4
 IQD_OP_FP8 = 5
 IQD_OP_KQ6 = 6
+IQD_OP_KQ4 = 7
 
 IQD_K_MAX = 131071
 IQD_SPLIT_K_MAX = 64
@@ -56,6 +57,7 @@ SIGNATURES = {
     "w8a8_linear_bf16": (ctypes.c_int, [P, P, P, I64, I64, I64, P, P, P, P, SZ, P]),
     "blockq8_linear": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]),
     "kq6_linear": (ctypes.c_int, [P, P, P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]),
+    "kq4_linear": (ctypes.c_int, [P, P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]),
     "lm_head_argmax": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, P, SZ, P]),
     "pow2_requantize": (ctypes.c_int, [P, P, I64, I64, P, P, P]),
     "quantize_fp8": (ctypes.c_int, [P, I64, I64, P, P, P]),
@@ -235,6 +237,30 @@ def kq6_linear(q, d_a, ql, qh, sc, d, split_k: int = 1, y=None, workspace=None):
     st = load().kq6_linear(_ptr(q), _ptr(d_a), _ptr(ql), _ptr(qh), _ptr(sc), _ptr(d), b, N, K, _ptr(y), split_k,
                            _ptr(workspace), wsb, _stream_ptr())
     _raise(st, "kq6_linear")
+    return y
+
+
+def kq4_linear(q, d_a, ql, scm, dm, split_k: int = 1, y=None, workspace=None):
+    """q int8 [b, K], d_a fp32 [b, K/32], kq4 weights ql uint8 [N, K/2], scm uint8 [N, K/32, 2]
+    (sub-scale, minimum), dm fp16 [N, K/256, 2] (d, dmin) -> y bf16 [b, N]."""
+    torch = _torch()
+    _check_tensor(q, "q", (torch.int8,))
+    b, K = q.shape
+    N = ql.shape[0]
+    _check_tensor(d_a, "d_a", (torch.float32,), (b, K // 32))
+    _check_tensor(ql, "ql", (torch.uint8,), (N, K // 2))
+    _check_tensor(scm, "scm", (torch.uint8,), (N, K // 32, 2))
+    _check_tensor(dm, "dm", (torch.float16, torch.int16), (N, K // 256, 2))
+    if y is None:
+        y = torch.empty((b, N), dtype=torch.bfloat16, device=q.device)
+    _check_tensor(y, "y", (torch.bfloat16,), (b, N))
+    need = workspace_bytes(IQD_OP_KQ4, b, N, K, split_k)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().kq4_linear(_ptr(q), _ptr(d_a), _ptr(ql), _ptr(scm), _ptr(dm), b, N, K, _ptr(y), split_k,
+                           _ptr(workspace), wsb, _stream_ptr())
+    _raise(st, "kq4_linear")
     return y
 
 

@@ -185,6 +185,7 @@ size_t iqd_workspace_bytes(int op, int64_t b, int64_t N, int64_t K, int32_t spli
             return ws_lm_head(b, N, false);
         case IQD_OP_W8A8_BF16:
             return ws_w8a8_bf16(b, K);
+        case IQD_OP_KQ4:
         case IQD_OP_KQ6:
             if (K % 256 != 0 || blockq8_split_ok(b, K, split_k) != IQD_OK) return 0;
             return split_k > 1 ? round16(static_cast<size_t>(split_k) * b * N * 4) : 0;
@@ -364,6 +365,50 @@ int kq6_linear(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8
     float *part = static_cast<float *>(workspace);
     const int bi = static_cast<int>(b);
     hipError_t e = iqd::launch_kq6_matvec(q, d_a, ql, qh, sc, d, bi, Ni, Ki, nullptr, split_k, part, hs);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(iqd::launch_blockq8_combine(part, bi, Ni, split_k, y, hs));
+}
+
+int kq4_linear(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8_t *scm, const void *dm_fp16,
+               int64_t b, int64_t N, int64_t K, void *y_bf16, int32_t split_k, void *workspace,
+               size_t workspace_bytes, void *stream) {
+    if (!q || !d_a || !ql || !scm || !dm_fp16 || !y_bf16) return IQD_ERR_INVALID;
+    int st = check_shape(b, N, K);
+    if (st != IQD_OK) return st;
+    if (K % 256 != 0) return IQD_ERR_INVALID;
+    st = blockq8_split_ok(b, K, split_k);
+    if (st != IQD_OK) return st;
+    if (!aligned(q, 16) || !aligned(ql, 16) || !aligned(scm, 2) || !aligned(d_a, 4) || !aligned(dm_fp16, 4) ||
+        !aligned(y_bf16, 2))
+        return IQD_ERR_ALIGN;
+    const size_t ws = split_k > 1 ? round16(static_cast<size_t>(split_k) * b * N * 4) : 0;
+    if (ws > 0) {
+        if (!workspace || workspace_bytes < ws) return IQD_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return IQD_ERR_ALIGN;
+    }
+    const size_t m = static_cast<size_t>(K / 32), nk = static_cast<size_t>(N) * K;
+    if (any_overlap({{y_bf16, static_cast<size_t>(b) * N * 2}, {ws ? workspace : nullptr, ws}},
+                    {{q, static_cast<size_t>(b * K)}, {d_a, static_cast<size_t>(b) * m * 4}, {ql, nk / 2},
+                     {scm, nk / 16}, {dm_fp16, nk / 256 * 4}}))
+        return IQD_ERR_INVALID;
+    clear_stale_error();
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    uint16_t *y = static_cast<uint16_t *>(y_bf16);
+    const uint16_t *dm = static_cast<const uint16_t *>(dm_fp16);
+    const int Ni = static_cast<int>(N), Ki = static_cast<int>(K);
+    if (split_k == 1) {
+        // any b: chunks of at most 16 tokens (each token's row is independent of its chunk)
+        for (int64_t t0 = 0; t0 < b; t0 += kMatvecMaxB) {
+            const int bc = static_cast<int>(b - t0 < kMatvecMaxB ? b - t0 : kMatvecMaxB);
+            hipError_t e = iqd::launch_kq4_matvec(q + t0 * K, d_a + t0 * m, ql, scm, dm, bc, Ni, Ki, y + t0 * N, 1,
+                                                  nullptr, hs);
+            if (e != hipSuccess) return hip_status(e);
+        }
+        return IQD_OK;
+    }
+    float *part = static_cast<float *>(workspace);
+    const int bi = static_cast<int>(b);
+    hipError_t e = iqd::launch_kq4_matvec(q, d_a, ql, scm, dm, bi, Ni, Ki, nullptr, split_k, part, hs);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(iqd::launch_blockq8_combine(part, bi, Ni, split_k, y, hs));
 }

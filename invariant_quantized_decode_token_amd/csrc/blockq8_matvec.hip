@@ -52,10 +52,11 @@ struct BqArgs {
     const int8_t *q;
     const float *d_a;
     const int8_t *w;       // q8_0: int8 weights [N, K]
-    const uint16_t *d_w;   // q8_0: fp16 [N, K/32]; kq6: superblock scales fp16 [N, K/256]
+    const uint16_t *d_w;   // q8_0: fp16 [N, K/32]; kq6: superblock scales fp16 [N, K/256];
+                           // kq4: (d, dmin) fp16 pairs [N, K/256, 2]
     const uint8_t *ql;     // kq6: low plane [N, K/2]
     const uint8_t *qh;     // kq6: high plane [N, K/4]
-    const int8_t *sc;      // kq6: sub-scales [N, K/16]
+    const int8_t *sc;      // kq6: sub-scales [N, K/16]; kq4: (sub-scale, minimum) byte pairs [N, K/32, 2]
     int N, K, m, L;
     uint16_t *y;
     float *part;  // [split, B, N] subtree roots when split > 1
@@ -107,6 +108,21 @@ __device__ __forceinline__ v4i kq6_codes(uint32_t lo0, uint32_t lo1, uint32_t hi
     return c;
 }
 
+// kq4: the 16 codes (0..15) of half a block from its 8 bytes of the low
+// plane, one per byte (the nibble spread of kq6_codes).
+__device__ __forceinline__ v4i kq4_codes(uint32_t lo0, uint32_t lo1) {
+    v4i c;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t v = ((w < 2 ? lo0 : lo1) >> (16 * (w & 1))) & 0xFFFFu;
+        const uint32_t t = (v | (v << 8)) & 0x00FF00FFu;
+        c[w] = static_cast<int32_t>((t | (t << 4)) & 0x0F0F0F0Fu);
+    }
+    return c;
+}
+
+constexpr int kFmtQ8 = 0, kFmtKq6 = 1, kFmtKq4 = 2;  // weight formats of k_blockq8_matvec
+
 struct AddI {
     __device__ int32_t operator()(int32_t a, int32_t b) const { return a + b; }
 };
@@ -114,13 +130,15 @@ struct AddF {
     __device__ float operator()(float a, float b) const { return a + b; }
 };
 
-// KQ: the weights are kq6 superblocks (two bit planes, a sub-scale per 16
-// weights, an fp16 scale per 256) instead of q8_0 blocks.  The lane's 16
-// weights are then one sub-block; its integer dot is multiplied by the
-// sub-scale before the lane pair adds its halves, so the pair forms
-// isum_j = sum of (sc * c) * q over the block, and the block's weight scale is
-// its superblock's.
-template <int B, int RS, int U, bool KQ>
+// FMT: the weight format.  q8_0 blocks; kq6 superblocks (two bit planes, a
+// sub-scale per 16 weights, an fp16 scale per 256): the lane's 16 weights are
+// one sub-block, whose integer dot is multiplied by its sub-scale before the
+// lane pair adds its halves, so the pair forms isum_j = sum of (sc * c) * q
+// over the block, and the block's weight scale is its superblock's; kq4
+// superblocks (4-bit codes, a sub-scale and a minimum per block, d and dmin per
+// 256): the pair forms isum_j = sc * sum q * a and msum_j = m * sum a, and the
+// leaf is fl(fl(fl(fl32(isum_j) * d_a) * d) - fl(fl(fl32(msum_j) * d_a) * dmin)).
+template <int B, int RS, int U, int FMT>
 __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
     __shared__ float red[kBqWaves][kWave];
     const int lane = lane_id();
@@ -152,14 +170,16 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
         const int rfirst = min(row0, N - 1);
         const int rlast = min(row0 + RS - 1, N - 1);
         const int nrows = rlast - rfirst + 1;
-        const int dstride = KQ ? K / 256 : m;  // weight scales per row
+        constexpr bool KQ = FMT != kFmtQ8;
+        const int dstride = FMT == kFmtQ8 ? m : FMT == kFmtKq6 ? K / 256 : 2 * (K / 256);  // fp16 scales per row
         const __amdgpu_buffer_rsrc_t wr =
             KQ ? buf_rsrc(a.ql + static_cast<int64_t>(rfirst) * (K / 2), static_cast<int64_t>(nrows) * (K / 2))
                : buf_rsrc(a.w + static_cast<int64_t>(rfirst) * K, static_cast<int64_t>(nrows) * K);
-        const __amdgpu_buffer_rsrc_t hr =
-            buf_rsrc(KQ ? a.qh + static_cast<int64_t>(rfirst) * (K / 4) : nullptr, KQ ? static_cast<int64_t>(nrows) * (K / 4) : 0);
-        const __amdgpu_buffer_rsrc_t scr =
-            buf_rsrc(KQ ? a.sc + static_cast<int64_t>(rfirst) * (K / 16) : nullptr, KQ ? static_cast<int64_t>(nrows) * (K / 16) : 0);
+        const __amdgpu_buffer_rsrc_t hr = buf_rsrc(FMT == kFmtKq6 ? a.qh + static_cast<int64_t>(rfirst) * (K / 4) : nullptr,
+                                                   FMT == kFmtKq6 ? static_cast<int64_t>(nrows) * (K / 4) : 0);
+        // kq6 sub-scales and kq4 (sub-scale, minimum) pairs are both K/16 bytes per row
+        const __amdgpu_buffer_rsrc_t scr = buf_rsrc(KQ ? a.sc + static_cast<int64_t>(rfirst) * (K / 16) : nullptr,
+                                                    KQ ? static_cast<int64_t>(nrows) * (K / 16) : 0);
         const __amdgpu_buffer_rsrc_t dwr =
             buf_rsrc(a.d_w + static_cast<int64_t>(rfirst) * dstride, static_cast<int64_t>(nrows) * dstride * 2);
         int roff[RS];
@@ -183,7 +203,19 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
                 const int kb = j * 32 + 16 * half;
 #pragma unroll
                 for (int r = 0; r < RS; ++r) {
-                    if constexpr (KQ) {
+                    if constexpr (FMT == kFmtKq4) {
+                        // weights kb .. kb + 15: 8 bytes of the low plane; the block's
+                        // (sub-scale, minimum) pair and the superblock's (d, dmin) pair
+                        const auto lo = __builtin_amdgcn_raw_buffer_load_b64(
+                            wr, live ? roff[r] * (K / 2) + kb / 2 : kBqOob, 0, 2);
+                        wv[u][r][0] = static_cast<int32_t>(lo[0]);
+                        wv[u][r][1] = static_cast<int32_t>(lo[1]);
+                        wv[u][r][2] = 0;
+                        wv[u][r][3] = 0;
+                        scb[u][r] = __builtin_amdgcn_raw_buffer_load_b16(scr, live ? roff[r] * (K / 16) + 2 * j : kBqOob, 0, 0);
+                        dwb[u][r] =
+                            __builtin_amdgcn_raw_buffer_load_b32(dwr, live ? 2 * (roff[r] * dstride + 2 * (j >> 3)) : kBqOob, 0, 0);
+                    } else if constexpr (FMT == kFmtKq6) {
                         // weights kb .. kb + 15: 8 bytes of the low plane, 4 of the high
                         const auto lo = __builtin_amdgcn_raw_buffer_load_b64(
                             wr, live ? roff[r] * (K / 2) + kb / 2 : kBqOob, 0, 2);
@@ -217,10 +249,27 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
                 const bool live = j < m;  // blocks in [m, L) are +0 leaves, beyond L -0 (a slot of padding gives +0)
                 float cr = 0.0f;          // a slot made only of padding leaves
                 if (slot * 32 < m) {      // uniform
-                    int32_t isum[NP];
+                    int32_t isum[NP], msum[FMT == kFmtKq4 ? NP : 1];
 #pragma unroll
                     for (int v = 0; v < NP; ++v) isum[v] = 0;
-                    if constexpr (KQ) {
+                    if constexpr (FMT == kFmtKq4) {
+#pragma unroll
+                        for (int v = 0; v < NP; ++v) msum[v] = 0;
+                        int32_t asum[B];  // the half block's activation sum per token
+#pragma unroll
+                        for (int t = 0; t < B; ++t) asum[t] = dot16(v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101}, av[u][t], 0);
+#pragma unroll
+                        for (int r = 0; r < RS; ++r) {
+                            const v4i c = kq4_codes(static_cast<uint32_t>(wv[u][r][0]), static_cast<uint32_t>(wv[u][r][1]));
+                            const int32_t scv = static_cast<int32_t>(scb[u][r] & 0xFFu);
+                            const int32_t mnv = static_cast<int32_t>((scb[u][r] >> 8) & 0xFFu);
+#pragma unroll
+                            for (int t = 0; t < B; ++t) {
+                                isum[r * B + t] = dot16(c, av[u][t], 0) * scv;
+                                msum[r * B + t] = asum[t] * mnv;
+                            }
+                        }
+                    } else if constexpr (FMT == kFmtKq6) {
 #pragma unroll
                         for (int r = 0; r < RS; ++r) {
                             const v4i c = kq6_codes(static_cast<uint32_t>(wv[u][r][0]), static_cast<uint32_t>(wv[u][r][1]),
@@ -235,13 +284,17 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
 #pragma unroll
                             for (int r = 0; r < RS; ++r) isum[r * B + t] = dot16(wv[u][r], av[u][t], isum[r * B + t]);
                     }
-                    float dwv[RS];
+                    float dwv[RS], dmv[RS];  // the block's weight scale (kq4: d) and kq4's dmin
 #pragma unroll
-                    for (int r = 0; r < RS; ++r) dwv[r] = fp16_to_f32(static_cast<uint16_t>(dwb[u][r]));
+                    for (int r = 0; r < RS; ++r) {
+                        dwv[r] = fp16_to_f32(static_cast<uint16_t>(dwb[u][r] & 0xFFFFu));
+                        dmv[r] = fp16_to_f32(static_cast<uint16_t>(dwb[u][r] >> 16));
+                    }
                     // tree level 0 -> block sums: integer reduce-scatter over the lane pair
                     float leaf[NPH];
                     if constexpr (NP >= 2) {
                         rs_step<1, NP>(isum, lane, AddI());
+                        if constexpr (FMT == kFmtKq4) rs_step<1, NP>(msum, lane, AddI());
 #pragma unroll
                         for (int v = 0; v < NPH; ++v) {
                             const int vlo = v, vhi = v + NPH;
@@ -251,12 +304,21 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
                             const float dw_hi = vhi < NV ? dwv[vhi / B] : 0.0f;
                             const float da = sel(half != 0, da_hi, da_lo);
                             const float dw = sel(half != 0, dw_hi, dw_lo);
-                            const float p = (static_cast<float>(isum[v]) * da) * dw;
+                            float p = (static_cast<float>(isum[v]) * da) * dw;
+                            if constexpr (FMT == kFmtKq4) {
+                                const float dm_lo = vlo < NV ? dmv[vlo / B] : 0.0f;
+                                const float dm_hi = vhi < NV ? dmv[vhi / B] : 0.0f;
+                                p = p - (static_cast<float>(msum[v]) * da) * sel(half != 0, dm_hi, dm_lo);
+                            }
                             leaf[v] = live ? p : (j < L ? 0.0f : -0.0f);
                         }
                     } else {
                         const int32_t tot = isum[0] + xor_lane<1>(isum[0]);
-                        const float p = (static_cast<float>(tot) * dav[u][0]) * dwv[0];
+                        float p = (static_cast<float>(tot) * dav[u][0]) * dwv[0];
+                        if constexpr (FMT == kFmtKq4) {
+                            const int32_t mt = msum[0] + xor_lane<1>(msum[0]);
+                            p = p - (static_cast<float>(mt) * dav[u][0]) * dmv[0];
+                        }
                         leaf[0] = live ? p : (j < L ? 0.0f : -0.0f);
                     }
                     // tree levels 1..5 inside the chunk: lane masks 2..32
@@ -306,16 +368,16 @@ __global__ __launch_bounds__(256) void k_blockq8_combine(const float *__restrict
     y[i] = bf16_rne(root);
 }
 
-template <int B, int RS, int U, bool KQ>
+template <int B, int RS, int U, int FMT>
 hipError_t launch_rs(const BqArgs &a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((k_blockq8_matvec<B, RS, U, KQ>), dim3(grid, a.split), dim3(kBqThreads), 0, st, a);
+    hipLaunchKernelGGL((k_blockq8_matvec<B, RS, U, FMT>), dim3(grid, a.split), dim3(kBqThreads), 0, st, a);
     return hipGetLastError();
 }
 
 // Four rows per wave: each activation load serves four weight rows (measured
 // on MI355X at 4096 -> 4096 and 12288 -> 4096 against 1, 2 and 8 rows).  At
 // b = 1 a wave with at least four slots keeps two slots of loads in flight.
-template <int B, bool KQ>
+template <int B, int FMT>
 hipError_t launch_b(const BqArgs &base, hipStream_t st) {
     constexpr int RS = 4;
     BqArgs a = base;
@@ -330,30 +392,30 @@ hipError_t launch_b(const BqArgs &base, hipStream_t st) {
     int grid = device_info().cus * 8;
     if (grid > a.nsteps) grid = a.nsteps;
     if constexpr (B == 1) {
-        if (nss / ks >= 4) return launch_rs<B, RS, 2, KQ>(a, grid, st);
+        if (nss / ks >= 4) return launch_rs<B, RS, 2, FMT>(a, grid, st);
     }
-    return launch_rs<B, RS, 1, KQ>(a, grid, st);
+    return launch_rs<B, RS, 1, FMT>(a, grid, st);
 }
 
-template <bool KQ>
+template <int FMT>
 hipError_t launch_any_b(const BqArgs &a, int b, hipStream_t st) {
     switch (b) {
-        case 1: return launch_b<1, KQ>(a, st);
-        case 2: return launch_b<2, KQ>(a, st);
-        case 3: return launch_b<3, KQ>(a, st);
-        case 4: return launch_b<4, KQ>(a, st);
-        case 5: return launch_b<5, KQ>(a, st);
-        case 6: return launch_b<6, KQ>(a, st);
-        case 7: return launch_b<7, KQ>(a, st);
-        case 8: return launch_b<8, KQ>(a, st);
-        case 9: return launch_b<9, KQ>(a, st);
-        case 10: return launch_b<10, KQ>(a, st);
-        case 11: return launch_b<11, KQ>(a, st);
-        case 12: return launch_b<12, KQ>(a, st);
-        case 13: return launch_b<13, KQ>(a, st);
-        case 14: return launch_b<14, KQ>(a, st);
-        case 15: return launch_b<15, KQ>(a, st);
-        case 16: return launch_b<16, KQ>(a, st);
+        case 1: return launch_b<1, FMT>(a, st);
+        case 2: return launch_b<2, FMT>(a, st);
+        case 3: return launch_b<3, FMT>(a, st);
+        case 4: return launch_b<4, FMT>(a, st);
+        case 5: return launch_b<5, FMT>(a, st);
+        case 6: return launch_b<6, FMT>(a, st);
+        case 7: return launch_b<7, FMT>(a, st);
+        case 8: return launch_b<8, FMT>(a, st);
+        case 9: return launch_b<9, FMT>(a, st);
+        case 10: return launch_b<10, FMT>(a, st);
+        case 11: return launch_b<11, FMT>(a, st);
+        case 12: return launch_b<12, FMT>(a, st);
+        case 13: return launch_b<13, FMT>(a, st);
+        case 14: return launch_b<14, FMT>(a, st);
+        case 15: return launch_b<15, FMT>(a, st);
+        case 16: return launch_b<16, FMT>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -391,7 +453,7 @@ hipError_t launch_blockq8_matvec(const int8_t *q, const float *d_a, const int8_t
     a.d_a = d_a;
     a.w = w;
     a.d_w = d_w;
-    return launch_any_b<false>(a, b, st);
+    return launch_any_b<kFmtQ8>(a, b, st);
 }
 
 hipError_t launch_kq6_matvec(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8_t *qh, const int8_t *sc,
@@ -404,7 +466,18 @@ hipError_t launch_kq6_matvec(const int8_t *q, const float *d_a, const uint8_t *q
     a.qh = qh;
     a.sc = sc;
     a.d_w = d;
-    return launch_any_b<true>(a, b, st);
+    return launch_any_b<kFmtKq6>(a, b, st);
+}
+
+hipError_t launch_kq4_matvec(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8_t *scm, const uint16_t *dm,
+                             int b, int N, int K, uint16_t *y, int split, float *part, hipStream_t st) {
+    BqArgs a = bq_args(N, K, y, split, part);
+    a.q = q;
+    a.d_a = d_a;
+    a.ql = ql;
+    a.sc = reinterpret_cast<const int8_t *>(scm);
+    a.d_w = dm;
+    return launch_any_b<kFmtKq4>(a, b, st);
 }
 
 hipError_t launch_blockq8_combine(const float *part, int b, int N, int split, uint16_t *y,

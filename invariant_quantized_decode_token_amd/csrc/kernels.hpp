@@ -62,6 +62,10 @@ hipError_t launch_blockq8_combine(const float *part, int b, int N, int split, ui
 hipError_t launch_kq6_matvec(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8_t *qh, const int8_t *sc,
                              const uint16_t *d, int b, int N, int K, uint16_t *y, int split, float *part,
                              hipStream_t st);
+// And over kq4 superblocks: scm holds (sub-scale, minimum) byte pairs per 32
+// weights, dm (d, dmin) fp16 pairs per 256.
+hipError_t launch_kq4_matvec(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8_t *scm, const uint16_t *dm,
+                             int b, int N, int K, uint16_t *y, int split, float *part, hipStream_t st);
 
 // Argmax over bf16 logits [b, N]: smallest index of the row maximum.  part is
 // scratch for argmax_chunks(N) 64-bit keys per row.

@@ -19,7 +19,8 @@ def test_exports_every_declared_function(lib):
     names = iqd.header_functions()
     assert set(names) == {"quantize_activations", "w8a8_linear", "w8a8_linear_bf16", "blockq8_linear", "lm_head_argmax",
                           "pow2_requantize", "iqd_workspace_bytes", "iqd_status_str", "iqd_last_hip_error",
-                          "attn_decode", "attn_workspace_bytes", "quantize_fp8", "fp8_linear", "kq6_linear"}
+                          "attn_decode", "attn_workspace_bytes", "quantize_fp8", "fp8_linear", "kq6_linear",
+                          "kq4_linear"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -105,6 +106,20 @@ def test_kq6_validation(lib):
     assert call(ql=0) == L.IQD_ERR_INVALID
     assert iqd.workspace_bytes(L.IQD_OP_KQ6, 8, 4096, 12288, 16) == 16 * 8 * 4096 * 4
     assert iqd.workspace_bytes(L.IQD_OP_KQ6, 8, 4096, 1000, 1) == 0  # K % 256
+
+
+def test_kq4_validation(lib):
+    def call(b=4, N=64, K=1024, split=1, q=A, ql=3 * A, scm=4 * A, dm=6 * A, y=5 * A, ws=0, wsb=0):
+        return lib.kq4_linear(ptr(q), ptr(2 * A), ptr(ql), ptr(scm), ptr(dm), b, N, K, ptr(y), split, ptr(ws), wsb,
+                              None)
+    assert call(K=512 + 32) == L.IQD_ERR_INVALID             # K % 256
+    assert call(split=2) == L.IQD_ERR_UNSUPPORTED            # L = 32 leaves -> one split only
+    assert call(K=4096, split=4) == L.IQD_ERR_WORKSPACE
+    assert call(scm=4 * A + 1) == L.IQD_ERR_ALIGN
+    assert call(dm=6 * A + 2) == L.IQD_ERR_ALIGN
+    assert call(y=4 * A + 64) == L.IQD_ERR_INVALID           # output overlaps the (sub-scale, minimum) pairs
+    assert call(scm=0) == L.IQD_ERR_INVALID
+    assert iqd.workspace_bytes(L.IQD_OP_KQ4, 8, 4096, 12288, 16) == 16 * 8 * 4096 * 4
 
 
 def test_quantize_validation(lib):

@@ -1,7 +1,7 @@
 """Graph capture: the entry points a serving loop captures (quantize + linear
 in one call, the linear with split-K, block-quantized split-K, the LM-head
 argmax, decode attention with the chunk merge, FP8 with split-K, kq6
-superblocks with split-K) recorded in
+and kq4 superblocks with split-K) recorded in
 one HIP graph and replayed three times with eager work in between; every
 replay must equal the eager results bit for bit (no workspace state may leak
 from one replay into the next)."""
@@ -38,6 +38,9 @@ def test_graph_replays_equal_eager(iqd):
     Lk = W.kq6_layer(0, tokens=8)
     qlk, qhk, sck, dk = dev(Lk.ql), dev(Lk.qh), dev(Lk.sc), dev(Lk.d, "fp16")
     qk, dak = iqd.quantize_activations(dev(Lk.x), group=32)
+    L4 = W.kq4_layer(0, tokens=8)
+    ql4, scm4, dm4 = dev(L4.ql), dev(L4.scm), dev(L4.dm, "fp16")
+    q4, da4 = iqd.quantize_activations(dev(L4.x), group=32)
     Lf = W.fp8_layer(0, tokens=8)
     wf, swf = dev(Lf.w), dev(Lf.s_w)
     xf = dev(Lf.x)
@@ -56,6 +59,7 @@ def test_graph_replays_equal_eager(iqd):
         "attn": t.empty_like(qa),
         "fp8": t.empty((8, Lf.N), dtype=t.bfloat16, device="cuda"),
         "kq6": t.empty((8, Lk.N), dtype=t.bfloat16, device="cuda"),
+        "kq4": t.empty((8, L4.N), dtype=t.bfloat16, device="cuda"),
     }
     ws = {
         "split": t.zeros((iqd.workspace_bytes(iqd.IQD_OP_W8A8, 5, L.N, L.K, 4),), dtype=t.uint8, device="cuda"),
@@ -64,6 +68,7 @@ def test_graph_replays_equal_eager(iqd):
         "attn": t.zeros((iqd.attn_workspace_bytes(4, 32, 8, 128, att.pos0),), dtype=t.uint8, device="cuda"),
         "fp8": t.zeros((iqd.workspace_bytes(iqd.IQD_OP_FP8, 8, Lf.N, Lf.K, 2),), dtype=t.uint8, device="cuda"),
         "kq6": t.zeros((iqd.workspace_bytes(iqd.IQD_OP_KQ6, 8, Lk.N, Lk.K, 4),), dtype=t.uint8, device="cuda"),
+        "kq4": t.zeros((iqd.workspace_bytes(iqd.IQD_OP_KQ4, 8, L4.N, L4.K, 2),), dtype=t.uint8, device="cuda"),
         "bf16": t.zeros((iqd.workspace_bytes(iqd.IQD_OP_W8A8_BF16, 8, L.N, L.K, 1) + 16,), dtype=t.uint8,
                         device="cuda"),
     }
@@ -77,6 +82,7 @@ def test_graph_replays_equal_eager(iqd):
         iqd.attn_decode(qa, ka, va, att.pos0, float(att.scale), out=outs["attn"], workspace=ws["attn"])
         iqd.fp8_linear(qf, sf, wf, swf, split_k=2, y=outs["fp8"], workspace=ws["fp8"])
         iqd.kq6_linear(qk, dak, qlk, qhk, sck, dk, split_k=4, y=outs["kq6"], workspace=ws["kq6"])
+        iqd.kq4_linear(q4, da4, ql4, scm4, dm4, split_k=2, y=outs["kq4"], workspace=ws["kq4"])
 
     def snapshot():
         t.cuda.synchronize()
