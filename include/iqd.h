@@ -182,12 +182,14 @@ int blockq8_linear(const int8_t *q, const float *d_a, const int8_t *w, const voi
  * [P1 "the mat-vec kernel"]: a q6_k row is read as weight blocks of 256
  * against int8 activations in blocks of 32; each block's exact integer
  * result is scaled into fp32.  The pages give no bit layout; this one is the
- * library's own (6.5625 bits per weight, the same as q6_k's), packed in
- * weight order so that 16 consecutive weights are 8 + 4 contiguous bytes:
- *   weight k of a row has a code c in [-32, 31] kept as u = c + 32, a
- *   sub-scale sc[k / 16] and the scale d[k / 256] of its superblock;
- *   ql  in  uint8 [N, K/2]:  u & 15 of weight k in bits 4 (k%2) .. +3 of byte k/2
- *   qh  in  uint8 [N, K/4]:  u >> 4 of weight k in bits 2 (k%4) .. +1 of byte k/4
+ * library's own (6.5625 bits per weight, the same as q6_k's): each group of
+ * 16 weights is 8 + 4 contiguous bytes, arranged so that one shift and one
+ * mask per plane give the codes of 4 consecutive weights:
+ *   weight k = 16 g + i of a row has a code c in [-32, 31] kept as
+ *   u = c + 32, a sub-scale sc[k / 16] and the scale d[k / 256] of its
+ *   superblock;
+ *   ql  in  uint8 [N, K/2]:  u & 15 of weight k in bits 4 (i/8) .. +3 of byte 8 g + i%8
+ *   qh  in  uint8 [N, K/4]:  u >> 4 of weight k in bits 2 (i/4) .. +1 of byte 4 g + i%4
  *   sc  in  int8  [N, K/16]  sub-scales, one per 16 weights
  *   d_fp16 in fp16 [N, K/256] superblock scales
  * The result is the blockq8_linear tree with integer weights sc * c and the
@@ -214,8 +216,8 @@ int kq6_linear(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8
  * [P1 opening]: the pages' decode workload is Qwen3-8B at q4_k_m; [P1 "the
  * mat-vec kernel"]: exact integer sums per activation block of 32, each
  * scaled into fp32.  Layout (the library's own; 4.625 bits per weight):
- *   ql  in  uint8 [N, K/2]     code q in [0, 15] of weight k in bits
- *                              4 (k%2) .. +3 of byte k/2
+ *   ql  in  uint8 [N, K/2]     code q in [0, 15] of weight k = 16 g + i in
+ *                              bits 4 (i/8) .. +3 of byte 8 g + i%8
  *   scm in  uint8 [N, K/32, 2] (sub-scale sc_j, minimum m_j) per 32 weights,
  *                              both in [0, 63] (not checked)
  *   dm  in  fp16  [N, K/256, 2] (d, dmin) per superblock

@@ -85,39 +85,32 @@ __device__ __forceinline__ float carry_insert(float (&stk)[kMaxLevels], int i, f
     return v;
 }
 
-// kq6: the 16 codes of one sub-block from its 8 bytes of the low plane (lo0,
-// lo1: nibble i is weight i) and 4 bytes of the high plane (hi: 2-bit field i
-// is weight i).  Output word w holds weights 4w .. 4w+3, one per byte:
-// nibbles spread to bytes by two shift-or-mask steps, 2-bit fields likewise,
-// u = lo | hi << 4 in [0, 63], and the int8 code u - 32 for four bytes at
-// once: (u | 0x80) - 0x20 = u + 0x60 borrows nothing from the next byte, and
-// flipping bit 7 back gives u - 32 in two's complement.
+// kq6: the 16 codes of one group of 16 weights from its 8 bytes of the low
+// plane (lo0, lo1) and 4 bytes of the high plane (hi).  The planes hold weight
+// i of the group at byte i % 8, nibble i / 8, and at byte i % 4, bit pair
+// i / 4, so output word w (weights 4w .. 4w+3, one per byte) takes one shift
+// and one mask per plane; u = lo | hi << 4 in [0, 63], and the int8 code
+// u - 32 for four bytes at once: (u | 0x80) - 0x20 = u + 0x60 borrows nothing
+// from the next byte, and flipping bit 7 back gives u - 32 in two's
+// complement.
 __device__ __forceinline__ v4i kq6_codes(uint32_t lo0, uint32_t lo1, uint32_t hi) {
     v4i c;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        const uint32_t v = ((w < 2 ? lo0 : lo1) >> (16 * (w & 1))) & 0xFFFFu;
-        const uint32_t t = (v | (v << 8)) & 0x00FF00FFu;
-        const uint32_t l = (t | (t << 4)) & 0x0F0F0F0Fu;
-        const uint32_t hb = (hi >> (8 * w)) & 0xFFu;
-        const uint32_t s = (hb | (hb << 12)) & 0x000F000Fu;
-        const uint32_t h = (s | (s << 6)) & 0x03030303u;
+        const uint32_t l = ((w & 1 ? lo1 : lo0) >> (4 * (w >> 1))) & 0x0F0F0F0Fu;
+        const uint32_t h = (hi >> (2 * w)) & 0x03030303u;
         const uint32_t u = l | (h << 4);
         c[w] = static_cast<int32_t>(((u | 0x80808080u) - 0x20202020u) ^ 0x80808080u);
     }
     return c;
 }
 
-// kq4: the 16 codes (0..15) of half a block from its 8 bytes of the low
-// plane, one per byte (the nibble spread of kq6_codes).
+// kq4: the 16 codes (0..15) of a group of 16 weights from its 8 bytes of the
+// low plane, laid out as kq6's.
 __device__ __forceinline__ v4i kq4_codes(uint32_t lo0, uint32_t lo1) {
     v4i c;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint32_t v = ((w < 2 ? lo0 : lo1) >> (16 * (w & 1))) & 0xFFFFu;
-        const uint32_t t = (v | (v << 8)) & 0x00FF00FFu;
-        c[w] = static_cast<int32_t>((t | (t << 4)) & 0x0F0F0F0Fu);
-    }
+    for (int w = 0; w < 4; ++w) c[w] = static_cast<int32_t>(((w & 1 ? lo1 : lo0) >> (4 * (w >> 1))) & 0x0F0F0F0Fu);
     return c;
 }
 

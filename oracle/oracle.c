@@ -814,10 +814,11 @@ int oracle_fp8_linear(const uint8_t *q, const float *s_a, const uint8_t *w, cons
  * library's own (not GGUF's), with the same 6.5625 bits per weight:
  *   - a superblock is 256 consecutive weights of a row, s = k / 256;
  *   - each weight is a code c in [-32, 31] stored as u = c + 32 in [0, 63];
+ *   - weights go in groups of 16, g = k / 16, i = k % 16;
  *   - low plane  ql uint8 [N, K/2]: the low 4 bits of u for weight k are
- *     bits 4*(k%2) .. 4*(k%2)+3 of byte k/2;
+ *     bits 4*(i/8) .. +3 of byte 8*g + i%8;
  *   - high plane qh uint8 [N, K/4]: the top 2 bits of u for weight k are
- *     bits 2*(k%4), 2*(k%4)+1 of byte k/4;
+ *     bits 2*(i/4), +1 of byte 4*g + i%4;
  *   - sub-scales sc int8 [N, K/16], one per 16 weights;
  *   - superblock scale d fp16 [N, K/256].
  * Reading (the pages name only the block scaling): a weight's integer value is
@@ -833,8 +834,9 @@ int oracle_kq6_decode(const uint8_t *ql, const uint8_t *qh, int64_t N, int64_t K
     if (!ql || !qh || !codes || N < 1 || K < 256 || K % 256 != 0) return ORACLE_ERR_ARGS;
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k) {
-            const int lo = (ql[n * (K / 2) + k / 2] >> (4 * (k % 2))) & 15;
-            const int hi = (qh[n * (K / 4) + k / 4] >> (2 * (k % 4))) & 3;
+            const int64_t g = k / 16, i = k % 16;
+            const int lo = (ql[n * (K / 2) + 8 * g + i % 8] >> (4 * (i / 8))) & 15;
+            const int hi = (qh[n * (K / 4) + 4 * g + i % 4] >> (2 * (i / 4))) & 3;
             codes[n * K + k] = (int8_t)((lo | (hi << 4)) - 32);
         }
     return ORACLE_OK;
@@ -930,7 +932,7 @@ int oracle_kq6_linear(const int8_t *q, const float *d_a, const uint8_t *ql, cons
  * of 32.  The 4-bit form subtracts a per-sub-block minimum.  Layout (this
  * library's own):
  *   - weight k has a code q in [0, 15]; low plane ql uint8 [N, K/2] as kq6:
- *     q of weight k in bits 4*(k%2) .. +3 of byte k/2;
+ *     q of weight k = 16 g + i in bits 4*(i/8) .. +3 of byte 8 g + i%8;
  *   - per 32 weights (one activation block) j: a sub-scale sc_j and a minimum
  *     m_j, both in [0, 63], as the byte pair scm[n, j] = (sc_j, m_j),
  *     uint8 [N, K/32, 2];
@@ -970,7 +972,7 @@ static void *kq4_worker(void *arg) {
                 if (sc > 63 || mn > 63) j->status = ORACLE_ERR_ARGS;
                 int32_t qa = 0, asum = 0;
                 for (int64_t k = 32 * i; k < 32 * i + 32; ++k) {
-                    const int32_t code = (j->ql[n * (K / 2) + k / 2] >> (4 * (k % 2))) & 15;
+                    const int32_t code = (j->ql[n * (K / 2) + 8 * (k / 16) + (k % 16) % 8] >> (4 * ((k % 16) / 8))) & 15;
                     qa += code * (int32_t)j->q[t * K + k];
                     asum += (int32_t)j->q[t * K + k];
                 }

@@ -28,11 +28,11 @@ def planes(codes):
 
 def test_planes_match_bytes_worked_by_hand():
     """All codes 0 (u = 32 = 0b10_0000): every low byte 0x00, every high byte
-    0b10101010.  Then weight 131 set to 31 (u = 63 = 0b11_1111): low byte
-    131 / 2 = 65 gets 0xF in its upper nibble (131 is odd); high byte
-    131 / 4 = 32 gets 0b11 in bits 6-7 (131 % 4 = 3).  Weight 256 + 5 = 261
-    set to -32 (u = 0): low byte 130 keeps 0x00, high byte 65 gets 0b00 in
-    bits 2-3 (261 % 4 = 1)."""
+    0b10101010.  Weight 131 = 16 * 8 + 3 set to 31 (u = 63 = 0b11_1111): low
+    byte 8 * 8 + 3 = 67 gets 0xF in its lower nibble (3 < 8); high byte
+    4 * 8 + 3 = 35 gets 0b11 in bits 0-1 (3 / 4 = 0).  Weight 261 = 16 * 16 +
+    5 set to -32 (u = 0): low byte 128 + 5 keeps 0x00, high byte 64 + 1 = 65
+    gets 0b00 in bits 2-3 (5 / 4 = 1)."""
     c = np.zeros((1, 512), np.int8)
     ql, qh = planes(c)
     assert (ql == 0x00).all() and (qh == 0xAA).all()
@@ -40,9 +40,9 @@ def test_planes_match_bytes_worked_by_hand():
     c[0, 261] = -32
     ql, qh = planes(c)
     want_ql = np.zeros(256, np.uint8)
-    want_ql[65] = 0xF0
+    want_ql[67] = 0x0F
     want_qh = np.full(128, 0xAA, np.uint8)
-    want_qh[32] = 0xEA                     # 0b11_10_10_10
+    want_qh[35] = 0xAB                     # 0b10_10_10_11
     want_qh[65] = 0xA2                     # 0b10_10_00_10
     assert np.array_equal(ql[0], want_ql)
     assert np.array_equal(qh[0], want_qh)

@@ -306,9 +306,9 @@ def fp8_layer(i: int, tokens: int = 16) -> FP8Layer:
 # -- kq6: k-quant-style superblocks of 256 weights with 6-bit codes ------------------
 #
 # Layout (this library's own; the pages give none): code c in [-32, 31] kept as
-# u = c + 32, packed in weight order within each row.
-#   low plane  [N, K/2]: byte i = (u[2 i] & 15) | (u[2 i + 1] & 15) << 4
-#   high plane [N, K/4]: byte i = sum over g < 4 of (u[4 i + g] >> 4) << 2 g
+# u = c + 32; weights in groups of 16, u[i] the i-th of a group.
+#   low plane  [N, K/2]: group byte j < 8 = (u[j] & 15) | (u[j + 8] & 15) << 4
+#   high plane [N, K/4]: group byte j < 4 = sum over r < 4 of (u[j + 4 r] >> 4) << 2 r
 
 KQ6_SHAPES = [("o", 4096, 4096), ("down", 12288, 4096)]
 SEED_KQ6 = 8001
@@ -318,12 +318,12 @@ def kq6_pack(codes: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """codes int8 [N, K] in [-32, 31] -> (low plane uint8 [N, K/2], high plane uint8 [N, K/4])."""
     N, K = codes.shape
     assert K % 256 == 0 and codes.min() >= -32 and codes.max() <= 31
-    u = (codes.astype(np.int16) + 32).astype(np.uint8)
+    u = (codes.astype(np.int16) + 32).astype(np.uint8).reshape(N, K // 16, 16)
     lo = u & 15
-    ql = lo[:, 0::2] | (lo[:, 1::2] << 4)
+    ql = lo[:, :, :8] | (lo[:, :, 8:] << 4)
     hi = u >> 4
-    qh = hi[:, 0::4] | (hi[:, 1::4] << 2) | (hi[:, 2::4] << 4) | (hi[:, 3::4] << 6)
-    return ql.astype(np.uint8), qh.astype(np.uint8)
+    qh = hi[:, :, 0:4] | (hi[:, :, 4:8] << 2) | (hi[:, :, 8:12] << 4) | (hi[:, :, 12:16] << 6)
+    return ql.reshape(N, K // 2).astype(np.uint8), qh.reshape(N, K // 4).astype(np.uint8)
 
 
 def kq6_weights(g: np.random.Generator, N: int, K: int):
@@ -359,15 +359,16 @@ def kq6_layer(i: int, tokens: int = 16) -> KQ6Layer:
 
 # -- kq4: 4-bit codes with a sub-scale and a minimum per 32 weights --------------------
 #
-# Layout (this library's own): codes q in [0, 15] packed two per byte in weight
-# order (the kq6 low plane); scm [N, K/32, 2] uint8 = (sub-scale, minimum) per 32
+# Layout (this library's own): codes q in [0, 15] in the kq6 low plane (group
+# byte j < 8 of each 16 weights = q[j] | q[j + 8] << 4); scm [N, K/32, 2] uint8 = (sub-scale, minimum) per 32
 # weights, both in [0, 63]; dm [N, K/256, 2] fp16 = (d, dmin) per superblock.
 
 def kq4_pack(codes: np.ndarray) -> np.ndarray:
     """codes uint8 [N, K] in [0, 15] -> low plane uint8 [N, K/2]."""
     assert codes.min() >= 0 and codes.max() <= 15
-    c = codes.astype(np.uint8)
-    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    N, K = codes.shape
+    c = codes.astype(np.uint8).reshape(N, K // 16, 16)
+    return (c[:, :, :8] | (c[:, :, 8:] << 4)).reshape(N, K // 2).astype(np.uint8)
 
 
 def kq4_weights(g: np.random.Generator, N: int, K: int):
