@@ -391,6 +391,28 @@ def main():
                 ext.append({"op": "fp8_linear", "layer": Lf.name, "K": Lf.K, "N": Lf.N, "b": b, "us": round(us, 2),
                             "weight_GBs": round(by / (us * 1e-6) / 1e9, 1)})
             del wfs, wf0
+        # the W8A8 decode mat-vec on Qwen3-14B-shaped layers (shapes the launch tables were not tuned on)
+        for li in range(4):
+            L14 = W.qwen3_14b_layer(li, tokens=8)
+            by = L14.N * L14.K + 4 * L14.N
+            nc = copies_past_cache(by)
+            w0 = torch.from_numpy(L14.w).to(dev)
+            w14 = [w0] + [w0.clone() for _ in range(nc - 1)]
+            s14 = torch.from_numpy(L14.s_w).to(dev)
+            x14 = torch.from_numpy(L14.x.view(np.int16)).view(torch.bfloat16).to(dev)
+            q14, sa14 = iqd.quantize_activations(x14)
+            for b in (1, 4, 8):
+                y14 = torch.empty((b, L14.N), dtype=torch.bfloat16, device=dev)
+
+                def m14(b=b, y14=y14):
+                    for c in range(nc):
+                        iqd.w8a8_linear(q14[:b], sa14[:b], w14[c], s14, y=y14)
+                g = capture(m14)
+                g.replay()
+                us = time_graph(g, 10) * 1e3 / nc
+                ext.append({"op": "w8a8_linear", "model": "Qwen3-14B", "layer": L14.name, "K": L14.K, "N": L14.N,
+                            "b": b, "us": round(us, 2), "weight_GBs": round(by / (us * 1e-6) / 1e9, 1)})
+            del w14, w0
         # decode attention, Qwen3-8B heads (32 query, 8 kv, D = 128): enough cache
         # copies in rotation to exceed the 256 MB Infinity Cache
         name, Hq, Hkv, D = W.QWEN3_8B_ATTN

@@ -478,7 +478,11 @@ struct Pick {
 Pick pick(int b, int N, int K) {
     const int ntiles = (N + kTileRows - 1) / kTileRows;
     if (ntiles <= 256) return K > 8192 ? Pick{8, 8, 1} : Pick{8, 8, 0};
-    if (ntiles <= 512) return b > 8 ? Pick{8, 4, 3} : Pick{4, 4, 2};
+    // 257-512 tiles: the 4-wave, 4-way K split for few tokens (tuned at
+    // 4096 -> 6144); from b = 4 with K > 4096 the persistent 8-wave grid
+    // (measured at Qwen3-14B o, qkv and down, 5120 <= K <= 17408: b = 4
+    // 9.10 / 9.67 / 24.8 -> 8.36 / 9.54 / 20.3 us).
+    if (ntiles <= 512) return b > 8 || (b >= 4 && K > 4096) ? Pick{8, 4, 3} : Pick{4, 4, 2};
     return b > 12 ? Pick{8, 4, 5} : Pick{4, 2, 4};
 }
 
