@@ -1,13 +1,19 @@
-// Block-quantized (q8_0-style) mat-vec, 1 <= b <= 16, gfx950.
+// Block-quantized mat-vec, 1 <= b <= 16, gfx950: q8_0-style blocks, and the
+// kq6 / kq4 superblock formats decoded into the same block structure.
 //
 // Per 32-element block j of a row:  isum_j = sum q*w (int32, exact) and the
 // leaf  p_j = fl( fl( fl32(isum_j) * d_a[t,j] ) * fl32(d_w[n,j]) ).
+// kq6: w = sc * c (sub-scale per 16 weights) and d_w the superblock's scale;
+// kq4: the leaf is that of sc * sum q*a with d, minus that of m * sum a with
+// dmin (the superblock's pair).
 // The m = K/32 leaves are summed by the canonical tree: zero-padded to
 // L = 2^ceil(log2 m) leaves, adjacent pairs added level by level, so the root
 // is the same for every b, grid, wave count and split.  y = bf16(root).
 //
-// Sources: "why speculative decoding changed my output", section "the mat-vec
-// kernel" (each block's exact integer result is scaled into fp32; the stock
+// Sources: "why speculative decoding changed my output", opening (the decode
+// workload at q4_k_m and q6_k) and section "the mat-vec kernel" (q6_k rows as
+// 256-weight blocks against int8 activation blocks of 32; each block's exact
+// integer result is scaled into fp32; the stock
 // kernel dealt blocks to warps by a token-count-dependent table, changing
 // the float order).  "My speculative decoder got slower", section "Two
 // matmul schedules that survived" (split-K moved the rounding points); here
