@@ -327,11 +327,14 @@ def test_fused_bf16_matches_quantize_then_linear(iqd, N, K):
         assert_bits_equal(host_bits(y2)[:, rows], oy[:b], f"N={N} K={K} b={b} no outputs")
 
 
-def test_fused_bf16_qwen3_8b_layers_equal_unfused(iqd):
-    """Every Qwen3-8B decode layer at b = 1..8: the fused call equals
-    quantize_activations + w8a8_linear on all outputs."""
+@pytest.mark.parametrize("model", ["8B", "14B"])
+def test_fused_bf16_qwen3_layers_equal_unfused(iqd, model):
+    """Every Qwen3-8B and Qwen3-14B decode layer at b = 1..8 (the 14B shapes
+    change launch configuration between b = 2 and b = 4): the fused call
+    equals quantize_activations + w8a8_linear on all outputs."""
+    layer = W.qwen3_8b_layer if model == "8B" else W.qwen3_14b_layer
     for li in range(4):
-        L = W.qwen3_8b_layer(li, tokens=8)
+        L = layer(li, tokens=8)
         xd, wd, swd = dev(L.x), dev(L.w), dev(L.s_w)
         q, sa = iqd.quantize_activations(xd)
         for b in range(1, 9):
