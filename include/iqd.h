@@ -259,9 +259,10 @@ int lm_head_argmax(const int8_t *q, const float *s_a, const int8_t *w, const flo
 /*
  * pow2_requantize - move each weight row to a power-of-two scale.
  *
- * [P3 Abstract]: requantizing every weight scale to its nearest power of two
- * (re-rounding the weights, not only rewriting the scales) makes the scale
- * multiply exact.  Per row n, with |s| = m * 2^E, m in [1, 2):
+ * [P3 Abstract]: once each row's scale is a power of two, multiplying by it
+ * is exact, so the scale products no longer depend on their order; the
+ * weights are re-rounded to the new scale as well (changing the scale alone
+ * would change the layer's values).  Per row n, with |s| = m * 2^E, m in [1, 2):
  *     s'       = sign(s) * (m < 1.5 ? 2^E : 2^(E+1))
  *     w'[n,k]  = clamp(rint_half_even(w[n,k] * s / s'), -127, 127)
  * computed exactly (w * s has at most 32 significant bits; s' is a power of

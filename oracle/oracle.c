@@ -455,7 +455,10 @@ int oracle_pow2_requant(const int8_t *w, const float *s_w, int64_t N, int64_t K,
  *       matters is that it is fixed.
  *
  * The pages fix the structure (fixed chunks, partials, a merge) but not the
- * float order inside it.  The recipe below is this library's fixed order;
+ * float order inside it.  The recipe below is this library's fixed order,
+ * chosen to match the GPU mapping (8-dim score slices = one 16-byte load of
+ * keys per lane; 64-cell parts = one wave's cells); witnesses that tell it
+ * from the other plausible orders pin it;
  * every step depends only on the query's own row, its position and the
  * cache cells 0..position, never on how many queries share a launch, the
  * cache's allocated size or the grid.  Unlike the linear layer, it uses

@@ -224,3 +224,108 @@ def test_recipe_order_in_exact_arithmetic():
     vv = bf16_vals(v[:, 0])
     want = _recipe_exact(qv, kv, vv, cells - 1, SCALE)
     assert got[0, 0].tolist() == want
+
+
+# --- witnesses of the fixed in-chunk order -----------------------------------------
+# The pages fix chunking, partials and a merge but leave the float order inside
+# a chunk open ("My speculative decoder got slower", "Shipping the 6.4x as its
+# own backend": any one fixed rounding will do).  The recipe's order (8-dim
+# score slices joined by an adjacent-pair tree; four 64-cell parts per chunk
+# joined as (0 + 1) + (2 + 3)) is this library's choice.  Each witness below
+# places the values 2^27, 1, -2^27, 1 (binary32 spacing 16 above 2^27 and 8
+# below, so 2^27 + 1 and -2^27 + 1 both round back to +-2^27) so that the
+# chosen order gives one result and each plausible alternative another; the
+# expected outputs are worked out by hand in the docstrings.
+
+BIG = W.f32_to_bf16_bits(np.float32([2.0 ** 27]))[0]
+NBIG = W.f32_to_bf16_bits(np.float32([-(2.0 ** 27)]))[0]
+ONE = W.f32_to_bf16_bits(np.float32([1.0]))[0]
+
+
+def _part_case(cells_at):
+    """One full chunk (256 cells, the query at position 255), q = 0 so every
+    score is +0 and every weight E(0) = 1; dim 0 of the values holds the four
+    witness values at the given cells, every other value is 0.  Then l = 256
+    exactly and out[0] = bf16(o / 256) with o the chunk's sum of dim 0."""
+    D = 128
+    k = np.zeros((256, 1, D), np.uint16)
+    v = np.zeros((256, 1, D), np.uint16)
+    for cell, val in zip(cells_at, (BIG, ONE, NBIG, ONE)):
+        v[cell, 0, 0] = val
+    q = np.zeros((1, 1, D), np.uint16)
+    return oracle.attn_decode(q, k, v, 255, SCALE)[0, 0]
+
+
+def test_witness_chunk_parts_join_adjacent_pairs():
+    """Values at cells 0, 64, 128, 192 (one per part): parts [2^27, 1, -2^27,
+    1] joined (p0 + p1) + (p2 + p3) = 2^27 + -2^27 = 0.  A sequential sum over
+    the chunk would give 1 (out 2^-8), pairing at stride two 2 (out 2^-7)."""
+    out = _part_case((0, 64, 128, 192))
+    assert out[0] == 0x0000
+    assert np.all(out[1:] == 0)
+
+
+def test_witness_parts_are_64_cells_not_128():
+    """Cells 63, 64, 65, 66: part 0 ends at cell 63 (2^27), part 1 sums
+    1, -2^27, 1 in order to -2^27, the join gives 0.  With 128-cell parts the
+    four values would be one sequential run giving 1 (out 2^-8 = 0x3B80)."""
+    assert _part_case((63, 64, 65, 66))[0] == 0x0000
+
+
+def test_witness_parts_are_64_cells_not_32():
+    """Cells 31, 32, 33, 34 lie in one 64-cell part, summed in order:
+    ((2^27 + 1) - 2^27) + 1 = 1, out = bf16(1 / 256) = 2^-8.  With 32-cell
+    parts they would split into 2^27 and -2^27 and give 0."""
+    assert _part_case((31, 32, 33, 34))[0] == W.f32_to_bf16_bits(np.float32([2.0 ** -8]))[0]
+
+
+def _score_case(kdims):
+    """Two cells, the query (all ones, scale 1) at position 1.  Cell 0's key
+    carries the witness values at the given dims, cell 1's key is zero (score
+    0).  Values: cell 0 all 2, cell 1 all 4.  If cell 0 scores 0 both weights
+    are 1 and out = (2 + 4) / 2 = 3 exactly."""
+    D = 128
+    k = np.zeros((2, 1, D), np.uint16)
+    if kdims is not None:
+        for d, val in zip(kdims, (BIG, ONE, NBIG, ONE)):
+            k[0, 0, d] = val
+    v = np.zeros((2, 1, D), np.uint16)
+    v[0, 0, :] = W.f32_to_bf16_bits(np.float32([2.0]))[0]
+    v[1, 0, :] = W.f32_to_bf16_bits(np.float32([4.0]))[0]
+    q = np.full((1, 1, D), ONE, np.uint16)
+    return q, k, v
+
+
+def _score_out(kdims=None, plain_score=None):
+    q, k, v = _score_case(kdims)
+    if plain_score is not None:  # a key whose score is exactly plain_score: one nonzero dim
+        k[0, 0, 0] = W.f32_to_bf16_bits(np.float32([plain_score]))[0]
+    return oracle.attn_decode(q, k, v, 1, 1.0)[0, 0]
+
+
+def test_witness_score_slices_join_adjacent_pairs():
+    """Key dims 0, 8, 16, 24 (one per 8-dim slice): slice sums [2^27, 1, -2^27,
+    1, 0, ...], the adjacent-pair tree gives 0, so out = 3.  A single chain
+    over all 128 dims would score 1, stride pairing 2: both outputs differ."""
+    out = _score_out((0, 8, 16, 24))
+    three = W.f32_to_bf16_bits(np.float32([3.0]))[0]
+    assert np.all(out == three)
+    assert not np.array_equal(_score_out(plain_score=1.0), out)
+    assert not np.array_equal(_score_out(plain_score=2.0), out)
+
+
+def test_witness_score_slices_are_8_dims_not_16():
+    """Key dims 7, 8, 9, 10: slice 0 ends at dim 7 (2^27), slice 1 chains
+    1, -2^27, 1 to -2^27, the tree gives 0: out = 3.  16-dim slices would
+    chain all four to 1."""
+    three = W.f32_to_bf16_bits(np.float32([3.0]))[0]
+    assert np.all(_score_out((7, 8, 9, 10)) == three)
+
+
+def test_witness_score_slices_are_8_dims_not_4():
+    """Key dims 3, 4, 5, 6 lie in slice 0, chained in order to 1: the row
+    equals the row of a key that scores exactly 1.  4-dim slices would give
+    score 0 and out = 3."""
+    out = _score_out((3, 4, 5, 6))
+    assert np.array_equal(out, _score_out(plain_score=1.0))
+    assert not np.all(out == W.f32_to_bf16_bits(np.float32([3.0]))[0])

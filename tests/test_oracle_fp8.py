@@ -199,3 +199,31 @@ def test_rows_depend_only_on_their_token():
     full = oracle.fp8_linear(q, s_a, w, s_w)
     for t in range(8):
         assert np.array_equal(oracle.fp8_linear(q[t:t + 1], s_a[t:t + 1], w, s_w)[0], full[t])
+
+
+# Chain-length witnesses.  The pages leave the K order open ("My speculative
+# decoder got slower", "Two matmul schedules that survived": each schedule is
+# one fixed rounding); the recipe takes chains of 16 consecutive products
+# (one 16-byte load of codes), then the canonical tree over the chains.
+# Products B = 2^16 (256 * 256) and s = 2^-10 (2^-5 * 2^-5): B + s rounds to B
+# (spacing 2^-7 above 2^16) and -B + s rounds to -B (spacing 2^-8 below).
+
+def _chain_case(ks, K):
+    q = np.zeros((1, K), np.uint8)
+    w = np.zeros((1, K), np.uint8)
+    for k, (a, b) in zip(ks, ((256.0, 256.0), (2.0 ** -5, 2.0 ** -5), (256.0, -256.0), (2.0 ** -5, 2.0 ** -5))):
+        q[0, k], w[0, k] = code(a), code(b)
+    one = np.ones(1, np.float32)
+    return oracle.fp8_linear(q, one, w, one)[0, 0]
+
+
+def test_witness_chains_are_16_not_8():
+    """Products at k = 7, 8, 9, 10 share one 16-chain: ((B + s) - B) + s = s,
+    y = bf16(2^-10).  Chains of 8 would give B and (s - B) + s = -B, root 0."""
+    assert _chain_case((7, 8, 9, 10), 16) == bf16_bits_of(2.0 ** -10)
+
+
+def test_witness_chains_are_16_not_32():
+    """Products at k = 15, 16, 17, 18: chain 0 ends at k = 15 (B), chain 1
+    gives (s - B) + s = -B, root 0.  One 32-chain would give s."""
+    assert _chain_case((15, 16, 17, 18), 32) == 0x0000
