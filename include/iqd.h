@@ -166,9 +166,10 @@ int w8a8_linear_bf16(const void *x_bf16, const int8_t *w, const float *s_w, int6
  *   q      in  int8 [b, K]       d_a       in  fp32 [b, K/32]
  *   w      in  int8 [N, K]       d_w_fp16  in  fp16 [N, K/32]
  *   y_bf16 out bf16 [b, N]
- *   split_k    1, or a power of two with 32 * split_k <= L: split s owns the
- *              aligned subtree of leaves [s*L/split_k, (s+1)*L/split_k); a
- *              second kernel folds the top log2(split_k) tree levels.
+ *   split_k    1, or a power of two <= min(IQD_SPLIT_K_MAX, L) (and b <= 16):
+ *              split s owns the aligned subtree of leaves
+ *              [s*L/split_k, (s+1)*L/split_k); a second kernel folds the top
+ *              log2(split_k) tree levels.  Other values: IQD_ERR_UNSUPPORTED.
  * K must be a multiple of 32.
  */
 int blockq8_linear(const int8_t *q, const float *d_a, const int8_t *w, const void *d_w_fp16,

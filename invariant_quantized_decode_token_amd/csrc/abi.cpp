@@ -114,7 +114,7 @@ int w8a8_split_ok(int64_t, int64_t K, int32_t split) {
 int blockq8_split_ok(int64_t b, int64_t K, int32_t split) {
     if (split == 1) return IQD_OK;
     const int64_t L = pow2_ceil(K / 32);
-    if (b > kMatvecMaxB || !is_pow2(split) || split > IQD_SPLIT_K_MAX || 32 * static_cast<int64_t>(split) > L)
+    if (b > kMatvecMaxB || !is_pow2(split) || split > IQD_SPLIT_K_MAX || split > L)
         return IQD_ERR_UNSUPPORTED;
     return IQD_OK;
 }

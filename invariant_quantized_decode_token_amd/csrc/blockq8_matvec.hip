@@ -29,7 +29,8 @@
 // levels 1..5 over the chunk.  Chunk roots are combined with a binary carry
 // stack (the same tree, built left to right), the waves of a workgroup own
 // aligned sub-ranges of chunks and fold them in tree order, and API splits
-// own aligned subtrees folded by k_blockq8_combine.
+// own aligned subtrees folded by k_blockq8_combine (a subtree smaller than a
+// chunk is a window of lanes; the others give -0 leaves).
 // A wave takes RS rows at once, so that each activation load serves RS
 // weight rows, and issues the loads of U chunks before it uses any; loads of
 // blocks past m read zeros from out-of-range buffer offsets, so no branch
@@ -148,9 +149,17 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
     const int rg = wave / ks;
     const int kp = wave - rg * ks;
     const int rgs = kBqWaves / ks;
-    const int nss = a.nslots / a.split;  // slots per split
-    const int nsw = nss / ks;            // slots per wave
-    const int slot0 = s * nss + kp * nsw;
+    // Split s owns the aligned subtree of LS = L / split leaves.  When LS < 32
+    // the subtree is a window [wlo, wlo + LS) of one chunk: the lanes outside
+    // it read nothing and give -0 leaves, the exact identity of binary32
+    // addition, so the chunk's root is the window's root.
+    const int LS = L / a.split;
+    const bool window = LS < 32;
+    const int nss = window ? 1 : LS / 32;  // slots per split
+    const int nsw = nss / ks;              // slots per wave
+    const int slot0 = window ? (s * LS) >> 5 : s * nss + kp * nsw;
+    const int wlo = window ? (s * LS) & 31 : 0;
+    const bool inwin = (lane >> 1) >= wlo && (lane >> 1) < wlo + (window ? LS : 32);
     const int half = lane & 1;
 
     constexpr int NV = RS * B;
@@ -198,7 +207,7 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = (slot0 + i0 + u) * 32 + (lane >> 1);  // this lane's block
-                const bool live = i0 + u < nsw && j < m;
+                const bool live = i0 + u < nsw && j < m && inwin;
                 const int kb = j * 32 + 16 * half;
 #pragma unroll
                 for (int r = 0; r < RS; ++r) {
@@ -245,7 +254,8 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
                 const int slot = slot0 + i0 + u;
                 if (i0 + u >= nsw) break;  // uniform: past the wave's slots
                 const int j = slot * 32 + (lane >> 1);
-                const bool live = j < m;  // blocks in [m, L) are +0 leaves, beyond L -0 (a slot of padding gives +0)
+                const bool live = j < m && inwin;  // blocks in [m, L) are +0 leaves, beyond L or the window -0
+                const bool pad = j < L && inwin;    // (a slot made only of padding gives +0)
                 float cr = 0.0f;          // a slot made only of padding leaves
                 if (slot * 32 < m) {      // uniform
                     int32_t isum[NP], msum[FMT == kFmtKq4 ? NP : 1];
@@ -309,7 +319,7 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
                                 const float dm_hi = vhi < NV ? dmv[vhi / B] : 0.0f;
                                 p = p - (static_cast<float>(msum[v]) * da) * sel(half != 0, dm_hi, dm_lo);
                             }
-                            leaf[v] = live ? p : (j < L ? 0.0f : -0.0f);
+                            leaf[v] = live ? p : (pad ? 0.0f : -0.0f);
                         }
                     } else {
                         const int32_t tot = isum[0] + xor_lane<1>(isum[0]);
@@ -318,7 +328,7 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
                             const int32_t mt = msum[0] + xor_lane<1>(msum[0]);
                             p = p - (static_cast<float>(mt) * dav[u][0]) * dmv[0];
                         }
-                        leaf[0] = live ? p : (j < L ? 0.0f : -0.0f);
+                        leaf[0] = live ? p : (pad ? 0.0f : -0.0f);
                     }
                     // tree levels 1..5 inside the chunk: lane masks 2..32
                     cr = rs_chain<2, NPH>(leaf, lane, AddF());
@@ -382,7 +392,7 @@ hipError_t launch_b(const BqArgs &base, hipStream_t st) {
     BqArgs a = base;
     const int row_groups = (a.N + RS - 1) / RS;
     const int target = device_info().cus * 16;
-    const int nss = a.nslots / a.split;
+    const int nss = a.nslots >= a.split ? a.nslots / a.split : 1;  // whole chunk slots per split (or one window)
     int ks = 1;
     while (ks < kBqWaves && ks * 2 <= nss && static_cast<int64_t>(row_groups) * ks * a.split < target) ks *= 2;
     a.ks = ks;

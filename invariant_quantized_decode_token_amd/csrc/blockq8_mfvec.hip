@@ -368,7 +368,10 @@ bool blockq8_mfvec_fits(int b, int N, int K, int split) {
     if (b < 1 || b > 16 || K % 32 != 0) return false;
     if (static_cast<int64_t>(N + 3 * kTileRows) * K >= kOob) return false;
     if (static_cast<int64_t>(N) * (K / 32) * 2 >= kOob) return false;
-    (void)split;
+    // A split subtree must hold whole 8-leaf units (smaller ones: the lane-pair kernel).
+    int L = 1;
+    while (L < K / 32) L *= 2;
+    if (split > 1 && L / split < kUnitBlocks) return false;
     return lds_bytes(b, K) <= kMaxLds;
 }
 

@@ -37,6 +37,20 @@ class OracleError(RuntimeError):
     pass
 
 
+def default_threads() -> int:
+    """Worker threads when a call passes nthreads=0: OMP_NUM_THREADS when
+    it is set (the host's CPU share on a shared machine), else every core.
+    Threads split output rows only, so the count never changes a result."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    return os.cpu_count() or 1
+
+
+def _nt(n: int) -> int:
+    return n if n > 0 else default_threads()
+
+
 def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so with gcc and return its path."""
     if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
@@ -209,7 +223,7 @@ def w8a8(q, s_a, w, s_w, nthreads: int = 0) -> np.ndarray:
     N, K2 = w.shape
     assert K == K2 and s_a.shape == (b,) and s_w.shape == (N,)
     y = np.empty((b, N), np.uint16)
-    _check(_load().oracle_w8a8(_ptr(q), _ptr(s_a), _ptr(w), _ptr(s_w), b, N, K, _ptr(y), nthreads), "w8a8")
+    _check(_load().oracle_w8a8(_ptr(q), _ptr(s_a), _ptr(w), _ptr(s_w), b, N, K, _ptr(y), _nt(nthreads)), "w8a8")
     return y
 
 
@@ -223,7 +237,7 @@ def blockq8(q, d_a, w, d_w_bits, nthreads: int = 0) -> np.ndarray:
     N = w.shape[0]
     assert w.shape == (N, K) and d_a.shape == (b, K // 32) and d_w.shape == (N, K // 32)
     y = np.empty((b, N), np.uint16)
-    _check(_load().oracle_blockq8(_ptr(q), _ptr(d_a), _ptr(w), _ptr(d_w), b, N, K, _ptr(y), nthreads),
+    _check(_load().oracle_blockq8(_ptr(q), _ptr(d_a), _ptr(w), _ptr(d_w), b, N, K, _ptr(y), _nt(nthreads)),
            "blockq8")
     return y
 
@@ -244,7 +258,7 @@ def lm_head_argmax(q, s_a, w, s_w, nthreads: int = 0):
     logits = np.empty((b, N), np.uint16)
     am = np.empty((b,), np.int32)
     _check(_load().oracle_lm_head_argmax(_ptr(q), _ptr(s_a), _ptr(w), _ptr(s_w), b, N, K, _ptr(logits),
-                                         _ptr(am), nthreads), "lm_head_argmax")
+                                         _ptr(am), _nt(nthreads)), "lm_head_argmax")
     return logits, am
 
 
@@ -299,7 +313,7 @@ def attn_decode(q, k_cache, v_cache, pos0: int, scale, heads=None, nthreads: int
     kp = ctypes.c_void_p(k.__array_interface__["data"][0])
     vp = ctypes.c_void_p(v.__array_interface__["data"][0])
     _check(_load().oracle_attn_decode(_ptr(q), kp, vp, kc, kh, vc, vh, b, Hq, Hkv, D, pos0, float(np.float32(scale)),
-                                      h0, h1, _ptr(out), nthreads), "attn_decode")
+                                      h0, h1, _ptr(out), _nt(nthreads)), "attn_decode")
     return out
 
 
@@ -332,7 +346,7 @@ def fp8_linear(q, s_a, w, s_w, nthreads: int = 0) -> np.ndarray:
     b, K = q.shape
     N = w.shape[0]
     y = np.empty((b, N), np.uint16)
-    _check(_load().oracle_fp8_linear(_ptr(q), _ptr(s_a), _ptr(w), _ptr(s_w), b, N, K, _ptr(y), nthreads),
+    _check(_load().oracle_fp8_linear(_ptr(q), _ptr(s_a), _ptr(w), _ptr(s_w), b, N, K, _ptr(y), _nt(nthreads)),
            "fp8_linear")
     return y
 
@@ -366,7 +380,7 @@ def kq6_linear(q, d_a, ql, qh, sc, d_bits, nthreads: int = 0) -> np.ndarray:
     assert d.shape == (N, K // 256) and d_a.shape == (b, K // 32)
     y = np.empty((b, N), np.uint16)
     _check(_load().oracle_kq6_linear(_ptr(q), _ptr(d_a), _ptr(ql), _ptr(qh), _ptr(sc), _ptr(d), b, N, K, _ptr(y),
-                                     nthreads), "kq6_linear")
+                                     _nt(nthreads)), "kq6_linear")
     return y
 
 
@@ -383,6 +397,6 @@ def kq4_linear(q, d_a, ql, scm, dm_bits, nthreads: int = 0) -> np.ndarray:
     assert ql.shape == (N, K // 2) and scm.shape == (N, K // 32, 2) and dm.shape == (N, K // 256, 2)
     assert d_a.shape == (b, K // 32)
     y = np.empty((b, N), np.uint16)
-    _check(_load().oracle_kq4_linear(_ptr(q), _ptr(d_a), _ptr(ql), _ptr(scm), _ptr(dm), b, N, K, _ptr(y), nthreads),
+    _check(_load().oracle_kq4_linear(_ptr(q), _ptr(d_a), _ptr(ql), _ptr(scm), _ptr(dm), b, N, K, _ptr(y), _nt(nthreads)),
            "kq4_linear")
     return y

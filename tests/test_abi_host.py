@@ -38,7 +38,8 @@ def test_workspace_bytes():
     assert iqd.workspace_bytes(L.IQD_OP_W8A8, 8, 4096, 4096, 3) == 0       # rejected split
     assert iqd.workspace_bytes(L.IQD_OP_W8A8, 8, 4096, 131072, 1) == 0     # rejected K
     assert iqd.workspace_bytes(L.IQD_OP_BLOCKQ8, 16, 4096, 12288, 16) == 16 * 16 * 4096 * 4
-    assert iqd.workspace_bytes(L.IQD_OP_BLOCKQ8, 16, 4096, 4096, 8) == 0   # 32*8 > L=128
+    assert iqd.workspace_bytes(L.IQD_OP_BLOCKQ8, 16, 4096, 4096, 8) == 8 * 16 * 4096 * 4  # 16-leaf subtrees
+    assert iqd.workspace_bytes(L.IQD_OP_BLOCKQ8, 16, 4096, 256, 16) == 0   # 16 > L = 8
     chunks = (151936 + 4095) // 4096  # argmax chunk keys: 8 bytes per (token, chunk of 4096 logits)
     assert iqd.workspace_bytes(L.IQD_OP_LM_HEAD, 5, 151936, 4096, 1) == \
         (5 * 151936 * 2 + 15) // 16 * 16 + (5 * chunks * 8 + 15) // 16 * 16
@@ -84,8 +85,11 @@ def test_blockq8_validation(lib):
                                   None)
     assert call(K=48) == L.IQD_ERR_INVALID                   # K % 32
     assert call(K=131072 + 32) == L.IQD_ERR_RANGE
-    assert call(split=2) == L.IQD_ERR_UNSUPPORTED            # L = 32 leaves -> one split only
-    assert call(K=4096, split=8) == L.IQD_ERR_UNSUPPORTED    # 32 * 8 > 128
+    assert call(K=256, split=16) == L.IQD_ERR_UNSUPPORTED    # L = 8 leaves: at most 8 splits
+    assert call(K=256, split=8) == L.IQD_ERR_WORKSPACE       # one leaf per split
+    assert call(split=3) == L.IQD_ERR_UNSUPPORTED
+    assert call(K=4096, split=128) == L.IQD_ERR_UNSUPPORTED  # above IQD_SPLIT_K_MAX
+    assert call(K=4096, split=8) == L.IQD_ERR_WORKSPACE      # 16-leaf subtrees
     assert call(K=4096, split=4) == L.IQD_ERR_WORKSPACE
     assert call(dw=4 * A + 1) == L.IQD_ERR_ALIGN
 
@@ -96,8 +100,11 @@ def test_kq6_validation(lib):
                               wsb, None)
     assert call(K=512 + 32) == L.IQD_ERR_INVALID             # K % 256
     assert call(K=131072 + 256) == L.IQD_ERR_RANGE
-    assert call(split=2) == L.IQD_ERR_UNSUPPORTED            # L = 32 leaves -> one split only
-    assert call(K=4096, split=8) == L.IQD_ERR_UNSUPPORTED    # 32 * 8 > 128
+    assert call(K=256, split=16) == L.IQD_ERR_UNSUPPORTED    # L = 8 leaves: at most 8 splits
+    assert call(K=256, split=8) == L.IQD_ERR_WORKSPACE       # one leaf per split
+    assert call(split=3) == L.IQD_ERR_UNSUPPORTED
+    assert call(K=4096, split=128) == L.IQD_ERR_UNSUPPORTED  # above IQD_SPLIT_K_MAX
+    assert call(K=4096, split=8) == L.IQD_ERR_WORKSPACE      # 16-leaf subtrees
     assert call(K=4096, split=4) == L.IQD_ERR_WORKSPACE
     assert call(ql=3 * A + 8) == L.IQD_ERR_ALIGN
     assert call(qh=4 * A + 4) == L.IQD_ERR_ALIGN
@@ -113,7 +120,7 @@ def test_kq4_validation(lib):
         return lib.kq4_linear(ptr(q), ptr(2 * A), ptr(ql), ptr(scm), ptr(dm), b, N, K, ptr(y), split, ptr(ws), wsb,
                               None)
     assert call(K=512 + 32) == L.IQD_ERR_INVALID             # K % 256
-    assert call(split=2) == L.IQD_ERR_UNSUPPORTED            # L = 32 leaves -> one split only
+    assert call(K=256, split=16) == L.IQD_ERR_UNSUPPORTED    # L = 8 leaves: at most 8 splits
     assert call(K=4096, split=4) == L.IQD_ERR_WORKSPACE
     assert call(scm=4 * A + 1) == L.IQD_ERR_ALIGN
     assert call(dm=6 * A + 2) == L.IQD_ERR_ALIGN

@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_util import assert_bits_equal, dev, host, host_bits, sample_rows, torch
+from gpu_util import assert_bits_equal, dev, host, host_bits, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +23,7 @@ def splits_for(K):
     L = 1
     while L < m:
         L *= 2
-    return [s for s in (1, 2, 4, 8, 16, 32, 64) if s == 1 or 32 * s <= L]
+    return [s for s in (1, 2, 4, 8, 16, 32, 64) if s <= L]
 
 
 @pytest.mark.parametrize("K", [32, 64, 96, 160, 544, 1056, 2080, 4128, 8224])
@@ -89,9 +89,7 @@ def test_blockq8_config_invariance_and_parity(iqd, li):
     for i in range(16):
         iqd.blockq8_linear(q[i:i + 1], d[i:i + 1], w, dw, y=y1[i:i + 1])
     ref = host_bits(y1)
-    rows = sample_rows(N, 64, 3001 + li)
-    oy = oracle.blockq8(oq, od, L.w[rows], L.d_w[rows])
-    assert_bits_equal(ref[:, rows], oy, f"{L.name} b=1 vs oracle")
+    assert_bits_equal(ref, oracle.blockq8(oq, od, L.w, L.d_w), f"{L.name} b=1 vs oracle, all rows")
     for b in range(2, 17):
         for split in splits_for(L.K):
             out = t.empty((16, N), dtype=t.bfloat16, device="cuda")

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_util import assert_bits_equal, dev, host, host_bits, sample_rows, torch
+from gpu_util import assert_bits_equal, dev, host, host_bits, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -136,8 +136,7 @@ def test_qwen3_8b_invariance_and_parity(iqd, li):
     for i in range(16):
         iqd.fp8_linear(q[i:i + 1], s_a[i:i + 1], wd, swd, y=one[i:i + 1])
     ref = host_bits(one)
-    rows = sample_rows(L.N, 48, 7001 + li)
-    assert_bits_equal(ref[:, rows], oracle.fp8_linear(oq, osa, L.w[rows], L.s_w[rows]), f"{L.name} b=1 vs oracle")
+    assert_bits_equal(ref, oracle.fp8_linear(oq, osa, L.w, L.s_w), f"{L.name} b=1 vs oracle, all rows")
     for b in range(2, 17):
         out = t.empty((16, L.N), dtype=t.bfloat16, device="cuda")
         for t0 in range(0, 16, b):

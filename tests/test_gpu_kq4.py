@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_util import assert_bits_equal, dev, host_bits, sample_rows, torch
+from gpu_util import assert_bits_equal, dev, host_bits, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +28,7 @@ def splits_for(K):
     L = 1
     while L < m:
         L *= 2
-    return [s for s in (1, 2, 4, 8, 16, 32) if s == 1 or 32 * s <= L]
+    return [s for s in (1, 2, 4, 8, 16, 32, 64) if s <= L]
 
 
 def run(iqd, q, d_a, ql, scm, dm, split_k=1):
@@ -122,9 +122,8 @@ def test_qwen3_8b_invariance_and_parity(iqd, li):
     for i in range(16):
         iqd.kq4_linear(q[i:i + 1], d_a[i:i + 1], qld, scmd, dmd, y=one[i:i + 1])
     ref = host_bits(one)
-    rows = sample_rows(L.N, 48, 9001 + li)
-    want = oracle.kq4_linear(oq, oda, L.ql[rows], L.scm[rows], L.dm[rows])
-    assert_bits_equal(ref[:, rows], want, f"{L.name} b=1 vs oracle")
+    want = oracle.kq4_linear(oq, oda, L.ql, L.scm, L.dm)
+    assert_bits_equal(ref, want, f"{L.name} b=1 vs oracle, all rows")
     for b in range(2, 17):
         out = t.empty((16, L.N), dtype=t.bfloat16, device="cuda")
         for t0 in range(0, 16, b):

@@ -3,6 +3,7 @@ power-of-two weight-scale requantization on Qwen3-14B-shaped layers."""
 import numpy as np
 import pytest
 
+import mutants
 import oracle
 import workloads as W
 from gpu_util import assert_bits_equal, dev, host, host_bits, sample_rows, torch
@@ -15,6 +16,7 @@ def iqd():
     import invariant_quantized_decode_token_amd as m
 
     m.load()
+    mutants._load()
     return m
 
 
@@ -53,8 +55,8 @@ def test_lm_head_small_full_oracle(iqd):
 
 def test_lm_head_verify_replay(iqd):
     """64 hidden states replayed in consecutive chunks of b: 0 argmax flips and
-    0 logit differences against b = 1; sampled vocab rows and two full rows
-    against the oracle."""
+    0 logit differences against b = 1; every logit and argmax against the
+    oracle."""
     t = torch()
     L = W.lm_head_layer(tokens=64)
     N = L.N
@@ -76,12 +78,9 @@ def test_lm_head_verify_replay(iqd):
         flips = int((am[b] != am[1]).sum())
         assert flips == 0, f"b={b}: {flips} argmax flips"
         assert_bits_equal(logits[b], logits[1], f"logits b={b} vs b=1")
-    rows = sample_rows(N, 64, 5001)
-    ol = oracle.w8a8(oq, osa, L.w[rows], L.s_w[rows])
-    assert_bits_equal(logits[1][:, rows], ol, "sampled logits vs oracle")
-    ol2, oa2 = oracle.lm_head_argmax(oq[:2], osa[:2], L.w, L.s_w)
-    assert_bits_equal(logits[1][:2], ol2, "full logits rows 0-1")
-    assert_bits_equal(am[1][:2], oa2, "argmax rows 0-1")
+    ol, oa = oracle.lm_head_argmax(oq, osa, L.w, L.s_w)
+    assert_bits_equal(logits[1], ol, "logits vs oracle, all 64 x 151936")
+    assert_bits_equal(am[1], oa, "argmax vs oracle, all 64 tokens")
     # argmax equals the host argmax of the returned logits on every row
     f = W.bf16_bits_to_f32(logits[1])
     assert np.array_equal(am[1], np.argmax(f, axis=1).astype(np.int32))
@@ -90,8 +89,10 @@ def test_lm_head_verify_replay(iqd):
 @pytest.mark.parametrize("li", range(4))
 def test_qwen3_14b_pow2_requant(iqd, li):
     """Requantization bit-exact vs the oracle; both scale sets invariant over
-    b in {1, 2, 4, 8, 512} and equal to the oracle on sampled rows; with
-    power-of-two scales the epilogue equals the F3 scale order exactly."""
+    b in {1, 2, 4, 8, 512}, equal to the oracle on every row of the 64-token
+    window (sampled rows beyond); with power-of-two scales the epilogue
+    equals the F3 scale order on every output, with the layer's own scales
+    it does not."""
     t = torch()
     L = W.qwen3_14b_layer(li, tokens=512)
     N = L.N
@@ -103,12 +104,17 @@ def test_qwen3_14b_pow2_requant(iqd, li):
     oq, osa = oracle.quantize_token(L.x)
     q, sa = iqd.quantize_activations(dev(L.x))
     rows = sample_rows(N, 32, 4001 + li)
+    refs = {}
     for name, (wd, swd, hw, hs) in {"own": (w, sw, L.w, L.s_w), "pow2": (w2, sw2, ow, os_)}.items():
         y1 = t.empty((512, N), dtype=t.bfloat16, device="cuda")
         for i in range(512):
             iqd.w8a8_linear(q[i:i + 1], sa[i:i + 1], wd, swd, y=y1[i:i + 1])
         ref = host_bits(y1)
-        assert_bits_equal(ref[:, rows], oracle.w8a8(oq, osa, hw[rows], hs[rows]), f"{L.name} {name} vs oracle")
+        refs[name] = ref
+        # every output of the 64-token window; the prefill tokens beyond on sampled rows
+        assert_bits_equal(ref[:64], oracle.w8a8(oq[:64], osa[:64], hw, hs), f"{L.name} {name} vs oracle, all rows")
+        assert_bits_equal(ref[64:, rows], oracle.w8a8(oq[64:], osa[64:], hw[rows], hs[rows]),
+                          f"{L.name} {name} vs oracle, tokens 64-511 sampled rows")
         for b in (2, 4, 8):
             out = t.empty((64, N), dtype=t.bfloat16, device="cuda")
             for t0 in range(0, 64, b):
@@ -116,3 +122,16 @@ def test_qwen3_14b_pow2_requant(iqd, li):
             assert_bits_equal(host_bits(out), ref[:64], f"{L.name} {name} b={b}")
         y512 = iqd.w8a8_linear(q, sa, wd, swd)
         assert_bits_equal(host_bits(y512), ref, f"{L.name} {name} b=512")
+    # The F3 scale order acc * (s_a * s_w), run by the test-only candidate
+    # kernel on the same operands: it equals the canonical order on every
+    # output under power-of-two weight scales, and not under the layer's own
+    # ("Deterministic LLM Inference Across GPU Kernels...", Abstract, Table V:
+    # the pow2 scales make the two epilogue orders agree).
+    y3p, _ = mutants.linear("F3", q[:64], sa[:64], w2, sw2, with_acc=False)
+    assert_bits_equal(host_bits(y3p), refs["pow2"][:64], f"{L.name} pow2: F3 order == canonical")
+    y3o, _ = mutants.linear("F3", q[:64], sa[:64], w, sw, with_acc=False)
+    assert int((host_bits(y3o) != refs["own"][:64]).sum()) > 0, f"{L.name} own scales: F3 order never differs"
+    # pow2 vs own scales: the outputs differ (the layer's values changed), in
+    # a bounded way: report-level figures are checked against the oracle's
+    # CPU pins; here only that the two sets are not identical
+    assert not np.array_equal(refs["pow2"][:64], refs["own"][:64])
