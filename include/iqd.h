@@ -367,6 +367,24 @@ int attn_decode(const void *q_bf16, const void *k_cache, const void *v_cache, in
  * reject). */
 size_t attn_workspace_bytes(int64_t b, int64_t Hq, int64_t Hkv, int64_t D, int64_t pos0);
 
+/*
+ * iqd_read_ceiling - measurement helper, not a step of the linear layer:
+ * stream `bytes` of device memory with the 16-byte non-temporal loads of the
+ * mat-vec kernels and keep nothing.  Timed over the byte count of one
+ * layer's weights, it is the practical HBM ceiling of one launch of that
+ * size (dispatch, first round trip and drain included, no arithmetic, no
+ * output).  Every HBM-bound kernel is ultimately priced against the
+ * device's peak; this gives the part of that peak a launch can reach.
+ *
+ *   p      in  device memory, 16-byte aligned, `bytes` readable
+ *   bytes      a multiple of 16, >= 16
+ *   sink   out 4 bytes of device memory, written only for one 32-bit value
+ *              of the xor of all loaded words (the loads must look used)
+ * Errors: IQD_ERR_INVALID (null, size, sink inside p), IQD_ERR_ALIGN,
+ * IQD_ERR_HIP.
+ */
+int iqd_read_ceiling(const void *p, int64_t bytes, int32_t *sink, void *stream);
+
 /* Workspace bytes the op needs for these sizes (0 if none); 0 also for
  * arguments the op would reject. */
 size_t iqd_workspace_bytes(int op, int64_t b, int64_t N, int64_t K, int32_t split_k);

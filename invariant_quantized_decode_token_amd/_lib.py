@@ -65,6 +65,7 @@ SIGNATURES = {
     "attn_decode": (ctypes.c_int, [P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, I64, ctypes.c_float, P, P, SZ,
                                    P]),
     "attn_workspace_bytes": (SZ, [I64, I64, I64, I64, I64]),
+    "iqd_read_ceiling": (ctypes.c_int, [P, I64, P, P]),
     "iqd_workspace_bytes": (SZ, [ctypes.c_int, I64, I64, I64, I32]),
     "iqd_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "iqd_last_hip_error": (ctypes.c_char_p, []),
@@ -411,3 +412,15 @@ def fp8_linear(q, s_a, w, s_w, split_k: int = 1, y=None, workspace=None):
                            _stream_ptr())
     _raise(st, "fp8_linear")
     return y
+
+
+def read_ceiling(t, sink):
+    """Measurement helper: stream the bytes of device tensor t (contiguous, a
+    multiple of 16 bytes) with the mat-vec kernels' loads; sink is an int32
+    [1] device tensor."""
+    torch = _torch()
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError("t must be a contiguous cuda tensor")
+    _check_tensor(sink, "sink", (torch.int32,), (1,))
+    st = load().iqd_read_ceiling(_ptr(t), t.numel() * t.element_size(), _ptr(sink), _stream_ptr())
+    _raise(st, "iqd_read_ceiling")

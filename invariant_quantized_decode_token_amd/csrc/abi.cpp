@@ -554,4 +554,12 @@ int pow2_requantize(const int8_t *w, const float *s_w, int64_t N, int64_t K, int
                                                static_cast<hipStream_t>(stream)));
 }
 
+int iqd_read_ceiling(const void *p, int64_t bytes, int32_t *sink, void *stream) {
+    if (!p || !sink || bytes < 16 || bytes % 16 != 0) return IQD_ERR_INVALID;
+    if (!aligned(p, 16) || !aligned(sink, 4)) return IQD_ERR_ALIGN;
+    if (overlap(sink, 4, p, static_cast<size_t>(bytes))) return IQD_ERR_INVALID;
+    clear_stale_error();
+    return hip_status(iqd::launch_read_ceiling(p, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

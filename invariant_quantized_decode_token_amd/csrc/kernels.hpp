@@ -89,6 +89,9 @@ hipError_t launch_attn_decode(const uint16_t *q, const uint16_t *k, const uint16
                               int64_t vc, int64_t vh, int b, int Hq, int Hkv, int pos0, float scale, uint16_t *out,
                               void *ws, hipStream_t st);
 
+// Read-ceiling measurement kernel: streams `bytes` (a multiple of 16) from p.
+hipError_t launch_read_ceiling(const void *p, int64_t bytes, int32_t *sink, hipStream_t st);
+
 hipError_t launch_pow2_requant(const int8_t *w, const float *s, int N, int K, int8_t *w_out,
                                float *s_out, hipStream_t st);
 

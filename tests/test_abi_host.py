@@ -20,9 +20,18 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"quantize_activations", "w8a8_linear", "w8a8_linear_bf16", "blockq8_linear", "lm_head_argmax",
                           "pow2_requantize", "iqd_workspace_bytes", "iqd_status_str", "iqd_last_hip_error",
                           "attn_decode", "attn_workspace_bytes", "quantize_fp8", "fp8_linear", "kq6_linear",
-                          "kq4_linear"}
+                          "kq4_linear", "iqd_read_ceiling"}
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_read_ceiling_validation(lib):
+    rc = lib.iqd_read_ceiling
+    assert rc(None, 1024, ptr(A), None) == L.IQD_ERR_INVALID
+    assert rc(ptr(A), 1000, ptr(2 * A), None) == L.IQD_ERR_INVALID     # not a multiple of 16
+    assert rc(ptr(A), 0, ptr(2 * A), None) == L.IQD_ERR_INVALID
+    assert rc(ptr(A + 8), 1024, ptr(2 * A), None) == L.IQD_ERR_ALIGN
+    assert rc(ptr(A), 1024, ptr(A + 64), None) == L.IQD_ERR_INVALID    # sink inside the buffer
 
 
 def test_status_strings(lib):
