@@ -77,6 +77,11 @@ def committed_traffic(kernel: str):
     return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
 
 
+def log(msg: str):
+    """One progress line per finished phase, on stderr (the JSON line is stdout's only line)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -221,6 +226,7 @@ def main():
         batch_variant_rows += int(np.any(y512 != b1_rows[li], axis=1).sum())
         rows_checked += PREFILL_T
         del qp, sp
+    log(f"gate: {batch_variant_rows} batch-variant rows of {rows_checked}")
     gate = {"batch_variant_rows": batch_variant_rows, "rows_checked": rows_checked,
             "what": "every output row of the 32 timed (layer, b) calls and of a b=512 prefill pass per layer, "
                     "bitwise against the same token computed alone (b=1)"}
@@ -236,6 +242,7 @@ def main():
     ms = statistics.median(group_ms)
     ms_min = min(group_ms)
     value = step_weight_bytes / (ms * 1e-3) / 1e9
+    log(f"step: {ms:.4f} ms (median of {groups}), {value:.0f} GB/s")
 
     # ---- the same work as separate quantize + linear calls -------------------------
     g_sep = capture(step_separate)
@@ -266,6 +273,7 @@ def main():
     avg_us = ms_mv * 1e3 / n_launch
     achieved = mv_bytes / n_launch / (avg_us * 1e-6) / 1e9
     traffic = committed_traffic("w8a8_decode_matvec")
+    log(f"mat-vec launches alone: {avg_us:.3f} us per launch, {achieved:.0f} GB/s")
 
     # ---- practical ceiling of these launch sizes: a plain streaming read of each
     # layer's weight bytes, launched as the step launches its mat-vecs ------------
@@ -289,6 +297,7 @@ def main():
         read_us_by_layer[L.name] = round(time_fn(rd, 20) * 1e3 / COPIES, 3)
     read_bytes = sum(L.N * L.K for L in layers) * len(B_LIST)
     ceiling_gbs = read_bytes / (ms_rd * 1e-3) / 1e9
+    log(f"read ceiling of the same launches: {ceiling_gbs:.0f} GB/s")
 
     # ---- practical ceiling of a copy: a device-to-device copy of 1 GiB (read + write bytes) --------
     # (not in a --calib run, whose one known-size copy scales the HBM counters)
@@ -397,17 +406,21 @@ def main():
                         "us_by_split": {str(k): round(v, 2) for k, v in per_split.items()}})
             del wsp, qp, sp
         out["prefill"] = pre
+        log("prefill timed")
 
     if not args.no_configs:
         out["configs"] = run_configs(iqd, W, np, torch, dev, to_dev_bf16, bits, time_fn, copies_past_cache,
                                      layers, wsets, swsets, xs)
+        log("configs timed")
 
     if args.extra:
         out["extra"] = run_extra(iqd, W, np, torch, dev, time_fn, copies_past_cache)
+        log("extra timed")
 
     if not args.no_cpu:
         out["cpu_baseline"], out["mismatches"], out["gate"]["oracle"] = run_cpu_baseline(
             np, layers, step_out, step_weight_bytes)
+        log(f"cpu baseline: {out['cpu_baseline']['value']} GB/s, {out['mismatches']} mismatches vs the oracle")
 
     if args.calib:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -494,6 +507,7 @@ def run_configs(iqd, W, np, torch, dev, to_dev_bf16, bits, time_fn, copies_past_
                     scales=scales)
             del wl
         rep.append(pow2_report(np, L14.name, bits, q14, sa14, (w0, s0), (w2, s2), outs))
+        log(f"C4 {L14.name} timed")
         del w0, w2, s0, s2
     res.append({"config": "C4 Qwen3-14B", "op": "pow2 vs own scales, 64 tokens", "layers": rep})
 
