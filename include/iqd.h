@@ -258,6 +258,28 @@ int lm_head_argmax(const int8_t *q, const float *s_a, const int8_t *w, const flo
                    size_t workspace_bytes, void *stream);
 
 /*
+ * lm_head_argmax_static - lm_head_argmax without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The workspace
+ * lm_head_argmax would take from the caller comes from a library-owned
+ * device array of IQD_STATIC_SCRATCH_BYTES per GPU, which each GPU the
+ * library runs on holds until the process ends.  The call allocates nothing
+ * (no hipMalloc, no hipFree, no allocating library routine).
+ *
+ * Same arguments, results and bits as lm_head_argmax.  Needs
+ * iqd_workspace_bytes(IQD_OP_LM_HEAD, b, N, K, 1) <= IQD_STATIC_SCRATCH_BYTES
+ * when logits_bf16 is NULL (b * N * 2 bytes of logits plus the argmax
+ * scratch), and 8 bytes per (token, chunk of 4096 logits) when the caller
+ * passes logits; larger sizes return IQD_ERR_WORKSPACE with nothing written.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (on different streams or host threads) race on it and must be
+ * serialised by the caller.  Nothing in the array needs to start at zero.
+ */
+#define IQD_STATIC_SCRATCH_BYTES (8u << 20)
+int lm_head_argmax_static(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int64_t b,
+                          int64_t N, int64_t K, void *logits_bf16, int32_t *argmax, void *stream);
+
+/*
  * pow2_requantize - move each weight row to a power-of-two scale.
  *
  * [P3 Abstract]: once each row's scale is a power of two, multiplying by it

@@ -59,6 +59,7 @@ SIGNATURES = {
     "kq6_linear": (ctypes.c_int, [P, P, P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]),
     "kq4_linear": (ctypes.c_int, [P, P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]),
     "lm_head_argmax": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, P, SZ, P]),
+    "lm_head_argmax_static": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, P]),
     "pow2_requantize": (ctypes.c_int, [P, P, I64, I64, P, P, P]),
     "quantize_fp8": (ctypes.c_int, [P, I64, I64, P, P, P]),
     "fp8_linear": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]),
@@ -317,6 +318,35 @@ def lm_head_argmax(q, s_a, w, s_w, logits=True, argmax=None, workspace=None):
     st = load().lm_head_argmax(_ptr(q), _ptr(s_a), _ptr(w), _ptr(s_w), b, N, K, _ptr(lg), _ptr(argmax),
                                _ptr(workspace), wsb, _stream_ptr())
     _raise(st, "lm_head_argmax")
+    return lg, argmax
+
+
+IQD_STATIC_SCRATCH_BYTES = 8 << 20
+
+
+def lm_head_argmax_static(q, s_a, w, s_w, logits=True, argmax=None):
+    """lm_head_argmax with the library's own device scratch in place of a
+    workspace (allocates nothing when logits and argmax are given) ->
+    (logits bf16 [b, N] or None, argmax int32 [b])."""
+    torch = _torch()
+    _check_tensor(q, "q", (torch.int8,))
+    b, K = q.shape
+    N = w.shape[0]
+    _check_tensor(s_a, "s_a", (torch.float32,), (b,))
+    _check_tensor(w, "w", (torch.int8,), (N, K))
+    _check_tensor(s_w, "s_w", (torch.float32,), (N,))
+    lg = None
+    if logits is True:
+        lg = torch.empty((b, N), dtype=torch.bfloat16, device=q.device)
+    elif isinstance(logits, torch.Tensor):
+        lg = logits
+        _check_tensor(lg, "logits", (torch.bfloat16,), (b, N))
+    if argmax is None:
+        argmax = torch.empty((b,), dtype=torch.int32, device=q.device)
+    _check_tensor(argmax, "argmax", (torch.int32,), (b,))
+    st = load().lm_head_argmax_static(_ptr(q), _ptr(s_a), _ptr(w), _ptr(s_w), b, N, K, _ptr(lg), _ptr(argmax),
+                                      _stream_ptr())
+    _raise(st, "lm_head_argmax_static")
     return lg, argmax
 
 

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libiqd.so")
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "quantize.hip", "w8a8_matvec.hip", "w8a8_mfvec.hip", "w8a8_mfma.hip", "blockq8_matvec.hip", "blockq8_mfvec.hip",
-           "lm_head.hip", "requant.hip", "attention.hip", "fp8.hip", "ceiling.hip"]
+           "lm_head.hip", "requant.hip", "attention.hip", "fp8.hip", "ceiling.hip", "static_scratch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

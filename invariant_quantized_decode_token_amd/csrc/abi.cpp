@@ -413,6 +413,56 @@ int kq4_linear(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8
     return hip_status(iqd::launch_blockq8_combine(part, bi, Ni, split_k, y, hs));
 }
 
+namespace {
+
+// The LM head after validation of everything but the workspace.
+int lm_head_run(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int64_t b, int64_t N,
+                int64_t K, void *logits_bf16, int32_t *argmax, void *workspace, hipStream_t hs) {
+    clear_stale_error();
+    uint16_t *logits = static_cast<uint16_t *>(logits_bf16 ? logits_bf16 : workspace);
+    uint64_t *keys = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) +
+                                                  ws_lm_head_logits(b, N, logits_bf16 != nullptr));
+    const int Ni = static_cast<int>(N), Ki = static_cast<int>(K);
+    for (int64_t t0 = 0; t0 < b; t0 += kMatvecMaxB) {
+        const int bc = static_cast<int>(b - t0 < kMatvecMaxB ? b - t0 : kMatvecMaxB);
+        hipError_t e = iqd::launch_w8a8_matvec(q + t0 * K, s_a + t0, w, s_w, bc, Ni, Ki, logits + t0 * N, 1, nullptr,
+                                               hs);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return hip_status(iqd::launch_argmax_rows(logits, static_cast<int>(b), Ni, argmax, keys, hs));
+}
+
+int lm_head_check(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int64_t b, int64_t N,
+                  int64_t K, void *logits_bf16, int32_t *argmax) {
+    if (!q || !s_a || !w || !s_w || !argmax) return IQD_ERR_INVALID;
+    int st = check_shape(b, N, K);
+    if (st != IQD_OK) return st;
+    if (!aligned(q, 16) || !aligned(w, 16) || !aligned(s_a, 4) || !aligned(s_w, 4) || !aligned(argmax, 4) ||
+        (logits_bf16 && !aligned(logits_bf16, 2)))
+        return IQD_ERR_ALIGN;
+    const size_t lbytes = static_cast<size_t>(b) * N * 2;
+    if (any_overlap({{logits_bf16, logits_bf16 ? lbytes : 0}, {argmax, static_cast<size_t>(b) * 4}},
+                    {{q, static_cast<size_t>(b * K)}, {s_a, static_cast<size_t>(b) * 4},
+                     {w, static_cast<size_t>(N) * K}, {s_w, static_cast<size_t>(N) * 4}}))
+        return IQD_ERR_INVALID;
+    return IQD_OK;
+}
+
+}  // namespace
+
+static_assert(IQD_STATIC_SCRATCH_BYTES == iqd::kStaticScratchBytes, "the header's scratch size is the library's");
+
+int lm_head_argmax_static(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int64_t b,
+                          int64_t N, int64_t K, void *logits_bf16, int32_t *argmax, void *stream) {
+    int st = lm_head_check(q, s_a, w, s_w, b, N, K, logits_bf16, argmax);
+    if (st != IQD_OK) return st;
+    if (ws_lm_head(b, N, logits_bf16 != nullptr) > IQD_STATIC_SCRATCH_BYTES) return IQD_ERR_WORKSPACE;
+    void *scratch = nullptr;
+    hipError_t e = iqd::static_scratch(&scratch);
+    if (e != hipSuccess) return hip_status(e);
+    return lm_head_run(q, s_a, w, s_w, b, N, K, logits_bf16, argmax, scratch, static_cast<hipStream_t>(stream));
+}
+
 int lm_head_argmax(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int64_t b, int64_t N,
                    int64_t K, void *logits_bf16, int32_t *argmax, void *workspace, size_t workspace_bytes,
                    void *stream) {
@@ -433,19 +483,7 @@ int lm_head_argmax(const int8_t *q, const float *s_a, const int8_t *w, const flo
                     {{q, static_cast<size_t>(b * K)}, {s_a, static_cast<size_t>(b) * 4},
                      {w, static_cast<size_t>(N) * K}, {s_w, static_cast<size_t>(N) * 4}}))
         return IQD_ERR_INVALID;
-    clear_stale_error();
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    uint16_t *logits = static_cast<uint16_t *>(logits_bf16 ? logits_bf16 : workspace);
-    uint64_t *keys = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) +
-                                                  ws_lm_head_logits(b, N, logits_bf16 != nullptr));
-    const int Ni = static_cast<int>(N), Ki = static_cast<int>(K);
-    for (int64_t t0 = 0; t0 < b; t0 += kMatvecMaxB) {
-        const int bc = static_cast<int>(b - t0 < kMatvecMaxB ? b - t0 : kMatvecMaxB);
-        hipError_t e = iqd::launch_w8a8_matvec(q + t0 * K, s_a + t0, w, s_w, bc, Ni, Ki, logits + t0 * N, 1, nullptr,
-                                               hs);
-        if (e != hipSuccess) return hip_status(e);
-    }
-    return hip_status(iqd::launch_argmax_rows(logits, static_cast<int>(b), Ni, argmax, keys, hs));
+    return lm_head_run(q, s_a, w, s_w, b, N, K, logits_bf16, argmax, workspace, static_cast<hipStream_t>(stream));
 }
 
 size_t attn_workspace_bytes(int64_t b, int64_t Hq, int64_t Hkv, int64_t D, int64_t pos0) {

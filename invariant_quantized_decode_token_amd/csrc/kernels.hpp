@@ -89,6 +89,12 @@ hipError_t launch_attn_decode(const uint16_t *q, const uint16_t *k, const uint16
                               int64_t vc, int64_t vh, int b, int Hq, int Hkv, int pos0, float scale, uint16_t *out,
                               void *ws, hipStream_t st);
 
+// The library-owned device scratch of the entry points that allocate
+// nothing: kStaticScratchBytes per GPU, its device address for the current
+// device (taken once per device; no allocation).
+constexpr size_t kStaticScratchBytes = size_t{8} << 20;
+hipError_t static_scratch(void **out);
+
 // Read-ceiling measurement kernel: streams `bytes` (a multiple of 16) from p.
 hipError_t launch_read_ceiling(const void *p, int64_t bytes, int32_t *sink, hipStream_t st);
 

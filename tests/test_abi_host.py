@@ -20,9 +20,19 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"quantize_activations", "w8a8_linear", "w8a8_linear_bf16", "blockq8_linear", "lm_head_argmax",
                           "pow2_requantize", "iqd_workspace_bytes", "iqd_status_str", "iqd_last_hip_error",
                           "attn_decode", "attn_workspace_bytes", "quantize_fp8", "fp8_linear", "kq6_linear",
-                          "kq4_linear", "iqd_read_ceiling"}
+                          "kq4_linear", "iqd_read_ceiling", "lm_head_argmax_static"}
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_lm_head_static_validation(lib):
+    def call(b=4, N=1000, K=512, q=A, lg=0, am=5 * A):
+        return lib.lm_head_argmax_static(ptr(q), ptr(2 * A), ptr(3 * A), ptr(4 * A), b, N, K, ptr(lg), ptr(am), None)
+    assert call(b=16, N=300000, K=64, am=64 * A) == L.IQD_ERR_WORKSPACE  # 9.6 MB of logits > the static scratch
+    assert call(q=A + 8) == L.IQD_ERR_ALIGN
+    assert call(K=40) == L.IQD_ERR_INVALID
+    assert call(am=0) == L.IQD_ERR_INVALID
+    assert call(am=3 * A + 16) == L.IQD_ERR_INVALID             # argmax inside the weights
 
 
 def test_read_ceiling_validation(lib):
