@@ -312,13 +312,20 @@ hipError_t launch_w8a8_mfma(const int8_t *q, const float *s_a, const int8_t *w, 
     }
     // Tile choice, measured at b = 512 on the Qwen3-8B layers (weights read
     // from HBM) against 64- to 256-token and -row tiles, 4 or 8 waves and
-    // rings of 2 to 4 stages: 8 waves and two workgroups per CU throughout;
-    // 128 x 128 tiles with 2 stages while they (times the K splits) number
-    // at least two per CU, 128 x 64 tiles with 3 stages below that.
+    // rings of 2 to 5 stages; 8 waves throughout:
+    //  * 128 x 128 tiles with 2 stages (two workgroups per CU) while they,
+    //    times the K splits, number at least two per CU (gate_up);
+    //  * else 64 x 128 tiles with a 4-stage ring (one workgroup per CU) when
+    //    they fill at most one round of CUs (o and down: 17.7 and 40.0 us
+    //    against 19.1 and 44.5 us with the 128 x 64, 3-stage tiles);
+    //  * else 128 x 128 tiles with a 4-stage ring (qkv: 24.3 against 25.4 us;
+    //    its 384 64 x 128 tiles take 1.5 rounds and 30 us).
     const int cus = device_info().cus;
     const int64_t big = static_cast<int64_t>((b + 127) / 128) * ((N + 127) / 128) * split;
-    hipError_t e = big >= 2 * cus ? launch_tiles<128, 128, 2, 2, 4>(q, s_a, w, s_w, b, N, K, y, split, part, st)
-                                  : launch_tiles<128, 64, 3, 4, 2>(q, s_a, w, s_w, b, N, K, y, split, part, st);
+    const int64_t narrow = static_cast<int64_t>((b + 63) / 64) * ((N + 127) / 128) * split;
+    hipError_t e = big >= 2 * cus   ? launch_tiles<128, 128, 2, 2, 4>(q, s_a, w, s_w, b, N, K, y, split, part, st)
+                   : narrow <= cus ? launch_tiles<64, 128, 4, 2, 4>(q, s_a, w, s_w, b, N, K, y, split, part, st)
+                                   : launch_tiles<128, 128, 4, 4, 2>(q, s_a, w, s_w, b, N, K, y, split, part, st);
     if (e != hipSuccess || split == 1) return e;
     return launch_w8a8_combine(part, s_a, s_w, b, N, split, y, st);
 }
