@@ -127,6 +127,50 @@ hipError_t launch_w8a8_matvec(const int8_t *q, const float *s_a, const int8_t *w
     }
 }
 
+// Quantization fused in, one or two tokens: every workgroup quantizes the
+// bf16 rows into its LDS activations while its first weight chunks are in
+// flight, on a grid of two workgroups per CU that walks the row groups (so
+// that each workgroup quantizes once).
+namespace {
+
+template <int B, int XB>
+hipError_t launch_fused_xb(const MvArgs &a, hipStream_t st) {
+    const int cus = device_info().cus;
+    return mv_launch<B, 4, 2, 4, 3, XB>(a, st, cus, a.K > 8192 ? 4 : 2, 2 * cus, true);
+}
+
+template <int B>
+hipError_t launch_fused_b(const MvArgs &a, hipStream_t st) {
+    const int per_thread = (B * (a.K / 8) + 4 * kWave - 1) / (4 * kWave);  // 16-byte bf16 vectors per thread
+    if (per_thread <= 2) return launch_fused_xb<B, 2>(a, st);
+    if (per_thread <= 4) return launch_fused_xb<B, 4>(a, st);
+    if (per_thread <= 8) return launch_fused_xb<B, 8>(a, st);
+    return launch_fused_xb<B, 16>(a, st);
+}
+
+}  // namespace
+
+bool w8a8_matvec_fused_ok(int b, int N, int K) {
+    (void)N;
+    return (b == 1 || b == 2) && b * (K / 8) <= 16 * 4 * kWave;
+}
+
+hipError_t launch_w8a8_matvec_fused(const uint16_t *x, const int8_t *w, const float *s_w, int b, int N, int K,
+                                    uint16_t *y, int8_t *q_out, float *s_out, hipStream_t st) {
+    if (!w8a8_matvec_fused_ok(b, N, K)) return hipErrorInvalidValue;
+    MvArgs a{};
+    a.x = x;
+    a.q_out = q_out;
+    a.s_out = s_out;
+    a.w = w;
+    a.s_w = s_w;
+    a.N = N;
+    a.K = K;
+    a.y = y;
+    a.split = 1;
+    return b == 1 ? launch_fused_b<1>(a, st) : launch_fused_b<2>(a, st);
+}
+
 hipError_t launch_w8a8_combine(const int32_t *part, const float *s_a, const float *s_w, int b, int N,
                                int split, uint16_t *y, hipStream_t st) {
     const int64_t total = static_cast<int64_t>(b) * N;

@@ -3,6 +3,7 @@
 // template so that every launch configuration shares one definition.
 #pragma once
 
+#include "act_quant.hpp"
 #include "device.hpp"
 
 namespace iqd {
@@ -10,6 +11,9 @@ namespace iqd {
 struct MvArgs {
     const int8_t *q;
     const float *s_a;
+    const uint16_t *x;  // fused quantization: bf16 activations [B, K] (then q and s_a are unused)
+    int8_t *q_out;      // fused, optional: workgroup 0 writes the quantized activations here
+    float *s_out;       // fused, optional: and their scales here
     const int8_t *w;
     const float *s_w;
     int N, K;
@@ -41,8 +45,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 
 constexpr int kAuxStream = 2;  // non-temporal: weights are read exactly once
 
-template <int B, int RS, int U, int NW, int D, bool LDS>
+// XB > 0: the per-token quantization is fused in (split 1, activations in
+// LDS): every workgroup loads the bf16 rows (XB 16-byte vectors of 8 values
+// per thread, ahead of its first weight chunks), forms each token's absmax
+// and quantizes the rows into its LDS activations.
+template <int B, int RS, int U, int NW, int D, bool LDS, int XB = 0>
 __global__ __launch_bounds__(NW * kWave) void k_w8a8_matvec(MvArgs a) {
+    static_assert(XB == 0 || LDS, "fused quantization stages the activations in LDS");
     __shared__ int32_t red[NW][kWave];
     extern __shared__ v4i act[];  // [B][nvs] activations of this split when LDS
     const int K = a.K, N = a.N;
@@ -90,7 +99,7 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_matvec(MvArgs a) {
     const bool writer = kp == 0 && lane < NP && idx < NV;
     const int r_out = idx / B;
     const int t_out = idx - r_out * B;
-    const float sa_out = (writer && a.split == 1) ? a.s_a[t_out] : 0.0f;
+    float sa_out = (XB == 0 && writer && a.split == 1) ? a.s_a[t_out] : 0.0f;
     auto scale_of = [&](int c) __attribute__((always_inline)) {
         const int row = min(row0_of(c) + r_out, N - 1);
         return (writer && a.split == 1) ? a.s_w[row] : 0.0f;
@@ -161,10 +170,80 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_matvec(MvArgs a) {
 
     static_assert(D >= 2, "ring of at least two chunks");
     WChunk<U, RS> ring[D];  // chunk c lives in ring[c % D]; D - 1 chunks stay in flight
+    if constexpr (XB > 0) {
+        // Fused quantization.  The bf16 rows go out first (vector memory loads
+        // return in issue order, so the quantization waits for them alone),
+        // then the first weight chunks, which stay in flight meanwhile.
+        constexpr int NTH = NW * kWave;
+        const int tid = static_cast<int>(threadIdx.x);
+        const int kv8 = K / 8;  // 16-byte vectors of 8 values per token row
+        const int nv = B * kv8;
+        const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, B * K * 2);
+        v4i xa[XB];
 #pragma unroll
-    for (int i = 0; i < D - 1; ++i)
-        if (i < total) ring[i] = load_chunk(i);
-    if constexpr (LDS) {  // staged after the first weight loads, whose latency it overlaps
+        for (int j = 0; j < XB; ++j) {
+            const int v = j * NTH + tid;
+            xa[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, v < nv ? 16 * v : 0x7FFFFFF0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < D - 1; ++i)
+            if (i < total) ring[i] = load_chunk(i);
+        __shared__ uint32_t amx[B];
+        __shared__ float ssc[B], src[B];
+        if (tid < B) amx[tid] = 0u;
+        __syncthreads();
+        // Per-token maximum of |x| (|x| >= 0, so float bits order as the
+        // values): per thread, then over the wave, one LDS atomic per wave
+        // and token.
+        float m[B];
+#pragma unroll
+        for (int t = 0; t < B; ++t) m[t] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < XB; ++j) {
+            const int v = j * NTH + tid;
+            const float mj = v < nv ? act_amax8(xa[j]) : 0.0f;
+#pragma unroll
+            for (int t = 0; t < B; ++t) m[t] = (v >= t * kv8 && v < (t + 1) * kv8) ? fmaxf(m[t], mj) : m[t];
+        }
+#pragma unroll
+        for (int t = 0; t < B; ++t) {
+            m[t] = fmaxf(m[t], xor_lane<1>(m[t]));
+            m[t] = fmaxf(m[t], xor_lane<2>(m[t]));
+            m[t] = fmaxf(m[t], xor_lane<4>(m[t]));
+            m[t] = fmaxf(m[t], xor_lane<8>(m[t]));
+            m[t] = fmaxf(m[t], xor_lane<16>(m[t]));
+            m[t] = fmaxf(m[t], xor_lane<32>(m[t]));
+            if (lane == 0) atomicMax(&amx[t], __float_as_uint(m[t]));
+        }
+        __syncthreads();
+        if (tid < B) {
+            const float sc = __uint_as_float(amx[tid]) / 127.0f;  // the quantizer's scale, IEEE division
+            ssc[tid] = sc;
+            src[tid] = 1.0f / sc;
+        }
+        __syncthreads();
+        int8_t *act8 = reinterpret_cast<int8_t *>(act);  // [B][K]
+        const bool out = bx == 0 && a.q_out != nullptr;
+#pragma unroll
+        for (int j = 0; j < XB; ++j) {
+            const int v = j * NTH + tid;
+            if (v < nv) {
+                const int t = B == 1 ? 0 : v / kv8;
+                const float rc = src[t];
+                const uint2 q8 = act_quant8(xa[j], ssc[t], rc, __builtin_isfinite(rc));
+                *reinterpret_cast<uint2 *>(act8 + 8 * v) = q8;  // token t, bytes 8 (v - t kv8): t K + 8 (v - t kv8)
+                if (out) *reinterpret_cast<uint2 *>(a.q_out + 8 * static_cast<int64_t>(v)) = q8;
+            }
+        }
+        if (bx == 0 && a.s_out != nullptr && tid < B) a.s_out[tid] = ssc[tid];
+        if (writer) sa_out = ssc[t_out];
+        __syncthreads();
+    } else {
+#pragma unroll
+        for (int i = 0; i < D - 1; ++i)
+            if (i < total) ring[i] = load_chunk(i);
+    }
+    if constexpr (LDS && XB == 0) {  // staged after the first weight loads, whose latency it overlaps
         for (int i = threadIdx.x; i < B * nvs; i += NW * kWave) {
             const int t = i / nvs;
             act[i] = __builtin_amdgcn_raw_buffer_load_b128(qr, 16 * (sv0 + i - t * nvs), t * K, 0);
@@ -203,8 +282,10 @@ __global__ __launch_bounds__(256) void k_w8a8_combine(const int32_t *__restrict_
 // (row group, K part) units for about 16 waves per CU; grid = 0 gives one
 // workgroup per row-group step (with LDS: at most as many workgroups as fit,
 // persistent over the steps, so that activations are staged once each).
-template <int B, int RS, int U, int NW, int D>
+template <int B, int RS, int U, int NW, int D, int XB = 0>
 hipError_t mv_launch(MvArgs a, hipStream_t st, int cus, int ks, int grid, bool lds = false) {
+    static_assert(XB == 0 || B <= 2, "fused quantization: one or two tokens");
+    if (XB > 0 && (!lds || a.split != 1)) return hipErrorInvalidValue;
     const int kvec = a.K / 16;
     const int nvs_min = kvec / a.split;
     const int nvs_max = (kvec + a.split - 1) / a.split;
@@ -219,16 +300,19 @@ hipError_t mv_launch(MvArgs a, hipStream_t st, int cus, int ks, int grid, bool l
     a.nsteps = (a.N + rows_per_step - 1) / rows_per_step;
     const int per_wave = (nvs_max + ks - 1) / ks;
     a.nch = (per_wave + kWave * U - 1) / (kWave * U);
-    if (!lds) {
-        if (grid <= 0 || grid > a.nsteps) grid = a.nsteps;
-        hipLaunchKernelGGL((k_w8a8_matvec<B, RS, U, NW, D, false>), dim3(grid, a.split), dim3(NW * kWave), 0, st, a);
-        return hipGetLastError();
+    if constexpr (XB == 0) {
+        if (!lds) {
+            if (grid <= 0 || grid > a.nsteps) grid = a.nsteps;
+            hipLaunchKernelGGL((k_w8a8_matvec<B, RS, U, NW, D, false>), dim3(grid, a.split), dim3(NW * kWave), 0, st,
+                               a);
+            return hipGetLastError();
+        }
     }
     const size_t smem = static_cast<size_t>(B) * nvs_max * 16;
     const size_t lds_total = smem + static_cast<size_t>(NW) * kWave * 4;
     if (lds_total > 160 * 1024) return hipErrorInvalidValue;
     if (smem > 48 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w8a8_matvec<B, RS, U, NW, D, true>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w8a8_matvec<B, RS, U, NW, D, true, XB>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
         if (e != hipSuccess) return e;
     }
@@ -239,7 +323,7 @@ hipError_t mv_launch(MvArgs a, hipStream_t st, int cus, int ks, int grid, bool l
         grid = cus * per_cu;
     }
     if (grid > a.nsteps) grid = a.nsteps;
-    hipLaunchKernelGGL((k_w8a8_matvec<B, RS, U, NW, D, true>), dim3(grid, a.split), dim3(NW * kWave), smem, st, a);
+    hipLaunchKernelGGL((k_w8a8_matvec<B, RS, U, NW, D, true, XB>), dim3(grid, a.split), dim3(NW * kWave), smem, st, a);
     return hipGetLastError();
 }
 

@@ -36,6 +36,7 @@
 //  * result register i of lane l is D[4 (l / 16) + i][l % 16]: rows
 //    4 (l / 16) .. + 3 of token l % 16.  The KS partial tiles are added
 //    through LDS (exact int32) and the epilogue is applied once per output.
+#include "act_quant.hpp"
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -62,56 +63,6 @@ struct MfvArgs {
     int ntiles;  // ceil(N / 16)
     int nch;     // chunks per tile per wave
 };
-
-// Per-token quantization of 8 bf16 values (one 16-byte vector), the same
-// result as the quantize kernel: q = clamp(rint_half_even(fl(x / s)), -127,
-// 127), 0 when s == 0.  The quotient is formed as y = fl(x * fl(1 / s)) first:
-// |y - fl(x / s)| <= |x / s| (3 u + u^2) < 2.3e-5 (u = 2^-24, |x / s| <= 127
-// (1 + u)), so rint(y) == rint(fl(x / s)) unless y lies within 2^-14 of a
-// half-integer.  A vector with such a value (or any vector when 1 / s
-// overflows) is redone with the correctly rounded division.  |x / s| never
-// exceeds 127 (1 + u) for finite x, so the clamp only matters for the slow
-// path's non-finite inputs.
-__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
-
-__device__ __forceinline__ uint32_t pack4(int32_t a, int32_t b, int32_t c, int32_t d) {
-    return (static_cast<uint32_t>(a) & 0xFFu) | ((static_cast<uint32_t>(b) & 0xFFu) << 8) |
-           ((static_cast<uint32_t>(c) & 0xFFu) << 16) | (static_cast<uint32_t>(d) << 24);
-}
-
-__device__ __forceinline__ uint2 quant8(const v4i &v, float s, float rcp, bool fast_ok) {
-    if (s == 0.0f) return make_uint2(0u, 0u);
-    float e[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        e[2 * i] = bf16_lo(static_cast<uint32_t>(v[i]));
-        e[2 * i + 1] = bf16_hi(static_cast<uint32_t>(v[i]));
-    }
-    int32_t q[8];
-    bool near = !fast_ok;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float y = e[i] * rcp;
-        near |= __builtin_fabsf(__builtin_amdgcn_fractf(y) - 0.5f) <= 0x1p-14f;
-        q[i] = static_cast<int32_t>(__builtin_rintf(y));
-    }
-    if (__builtin_expect(near, 0)) {  // one branch per vector
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = static_cast<int32_t>(fminf(fmaxf(__builtin_rintf(e[i] / s), -127.0f), 127.0f));
-    }
-    return make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
-}
-
-__device__ __forceinline__ float amax8(const v4i &v) {
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m = fmaxf(m, __builtin_fabsf(bf16_lo(static_cast<uint32_t>(v[i]))));
-        m = fmaxf(m, __builtin_fabsf(bf16_hi(static_cast<uint32_t>(v[i]))));
-    }
-    return m;
-}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
@@ -280,7 +231,7 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_mfvec(MfvArgs a) {
             int tj[XB];
 #pragma unroll
             for (int j = 0; j < XB; ++j) {
-                m[j] = base + j * NTH + tid < nvx ? amax8(xa[j]) : 0.0f;
+                m[j] = base + j * NTH + tid < nvx ? act_amax8(xa[j]) : 0.0f;
                 tj[j] = t;
                 advance(t, p);
             }
@@ -330,7 +281,7 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_mfvec(MfvArgs a) {
                 const int v = base + j * NTH + tid;
                 if (v < nvx) {
                     const float rc = src[t];
-                    const uint2 q8 = quant8(xa[j], ssc[t], rc, __builtin_isfinite(rc));
+                    const uint2 q8 = act_quant8(xa[j], ssc[t], rc, __builtin_isfinite(rc));
                     *reinterpret_cast<uint2 *>(xs + t * KP + 8 * p) = q8;
                     if (out) *reinterpret_cast<uint2 *>(a.q_out + 8 * static_cast<int64_t>(v)) = q8;
                 }
