@@ -67,9 +67,10 @@ hipError_t launch_b(const MvArgs &a, hipStream_t st) {
     const int64_t wbytes = static_cast<int64_t>(a.N) * a.K;
     const bool big = wbytes >= kLdsMinWeightBytes && static_cast<int64_t>(B) * a.K / a.split <= 128 * 1024;
     if constexpr (B <= 4) {
-        // K split over all four waves of a row group for long rows (12288 -> 4096
-        // at b = 1: 10.3 us against 11.0 us with two)
-        return launch_cfg<B, 4, 2, 4, 3>(a, st, a.K > 8192 ? 4 : 2, false);
+        // K split over all four waves of a row group past K = 4096 (b = 1:
+        // 12288 -> 4096 10.3 against 11.0 us with two; 5120 -> 5120 7.1
+        // against 7.3; 5120 -> 7168 8.6 against 9.0)
+        return launch_cfg<B, 4, 2, 4, 3>(a, st, a.K > 4096 ? 4 : 2, false);
     } else if constexpr (B <= 8) {
         if (big) return launch_cfg<B, 2, 1, 16, 2>(a, st, 2, true);
         return launch_cfg<B, 4, 1, 4, 3>(a, st, 2, false);
@@ -136,7 +137,7 @@ namespace {
 template <int B, int XB>
 hipError_t launch_fused_xb(const MvArgs &a, hipStream_t st) {
     const int cus = device_info().cus;
-    return mv_launch<B, 4, 2, 4, 3, XB>(a, st, cus, a.K > 8192 ? 4 : 2, 2 * cus, true);
+    return mv_launch<B, 4, 2, 4, 3, XB>(a, st, cus, a.K > 4096 ? 4 : 2, 2 * cus, true);
 }
 
 template <int B>
