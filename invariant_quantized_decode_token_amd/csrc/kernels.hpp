@@ -37,8 +37,8 @@ hipError_t launch_w8a8_mfvec_fused(const uint16_t *x, const int8_t *w, const flo
                                    uint16_t *y, int8_t *q_out, float *s_out, hipStream_t st);
 hipError_t launch_w8a8_combine(const int32_t *part, const float *s_a, const float *s_w, int b, int N,
                                int split, uint16_t *y, hipStream_t st);
-// The dot4 mat-vec with the quantization fused in (b = 1 or 2; fused_ok says
-// which shapes): bf16 x [b, K] in, the bits of quantize + w8a8_linear out.
+// The dot4 mat-vec with the quantization fused in (one token; fused_ok says
+// which shapes): bf16 x [1, K] in, the bits of quantize + w8a8_linear out.
 bool w8a8_matvec_fused_ok(int b, int N, int K);
 hipError_t launch_w8a8_matvec_fused(const uint16_t *x, const int8_t *w, const float *s_w, int b, int N, int K,
                                     uint16_t *y, int8_t *q_out, float *s_out, hipStream_t st);

@@ -128,10 +128,12 @@ hipError_t launch_w8a8_matvec(const int8_t *q, const float *s_a, const int8_t *w
     }
 }
 
-// Quantization fused in, one or two tokens: every workgroup quantizes the
-// bf16 rows into its LDS activations while its first weight chunks are in
-// flight, on a grid of two workgroups per CU that walks the row groups (so
-// that each workgroup quantizes once).
+// Quantization fused in, one token: every workgroup quantizes the bf16 row
+// into its LDS activations while its first weight chunks are in flight, on a
+// grid of two workgroups per CU that walks the row groups (so that each
+// workgroup quantizes once).  Measured against the fused matrix-core kernel
+// on the Qwen3 layers it wins only for rows longer than 8192 (and loses at
+// b = 2 everywhere), so the entry point takes it there alone.
 namespace {
 
 template <int B, int XB>
@@ -153,7 +155,7 @@ hipError_t launch_fused_b(const MvArgs &a, hipStream_t st) {
 
 bool w8a8_matvec_fused_ok(int b, int N, int K) {
     (void)N;
-    return (b == 1 || b == 2) && b * (K / 8) <= 16 * 4 * kWave;
+    return b == 1 && K / 8 <= 16 * 4 * kWave;
 }
 
 hipError_t launch_w8a8_matvec_fused(const uint16_t *x, const int8_t *w, const float *s_w, int b, int N, int K,
@@ -169,7 +171,7 @@ hipError_t launch_w8a8_matvec_fused(const uint16_t *x, const int8_t *w, const fl
     a.K = K;
     a.y = y;
     a.split = 1;
-    return b == 1 ? launch_fused_b<1>(a, st) : launch_fused_b<2>(a, st);
+    return launch_fused_b<1>(a, st);
 }
 
 hipError_t launch_w8a8_combine(const int32_t *part, const float *s_a, const float *s_w, int b, int N,

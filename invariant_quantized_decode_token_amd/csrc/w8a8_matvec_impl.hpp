@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256) void k_w8a8_combine(const int32_t *__restrict_
 // persistent over the steps, so that activations are staged once each).
 template <int B, int RS, int U, int NW, int D, int XB = 0>
 hipError_t mv_launch(MvArgs a, hipStream_t st, int cus, int ks, int grid, bool lds = false) {
-    static_assert(XB == 0 || B <= 2, "fused quantization: one or two tokens");
+    static_assert(XB == 0 || B <= 2, "fused quantization: one or two tokens (the kernel's token test)");
     if (XB > 0 && (!lds || a.split != 1)) return hipErrorInvalidValue;
     const int kvec = a.K / 16;
     const int nvs_min = kvec / a.split;
