@@ -401,9 +401,30 @@ def main():
             best = min(per_split, key=per_split.get)
             us = per_split[best]
             tops = 2.0 * T * L.N * L.K / (us * 1e-6) / 1e12
-            pre.append({"layer": L.name, "b": T, "split_k": best, "us": round(us, 2), "TOPS": round(tops, 1),
-                        "mfma_frac": round(tops / MFMA_I8_PEAK_TOPS, 4),
-                        "us_by_split": {str(k): round(v, 2) for k, v in per_split.items()}})
+            row = {"layer": L.name, "b": T, "split_k": best, "us": round(us, 2), "TOPS": round(tops, 1),
+                   "mfma_frac": round(tops / MFMA_I8_PEAK_TOPS, 4),
+                   "us_by_split": {str(k): round(v, 2) for k, v in per_split.items()}}
+            # Context only: the vendor int8 GEMM (torch._int_mm, hipBLASLt) on the same operands and weight
+            # copies, timed eagerly (median of 5); int32 output, no scale epilogue.
+            try:
+                def vend(li=li):
+                    for c in range(COPIES):
+                        torch._int_mm(qp, wsets[li][c].t())
+                vend()  # eager, outside any graph: the library may record work a graph replay mishandles
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                vts = []
+                for _ in range(5):
+                    e0.record()
+                    vend()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    vts.append(e0.elapsed_time(e1))
+                vus = sorted(vts)[2] * 1e3 / COPIES
+                row["vendor_int8_gemm"] = {"us": round(vus, 2), "mfma_frac": round(
+                    2.0 * T * L.N * L.K / (vus * 1e-6) / 1e12 / MFMA_I8_PEAK_TOPS, 4)}
+            except RuntimeError as e:
+                row["vendor_int8_gemm"] = {"error": str(e)[:120]}
+            pre.append(row)
             del wsp, qp, sp
         out["prefill"] = pre
         log("prefill timed")

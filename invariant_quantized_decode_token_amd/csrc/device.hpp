@@ -120,6 +120,19 @@ __device__ __forceinline__ float sel(bool c, float x, float y) {
     return __int_as_float(sel(c, __float_as_int(x), __float_as_int(y)));
 }
 
+// Argmax key of a bf16 logit h at index idx: the value mapped to an
+// order-preserving integer in the high word (-0 and +0 both map to 0x8000),
+// the complemented index in the low word.  The largest key of a row is its
+// maximum at the smallest index, and a maximum of keys is order-free.  Every
+// key of a real logit is >= 2^32, so 0 never wins.
+__device__ __forceinline__ uint64_t argmax_key(uint32_t h, uint32_t idx) {
+    const int32_t o = (h & 0x8000u) ? -static_cast<int32_t>(h & 0x7FFFu) : static_cast<int32_t>(h & 0x7FFFu);
+    const uint32_t hi = static_cast<uint32_t>(o + 0x8000);
+    return (static_cast<uint64_t>(hi) << 32) | static_cast<uint64_t>(0xFFFFFFFFu - idx);
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 constexpr int pow2_ceil(int v) { return v <= 1 ? 1 : 2 * pow2_ceil((v + 1) / 2); }
 

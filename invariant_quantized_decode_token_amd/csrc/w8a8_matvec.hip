@@ -55,28 +55,28 @@ struct MvConfig {
 
 constexpr int64_t kLdsMinWeightBytes = 32ll << 20;
 
-template <int B, int RS, int U, int NW, int D>
-hipError_t launch_cfg(const MvArgs &a, hipStream_t st, int ks, bool lds) {
+template <int B, int RS, int U, int NW, int D, bool KEYS>
+hipError_t launch_cfg(const MvArgs &a, hipStream_t st, int ks, bool lds, int *grid_out) {
     const int kvec = a.K / 16;
     if (ks > kvec / a.split) ks = 1;
-    return mv_launch<B, RS, U, NW, D>(a, st, device_info().cus, ks, /*grid*/ 0, lds);
+    return mv_launch<B, RS, U, NW, D, 0, KEYS>(a, st, device_info().cus, ks, /*grid*/ 0, lds, grid_out);
 }
 
-template <int B>
-hipError_t launch_b(const MvArgs &a, hipStream_t st) {
+template <int B, bool KEYS = false>
+hipError_t launch_b(const MvArgs &a, hipStream_t st, int *grid_out = nullptr) {
     const int64_t wbytes = static_cast<int64_t>(a.N) * a.K;
     const bool big = wbytes >= kLdsMinWeightBytes && static_cast<int64_t>(B) * a.K / a.split <= 128 * 1024;
     if constexpr (B <= 4) {
         // K split over all four waves of a row group past K = 4096 (b = 1:
         // 12288 -> 4096 10.3 against 11.0 us with two; 5120 -> 5120 7.1
         // against 7.3; 5120 -> 7168 8.6 against 9.0)
-        return launch_cfg<B, 4, 2, 4, 3>(a, st, a.K > 4096 ? 4 : 2, false);
+        return launch_cfg<B, 4, 2, 4, 3, KEYS>(a, st, a.K > 4096 ? 4 : 2, false, grid_out);
     } else if constexpr (B <= 8) {
-        if (big) return launch_cfg<B, 2, 1, 16, 2>(a, st, 2, true);
-        return launch_cfg<B, 4, 1, 4, 3>(a, st, 2, false);
+        if (big) return launch_cfg<B, 2, 1, 16, 2, KEYS>(a, st, 2, true, grid_out);
+        return launch_cfg<B, 4, 1, 4, 3, KEYS>(a, st, 2, false, grid_out);
     } else {
-        if (big) return launch_cfg<B, 4, 1, 8, 2>(a, st, 1, true);
-        return launch_cfg<B, 4, 2, 4, 4>(a, st, 2, false);
+        if (big) return launch_cfg<B, 4, 1, 8, 2, KEYS>(a, st, 1, true, grid_out);
+        return launch_cfg<B, 4, 2, 4, 4, KEYS>(a, st, 2, false, grid_out);
     }
 }
 
@@ -172,6 +172,40 @@ hipError_t launch_w8a8_matvec_fused(const uint16_t *x, const int8_t *w, const fl
     a.y = y;
     a.split = 1;
     return launch_fused_b<1>(a, st);
+}
+
+hipError_t launch_w8a8_matvec_keys(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int b, int N,
+                                   int K, uint16_t *y, uint64_t *keys, int *grid, hipStream_t st) {
+    if (use_mfvec(b, N, K)) return launch_w8a8_mfvec_keys(q, s_a, w, s_w, b, N, K, y, keys, grid, st);
+    MvArgs a{};
+    a.q = q;
+    a.s_a = s_a;
+    a.w = w;
+    a.s_w = s_w;
+    a.N = N;
+    a.K = K;
+    a.y = y;
+    a.keys = keys;
+    a.split = 1;
+    switch (b) {
+        case 1: return launch_b<1, true>(a, st, grid);
+        case 2: return launch_b<2, true>(a, st, grid);
+        case 3: return launch_b<3, true>(a, st, grid);
+        case 4: return launch_b<4, true>(a, st, grid);
+        case 5: return launch_b<5, true>(a, st, grid);
+        case 6: return launch_b<6, true>(a, st, grid);
+        case 7: return launch_b<7, true>(a, st, grid);
+        case 8: return launch_b<8, true>(a, st, grid);
+        case 9: return launch_b<9, true>(a, st, grid);
+        case 10: return launch_b<10, true>(a, st, grid);
+        case 11: return launch_b<11, true>(a, st, grid);
+        case 12: return launch_b<12, true>(a, st, grid);
+        case 13: return launch_b<13, true>(a, st, grid);
+        case 14: return launch_b<14, true>(a, st, grid);
+        case 15: return launch_b<15, true>(a, st, grid);
+        case 16: return launch_b<16, true>(a, st, grid);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_w8a8_combine(const int32_t *part, const float *s_a, const float *s_w, int b, int N,

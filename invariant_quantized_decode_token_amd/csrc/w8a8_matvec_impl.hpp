@@ -5,6 +5,7 @@
 
 #include "act_quant.hpp"
 #include "device.hpp"
+#include "kernels.hpp"
 
 namespace iqd {
 
@@ -19,6 +20,7 @@ struct MvArgs {
     int N, K;
     uint16_t *y;
     int32_t *part;  // [split, B, N] when split > 1
+    uint64_t *keys; // KEYS: [B][gridDim.x], each workgroup's largest argmax key per token
     int split;
     int ks;      // waves sharing one row group along K (divides the wave count)
     int nsteps;  // row-group steps: ceil(N / rows per step)
@@ -49,10 +51,17 @@ constexpr int kAuxStream = 2;  // non-temporal: weights are read exactly once
 // LDS): every workgroup loads the bf16 rows (XB 16-byte vectors of 8 values
 // per thread, ahead of its first weight chunks), forms each token's absmax
 // and quantizes the rows into its LDS activations.
-template <int B, int RS, int U, int NW, int D, bool LDS, int XB = 0>
+// KEYS (split 1): the workgroup also leaves, per token, the largest argmax
+// key of the outputs it wrote (the LM head's argmax reads no logits back).
+template <int B, int RS, int U, int NW, int D, bool LDS, int XB = 0, bool KEYS = false>
 __global__ __launch_bounds__(NW * kWave) void k_w8a8_matvec(MvArgs a) {
     static_assert(XB == 0 || LDS, "fused quantization stages the activations in LDS");
+    static_assert(!KEYS || XB == 0, "argmax keys with the plain mat-vec only");
     __shared__ int32_t red[NW][kWave];
+    __shared__ uint64_t kb[KEYS ? B : 1];
+    if constexpr (KEYS) {
+        if (threadIdx.x < B) kb[threadIdx.x] = 0;  // ordered before use by the barrier at the end
+    }
     extern __shared__ v4i act[];  // [B][nvs] activations of this split when LDS
     const int K = a.K, N = a.N;
     const int lane = lane_id();
@@ -100,6 +109,7 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_matvec(MvArgs a) {
     const int r_out = idx / B;
     const int t_out = idx - r_out * B;
     float sa_out = (XB == 0 && writer && a.split == 1) ? a.s_a[t_out] : 0.0f;
+    uint64_t kbest = 0;  // KEYS: the largest key of the outputs this lane wrote
     auto scale_of = [&](int c) __attribute__((always_inline)) {
         const int row = min(row0_of(c) + r_out, N - 1);
         return (writer && a.split == 1) ? a.s_w[row] : 0.0f;
@@ -158,9 +168,11 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_matvec(MvArgs a) {
         if (writer) {
             const int row = row0 + r_out;
             if (row < N) {
-                if (a.split == 1)
-                    a.y[static_cast<int64_t>(t_out) * N + row] = w8a8_epilogue(val, sa_out, sw_out);
-                else
+                if (a.split == 1) {
+                    const uint16_t h = w8a8_epilogue(val, sa_out, sw_out);
+                    a.y[static_cast<int64_t>(t_out) * N + row] = h;
+                    if constexpr (KEYS) kbest = umax64(kbest, argmax_key(h, static_cast<uint32_t>(row)));
+                } else
                     a.part[(static_cast<int64_t>(s) * B + t_out) * N + row] = val;
             }
         }
@@ -261,6 +273,12 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_matvec(MvArgs a) {
             }
         }
     }
+    if constexpr (KEYS) {
+        __syncthreads();
+        if (kbest != 0) atomicMax(reinterpret_cast<unsigned long long *>(&kb[t_out]), static_cast<unsigned long long>(kbest));
+        __syncthreads();
+        if (threadIdx.x < B) a.keys[static_cast<int64_t>(threadIdx.x) * gx + bx] = kb[threadIdx.x];
+    }
 }
 
 // Exact int32 sum of the split partials, then the canonical epilogue.
@@ -282,9 +300,12 @@ __global__ __launch_bounds__(256) void k_w8a8_combine(const int32_t *__restrict_
 // (row group, K part) units for about 16 waves per CU; grid = 0 gives one
 // workgroup per row-group step (with LDS: at most as many workgroups as fit,
 // persistent over the steps, so that activations are staged once each).
-template <int B, int RS, int U, int NW, int D, int XB = 0>
-hipError_t mv_launch(MvArgs a, hipStream_t st, int cus, int ks, int grid, bool lds = false) {
+// KEYS: the grid is capped at kArgKeysMaxGrid (the kernel is persistent over
+// row groups) and *grid_out receives it.
+template <int B, int RS, int U, int NW, int D, int XB = 0, bool KEYS = false>
+hipError_t mv_launch(MvArgs a, hipStream_t st, int cus, int ks, int grid, bool lds = false, int *grid_out = nullptr) {
     static_assert(XB == 0 || B <= 2, "fused quantization: one or two tokens (the kernel's token test)");
+    if (KEYS && a.split != 1) return hipErrorInvalidValue;
     if (XB > 0 && (!lds || a.split != 1)) return hipErrorInvalidValue;
     const int kvec = a.K / 16;
     const int nvs_min = kvec / a.split;
@@ -303,8 +324,10 @@ hipError_t mv_launch(MvArgs a, hipStream_t st, int cus, int ks, int grid, bool l
     if constexpr (XB == 0) {
         if (!lds) {
             if (grid <= 0 || grid > a.nsteps) grid = a.nsteps;
-            hipLaunchKernelGGL((k_w8a8_matvec<B, RS, U, NW, D, false>), dim3(grid, a.split), dim3(NW * kWave), 0, st,
-                               a);
+            if (KEYS && grid > kArgKeysMaxGrid) grid = kArgKeysMaxGrid;
+            if (grid_out) *grid_out = grid;
+            hipLaunchKernelGGL((k_w8a8_matvec<B, RS, U, NW, D, false, 0, KEYS>), dim3(grid, a.split), dim3(NW * kWave),
+                               0, st, a);
             return hipGetLastError();
         }
     }
@@ -312,8 +335,9 @@ hipError_t mv_launch(MvArgs a, hipStream_t st, int cus, int ks, int grid, bool l
     const size_t lds_total = smem + static_cast<size_t>(NW) * kWave * 4;
     if (lds_total > 160 * 1024) return hipErrorInvalidValue;
     if (smem > 48 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w8a8_matvec<B, RS, U, NW, D, true, XB>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+        hipError_t e =
+            hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w8a8_matvec<B, RS, U, NW, D, true, XB, KEYS>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
         if (e != hipSuccess) return e;
     }
     if (grid <= 0) {
@@ -323,7 +347,10 @@ hipError_t mv_launch(MvArgs a, hipStream_t st, int cus, int ks, int grid, bool l
         grid = cus * per_cu;
     }
     if (grid > a.nsteps) grid = a.nsteps;
-    hipLaunchKernelGGL((k_w8a8_matvec<B, RS, U, NW, D, true, XB>), dim3(grid, a.split), dim3(NW * kWave), smem, st, a);
+    if (KEYS && grid > kArgKeysMaxGrid) grid = kArgKeysMaxGrid;
+    if (grid_out) *grid_out = grid;
+    hipLaunchKernelGGL((k_w8a8_matvec<B, RS, U, NW, D, true, XB, KEYS>), dim3(grid, a.split), dim3(NW * kWave), smem,
+                       st, a);
     return hipGetLastError();
 }
 

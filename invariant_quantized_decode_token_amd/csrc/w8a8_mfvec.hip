@@ -60,6 +60,7 @@ struct MfvArgs {
     const float *s_w;
     int b, N, K;
     uint16_t *y;
+    uint64_t *keys;  // KEYS: [b][gridDim.x], each workgroup's largest argmax key per token
     int ntiles;  // ceil(N / 16)
     int nch;     // chunks per tile per wave
 };
@@ -76,11 +77,18 @@ struct TChunk {
 
 __host__ __device__ constexpr int act_stride(int K) { return (K + kUnit - 1) / kUnit * kUnit + 16; }
 
-template <int NW, int KS, int U, int D, int XB, bool WFIRST, bool FUSE>
+// KEYS: the workgroup also leaves, per token, the largest argmax key of the
+// outputs it wrote (the LM head's argmax reads no logits back).
+template <int NW, int KS, int U, int D, int XB, bool WFIRST, bool FUSE, bool KEYS = false>
 __global__ __launch_bounds__(NW * kWave) void k_w8a8_mfvec(MfvArgs a) {
     constexpr int NT = NW / KS;  // tile slots per workgroup
     static_assert(NW % KS == 0 && D >= 2, "tile slots and ring");
+    static_assert(!(KEYS && FUSE), "argmax keys with the plain mat-vec only");
     __shared__ v4i red[KS > 1 ? 2 : 1][KS > 1 ? NW : 1][kWave];
+    __shared__ uint64_t kb[KEYS ? 16 : 1];
+    if constexpr (KEYS) {
+        if (threadIdx.x < 16) kb[threadIdx.x] = 0;  // ordered before use by the barrier ahead of the main loop
+    }
     extern __shared__ __attribute__((aligned(16))) int8_t smem[];  // [NW][kTBytes], then x[b][KP]
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
@@ -302,6 +310,7 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_mfvec(MfvArgs a) {
     __syncthreads();
     const int kmax = KP - 16 - 64;  // last in-row start of a 64-byte step (past K the weights are 0)
     v4i acc = v4i{0, 0, 0, 0};
+    uint64_t kbest = 0;  // KEYS: the largest key of the outputs this lane wrote
     for (int c0 = 0; c0 < total; c0 += D) {
 #pragma unroll
         for (int i = 0; i < D; ++i) {
@@ -338,11 +347,21 @@ __global__ __launch_bounds__(NW * kWave) void k_w8a8_mfvec(MfvArgs a) {
                     uint16_t *yo = a.y + static_cast<int64_t>(r) * N;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (row0 + e < N) yo[row0 + e] = w8a8_epilogue(acc[e], sa, ring[i].sw[e]);
+                        if (row0 + e < N) {
+                            const uint16_t h = w8a8_epilogue(acc[e], sa, ring[i].sw[e]);
+                            yo[row0 + e] = h;
+                            if constexpr (KEYS) kbest = umax64(kbest, argmax_key(h, static_cast<uint32_t>(row0 + e)));
+                        }
                 }
                 acc = v4i{0, 0, 0, 0};
             }
         }
+    }
+    if constexpr (KEYS) {
+        __syncthreads();
+        if (kbest != 0) atomicMax(reinterpret_cast<unsigned long long *>(&kb[r]), static_cast<unsigned long long>(kbest));
+        __syncthreads();
+        if (tid < a.b) a.keys[static_cast<int64_t>(tid) * gx + bx] = kb[tid];
     }
 }
 
@@ -351,11 +370,11 @@ constexpr int lds_bytes_static() {
     return (KS > 1 ? 2 * NW : 1) * kWave * 16 + 256;  // + the fused path's per-token scale slots
 }
 
-template <int NW, int KS, int U, int D, int XB, bool WFIRST, bool FUSE>
-hipError_t launch_x(const MfvArgs &a, int grid, int smem, hipStream_t st) {
+template <int NW, int KS, int U, int D, int XB, bool WFIRST, bool FUSE, bool KEYS>
+hipError_t launch_x(const MfvArgs &a, int grid, int smem, hipStream_t st, int *grid_out) {
     constexpr int NT = NW / KS;
     const int ngroups = (a.ntiles + NT - 1) / NT;
-    const void *fn = reinterpret_cast<const void *>(&k_w8a8_mfvec<NW, KS, U, D, XB, WFIRST, FUSE>);
+    const void *fn = reinterpret_cast<const void *>(&k_w8a8_mfvec<NW, KS, U, D, XB, WFIRST, FUSE, KEYS>);
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     if (grid <= 0) {  // one round of resident workgroups: past that, persistent ones (activations staged once each)
@@ -369,47 +388,50 @@ hipError_t launch_x(const MfvArgs &a, int grid, int smem, hipStream_t st) {
         grid = (per_cu < 1 ? 1 : per_cu) * device_info().cus;
     }
     if (grid > ngroups) grid = ngroups;
-    hipLaunchKernelGGL((k_w8a8_mfvec<NW, KS, U, D, XB, WFIRST, FUSE>), dim3(grid), dim3(NW * kWave), smem, st, a);
+    if (KEYS && grid > kArgKeysMaxGrid) grid = kArgKeysMaxGrid;  // the kernel walks tiles with a grid stride
+    if (grid_out) *grid_out = grid;
+    hipLaunchKernelGGL((k_w8a8_mfvec<NW, KS, U, D, XB, WFIRST, FUSE, KEYS>), dim3(grid), dim3(NW * kWave), smem, st,
+                       a);
     return hipGetLastError();
 }
 
 // Staged 16-byte vectors per thread (int8 codes, or bf16 values when fused):
 // the smallest instantiated count that covers all of b x K in one batch (16
 // and a loop beyond that).
-template <int NW, int KS, int U, int D, bool WFIRST, bool FUSE>
-hipError_t launch_d(const MfvArgs &a, int grid, int smem, hipStream_t st) {
+template <int NW, int KS, int U, int D, bool WFIRST, bool FUSE, bool KEYS>
+hipError_t launch_d(const MfvArgs &a, int grid, int smem, hipStream_t st, int *go) {
     const int vec_bytes = FUSE ? 8 : 16;  // K elements per 16-byte vector
     const int per_thread = (a.b * (a.K / vec_bytes) + NW * kWave - 1) / (NW * kWave);
     if constexpr (FUSE) {  // the weights-first order does not apply: the activations always go first
-        if (per_thread <= 1) return launch_x<NW, KS, U, D, 1, false, FUSE>(a, grid, smem, st);
-        if (per_thread <= 2) return launch_x<NW, KS, U, D, 2, false, FUSE>(a, grid, smem, st);
-        if (per_thread <= 4) return launch_x<NW, KS, U, D, 4, false, FUSE>(a, grid, smem, st);
-        if (per_thread <= 8) return launch_x<NW, KS, U, D, 8, false, FUSE>(a, grid, smem, st);
-        return launch_x<NW, KS, U, D, 16, false, FUSE>(a, grid, smem, st);  // past 16: two batches, x read twice
+        if (per_thread <= 1) return launch_x<NW, KS, U, D, 1, false, FUSE, KEYS>(a, grid, smem, st, go);
+        if (per_thread <= 2) return launch_x<NW, KS, U, D, 2, false, FUSE, KEYS>(a, grid, smem, st, go);
+        if (per_thread <= 4) return launch_x<NW, KS, U, D, 4, false, FUSE, KEYS>(a, grid, smem, st, go);
+        if (per_thread <= 8) return launch_x<NW, KS, U, D, 8, false, FUSE, KEYS>(a, grid, smem, st, go);
+        return launch_x<NW, KS, U, D, 16, false, FUSE, KEYS>(a, grid, smem, st, go);  // past 16: x read twice
     }
-    if (per_thread <= 1) return launch_x<NW, KS, U, D, 1, WFIRST, FUSE>(a, grid, smem, st);
-    if (per_thread <= 2) return launch_x<NW, KS, U, D, 2, WFIRST, FUSE>(a, grid, smem, st);
-    if (per_thread <= 3) return launch_x<NW, KS, U, D, 3, WFIRST, FUSE>(a, grid, smem, st);
-    if (per_thread <= 4) return launch_x<NW, KS, U, D, 4, WFIRST, FUSE>(a, grid, smem, st);
-    if (per_thread <= 6) return launch_x<NW, KS, U, D, 6, WFIRST, FUSE>(a, grid, smem, st);
-    if (per_thread <= 8) return launch_x<NW, KS, U, D, 8, WFIRST, FUSE>(a, grid, smem, st);
-    if (per_thread <= 12) return launch_x<NW, KS, U, D, 12, WFIRST, FUSE>(a, grid, smem, st);
-    return launch_x<NW, KS, U, D, 16, WFIRST, FUSE>(a, grid, smem, st);
+    if (per_thread <= 1) return launch_x<NW, KS, U, D, 1, WFIRST, FUSE, KEYS>(a, grid, smem, st, go);
+    if (per_thread <= 2) return launch_x<NW, KS, U, D, 2, WFIRST, FUSE, KEYS>(a, grid, smem, st, go);
+    if (per_thread <= 3) return launch_x<NW, KS, U, D, 3, WFIRST, FUSE, KEYS>(a, grid, smem, st, go);
+    if (per_thread <= 4) return launch_x<NW, KS, U, D, 4, WFIRST, FUSE, KEYS>(a, grid, smem, st, go);
+    if (per_thread <= 6) return launch_x<NW, KS, U, D, 6, WFIRST, FUSE, KEYS>(a, grid, smem, st, go);
+    if (per_thread <= 8) return launch_x<NW, KS, U, D, 8, WFIRST, FUSE, KEYS>(a, grid, smem, st, go);
+    if (per_thread <= 12) return launch_x<NW, KS, U, D, 12, WFIRST, FUSE, KEYS>(a, grid, smem, st, go);
+    return launch_x<NW, KS, U, D, 16, WFIRST, FUSE, KEYS>(a, grid, smem, st, go);
 }
 
 // The prologue loads D - 1 chunks of the first tile, so D - 1 may not exceed
 // the chunks of one tile; shorter K falls back to a ring of two.
-template <int NW, int KS, int U, int D, bool WFIRST, bool FUSE>
-hipError_t launch_cfg(MfvArgs a, int grid, hipStream_t st) {
+template <int NW, int KS, int U, int D, bool WFIRST, bool FUSE, bool KEYS>
+hipError_t launch_cfg(MfvArgs a, int grid, hipStream_t st, int *go) {
     a.ntiles = (a.N + kTileRows - 1) / kTileRows;
     const int nku = (a.K + kUnit - 1) / kUnit;
     a.nch = ((nku + KS - 1) / KS + U - 1) / U;
     const int smem = NW * kTBytes + a.b * act_stride(a.K);
     if (smem + lds_bytes_static<NW, KS>() > kMaxLds) return hipErrorInvalidValue;
     if constexpr (D > 2) {
-        if (a.nch < D - 1) return launch_d<NW, KS, U, 2, WFIRST, FUSE>(a, grid, smem, st);
+        if (a.nch < D - 1) return launch_d<NW, KS, U, 2, WFIRST, FUSE, KEYS>(a, grid, smem, st, go);
     }
-    return launch_d<NW, KS, U, D, WFIRST, FUSE>(a, grid, smem, st);
+    return launch_d<NW, KS, U, D, WFIRST, FUSE, KEYS>(a, grid, smem, st, go);
 }
 
 // Launch shapes from a sweep on MI355X over the Qwen3-8B decode layers at
@@ -437,15 +459,15 @@ Pick pick(int b, int N, int K) {
     return b > 12 ? Pick{8, 4, 5} : Pick{4, 2, 4};
 }
 
-template <bool FUSE>
-hipError_t launch_pick(const Pick &p, const MfvArgs &a, hipStream_t st) {
+template <bool FUSE, bool KEYS = false>
+hipError_t launch_pick(const Pick &p, const MfvArgs &a, hipStream_t st, int *go = nullptr) {
     switch (p.id) {
-        case 0: return launch_cfg<8, 8, 1, 2, false, FUSE>(a, 0, st);
-        case 1: return launch_cfg<8, 8, 2, 2, false, FUSE>(a, 0, st);
-        case 2: return launch_cfg<4, 4, 2, 2, true, FUSE>(a, 0, st);
-        case 3: return launch_cfg<8, 4, 2, 3, false, FUSE>(a, device_info().cus, st);
-        case 4: return launch_cfg<4, 2, 2, 2, true, FUSE>(a, 0, st);
-        case 5: return launch_cfg<8, 4, 2, 3, true, FUSE>(a, 0, st);
+        case 0: return launch_cfg<8, 8, 1, 2, false, FUSE, KEYS>(a, 0, st, go);
+        case 1: return launch_cfg<8, 8, 2, 2, false, FUSE, KEYS>(a, 0, st, go);
+        case 2: return launch_cfg<4, 4, 2, 2, true, FUSE, KEYS>(a, 0, st, go);
+        case 3: return launch_cfg<8, 4, 2, 3, false, FUSE, KEYS>(a, device_info().cus, st, go);
+        case 4: return launch_cfg<4, 2, 2, 2, true, FUSE, KEYS>(a, 0, st, go);
+        case 5: return launch_cfg<8, 4, 2, 3, true, FUSE, KEYS>(a, 0, st, go);
     }
     return hipErrorInvalidValue;
 }
@@ -477,6 +499,22 @@ hipError_t launch_w8a8_mfvec(const int8_t *q, const float *s_a, const int8_t *w,
     a.K = K;
     a.y = y;
     return launch_pick<false>(pick(b, N, K), a, st);
+}
+
+hipError_t launch_w8a8_mfvec_keys(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int b, int N,
+                                  int K, uint16_t *y, uint64_t *keys, int *grid, hipStream_t st) {
+    if (!w8a8_mfvec_fits(b, N, K)) return hipErrorInvalidValue;
+    MfvArgs a{};
+    a.q = q;
+    a.s_a = s_a;
+    a.w = w;
+    a.s_w = s_w;
+    a.b = b;
+    a.N = N;
+    a.K = K;
+    a.y = y;
+    a.keys = keys;
+    return launch_pick<false, true>(pick(b, N, K), a, st, grid);
 }
 
 // Every workgroup repeats the quantization of all b x K activations, while

@@ -37,6 +37,26 @@ def test_argmax_ties_small(iqd):
     assert host(am).tolist() == [17, 17, 3, 0]
 
 
+def test_argmax_ties_across_workgroups(iqd):
+    """Exact ties at the maximum in rows far apart (different mat-vec
+    workgroups and argmax chunks) of a vocabulary-sized head, at b = 1 (the
+    chunked re-read) and b = 2..5 (per-workgroup keys): the lowest row wins."""
+    K, N = 64, 151936
+    w = np.zeros((N, K), np.int8)
+    w[[70001, 9, 151935], 0] = 100    # the tie, lowest index 9; every other logit is a signed zero
+    w[[123456], 0] = -100             # the maximum when s_a < 0
+    s_w = np.ones(N, np.float32)
+    q = np.zeros((5, K), np.int8)
+    q[:, 0] = 1
+    s_a = np.array([1.0, 0.25, -1.0, 2.0, 0.0], np.float32)  # token 4: all zero -> index 0
+    for b in (1, 2, 3, 5):
+        ol, oa = oracle.lm_head_argmax(q[:b], s_a[:b], w, s_w)
+        lg, am = iqd.lm_head_argmax(dev(q[:b]), dev(s_a[:b]), dev(w), dev(s_w))
+        assert_bits_equal(host_bits(lg), ol, f"tie logits b={b}")
+        assert_bits_equal(host(am), oa, f"tie argmax b={b}")
+    assert host(am).tolist() == [9, 9, 123456, 9, 0]
+
+
 def test_lm_head_small_full_oracle(iqd):
     g = W.rng(77)
     N, K = 5003, 512
@@ -44,7 +64,7 @@ def test_lm_head_small_full_oracle(iqd):
     s_w = W.log_uniform_scales(g, N)
     x = W.normal_bf16(g, 20, K)
     oq, osa = oracle.quantize_token(x)
-    for b in (1, 3, 8, 16, 20):
+    for b in (1, 3, 8, 16, 17, 20):  # 17: a pass of 16 tokens, then one of a single token
         ol, oa = oracle.lm_head_argmax(oq[:b], osa[:b], w, s_w)
         lg, am = iqd.lm_head_argmax(dev(oq[:b]), dev(osa[:b]), dev(w), dev(s_w))
         assert_bits_equal(host_bits(lg), ol, f"logits b={b}")
