@@ -29,9 +29,10 @@
 //
 // Layout: one workgroup per (chunk, kv head, group of up to 1, 2, 4, 8 or 16
 // query rows); a row is (query token, query head) with the query heads of one
-// kv head adjacent.  Wave w of the workgroup owns part w of the chunk (64 cells) and
-// issues all of that part's key and value loads before computing; the K and
-// V chunk rows are read once per workgroup.
+// kv head adjacent.  Wave w of the workgroup owns part w of the chunk (64
+// cells): it issues all of that part's key loads before computing its scores,
+// and its value loads right after them; the K and V chunk rows are read once
+// per workgroup.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -44,6 +45,7 @@ constexpr int kXcds = 8;
 constexpr int kPart = 64;  // a chunk's sums are formed in four parts of 64 cells, one per wave
 constexpr int kParts = 4;
 constexpr int kThreads = kWave * kParts;
+constexpr int kCB = 2;     // cells per lane that share one read of a query slice (scores)
 
 // e^x for x <= 0, binary32 operations only (see the file header).
 __device__ __forceinline__ float attn_exp(float x) {
@@ -115,12 +117,16 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
     __shared__ float mrow[RM];
 
     // Wave w owns part w: cells 64 w .. 64 w + 63 of the chunk, for the scores
-    // and for the value sums.  Its loads go out first, all at once, in the
-    // order they are used (they return in issue order): the query rows, the
-    // keys (four lanes per cell, lane `sub` holding dims 32 sub .. 32 sub +
-    // 31), then the values (lane: dims 2 lane, 2 lane + 1 of each cell).  The
-    // scores then run while the values are still arriving.  Cells past the
-    // last one read cell j0 instead (in range, never used).
+    // and for the value sums.  Its query and key loads go out first, all at
+    // once, in the order they are used (they return in issue order): the
+    // query rows, then the keys (four lanes per cell, lane `sub` holding dims
+    // 32 sub .. 32 sub + 31).  The values (lane: dims 2 lane, 2 lane + 1 of
+    // each cell) are loaded once the scores are done, so that their 64
+    // registers are not held through the score loop: at about 150 VGPRs three
+    // workgroups share a CU instead of two, which hides more of each one's
+    // load latency (measured on MI355X at Qwen3-8B heads, 32768 cells: b = 1
+    // 47 -> 41 us, b = 8 164 -> 120 us, with the score blocking below).
+    // Cells past the last one read cell j0 instead (in range, never used).
     // Query element i = tid + kThreads u is row i / kD, dim i % kD.
     constexpr int QU = (RM * kD + kThreads - 1) / kThreads;
     uint16_t qv[QU];
@@ -145,8 +151,67 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 32-bit offsets into a buffer over the chunk's values (cell strides are
-    // below 2^22 elements, so a chunk spans less than 2^31 bytes)
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+        const int i = tid + kThreads * u;
+        if (i < R * kD) qs[i / kD][i % kD] = bf16_to_f32(qv[u]) * a.scale;
+    }
+    __syncthreads();
+
+    // Scores: per cell, slice chains of 8 fused multiply-adds, then the tree:
+    // two levels in the lane, two across the cell's four lanes.  A lane takes
+    // kCB of its cells (16 apart) per pass, so that each query slice read
+    // from LDS feeds kCB chains: with one cell per read the LDS, not the
+    // vector ALUs, bounds this loop (kCB = 2: 32768 cells, b = 8, 164 -> 146
+    // us; kCB = 4 needs 30 more VGPRs and costs a workgroup per CU).
+#pragma unroll
+    for (int sp = 0; sp < 4 / kCB; ++sp) {
+        if (pbase + 16 * kCB * sp >= ncell) break;  // wave-uniform
+        float kf[kCB][32];
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const uint32_t wv = static_cast<uint32_t>(kw[kCB * sp + cb][i][h]);
+                    kf[cb][8 * i + 2 * h] = bf16_to_f32(wv & 0xFFFFu);
+                    kf[cb][8 * i + 2 * h + 1] = __uint_as_float(wv & 0xFFFF0000u);
+                }
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+            if (r >= R) break;  // wave-uniform
+            const float4 *qr = reinterpret_cast<const float4 *>(&qs[r][32 * sub]);
+            float part[kCB][4];
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) {
+                const float4 x0 = qr[2 * sl], x1 = qr[2 * sl + 1];
+#pragma unroll
+                for (int cb = 0; cb < kCB; ++cb) {
+                    float acc = __builtin_fmaf(x0.x, kf[cb][8 * sl + 0], 0.0f);
+                    acc = __builtin_fmaf(x0.y, kf[cb][8 * sl + 1], acc);
+                    acc = __builtin_fmaf(x0.z, kf[cb][8 * sl + 2], acc);
+                    acc = __builtin_fmaf(x0.w, kf[cb][8 * sl + 3], acc);
+                    acc = __builtin_fmaf(x1.x, kf[cb][8 * sl + 4], acc);
+                    acc = __builtin_fmaf(x1.y, kf[cb][8 * sl + 5], acc);
+                    acc = __builtin_fmaf(x1.z, kf[cb][8 * sl + 6], acc);
+                    acc = __builtin_fmaf(x1.w, kf[cb][8 * sl + 7], acc);
+                    part[cb][sl] = acc;
+                }
+            }
+#pragma unroll
+            for (int cb = 0; cb < kCB; ++cb) {
+                const int jj = pbase + 16 * (kCB * sp + cb) + cs;
+                float s = (part[cb][0] + part[cb][1]) + (part[cb][2] + part[cb][3]);
+                s = s + xor_lane<1>(s);  // slices 0-7 with 8-15 of the pair of lanes
+                s = s + xor_lane<2>(s);  // the root
+                if (jj < ncell && sub == 0) sc[jj][r] = s;
+            }
+        }
+    }
+    // The values, while the other waves finish their scores.  32-bit offsets
+    // into a buffer over the chunk's values (cell strides are below 2^22
+    // elements, so a chunk spans less than 2^31 bytes).
     uint32_t vw[kPart];
     {
         const __amdgpu_buffer_rsrc_t vr =
@@ -157,51 +222,6 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
             const int jj = pbase + i;
             vw[i] = __builtin_amdgcn_raw_buffer_load_b32(vr, static_cast<uint32_t>(jj < ncell ? jj : 0) * vcb + 4 * lane,
                                                          0, 0);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < QU; ++u) {
-        const int i = tid + kThreads * u;
-        if (i < R * kD) qs[i / kD][i % kD] = bf16_to_f32(qv[u]) * a.scale;
-    }
-    __syncthreads();
-
-    // Scores: per cell, slice chains of 8 fused multiply-adds, then the tree:
-    // two levels in the lane, two across the cell's four lanes.
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const int jj = pbase + 16 * st + cs;
-        if (pbase + 16 * st >= ncell) break;  // wave-uniform
-        float kf[32];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                kf[8 * i + 2 * h] = bf16_to_f32(static_cast<uint32_t>(kw[st][i][h]) & 0xFFFFu);
-                kf[8 * i + 2 * h + 1] = __uint_as_float(static_cast<uint32_t>(kw[st][i][h]) & 0xFFFF0000u);
-            }
-#pragma unroll
-        for (int r = 0; r < RM; ++r) {
-            if (r >= R) break;  // wave-uniform
-            const float4 *qr = reinterpret_cast<const float4 *>(&qs[r][32 * sub]);
-            float part[4];
-#pragma unroll
-            for (int sl = 0; sl < 4; ++sl) {
-                const float4 x0 = qr[2 * sl], x1 = qr[2 * sl + 1];
-                float acc = __builtin_fmaf(x0.x, kf[8 * sl + 0], 0.0f);
-                acc = __builtin_fmaf(x0.y, kf[8 * sl + 1], acc);
-                acc = __builtin_fmaf(x0.z, kf[8 * sl + 2], acc);
-                acc = __builtin_fmaf(x0.w, kf[8 * sl + 3], acc);
-                acc = __builtin_fmaf(x1.x, kf[8 * sl + 4], acc);
-                acc = __builtin_fmaf(x1.y, kf[8 * sl + 5], acc);
-                acc = __builtin_fmaf(x1.z, kf[8 * sl + 6], acc);
-                acc = __builtin_fmaf(x1.w, kf[8 * sl + 7], acc);
-                part[sl] = acc;
-            }
-            float s = (part[0] + part[1]) + (part[2] + part[3]);
-            s = s + xor_lane<1>(s);  // slices 0-7 with 8-15 of the pair of lanes
-            s = s + xor_lane<2>(s);  // the root
-            if (jj < ncell && sub == 0) sc[jj][r] = s;
         }
     }
     __syncthreads();
