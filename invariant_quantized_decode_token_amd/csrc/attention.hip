@@ -27,7 +27,7 @@
 // polynomial, all in binary32 operations.  With one chunk the merge returns
 // o_0 / l_0 exactly, so the chunk kernel writes that directly.
 //
-// Layout: one workgroup per (chunk, kv head, group of up to 1, 2, 4, 8 or 16
+// Layout: one workgroup per (chunk, kv head, group of up to 1, 2, 4 or 8
 // query rows); a row is (query token, query head) with the query heads of one
 // kv head adjacent.  Wave w of the workgroup owns part w of the chunk (64
 // cells): it issues all of that part's key loads before computing its scores,
@@ -454,23 +454,27 @@ hipError_t launch_attn_decode(const uint16_t *q, const uint16_t *k, const uint16
     const size_t mlb = static_cast<size_t>(b) * Hq * a.nc * 2 * sizeof(float);
     a.ml = merge ? static_cast<float *>(ws) : nullptr;
     a.o = merge ? reinterpret_cast<float *>(static_cast<char *>(ws) + (mlb + 255) / 256 * 256) : nullptr;
-    // Rows per workgroup.  Single-token decode (a kv head's rows fit in 4):
-    // split them over 2 or 4 workgroups while that still leaves no more
-    // workgroups than CUs (measured at Qwen3-8B shapes: 1024 cells 13.7 ->
-    // 10.1 us with 1 row, 4096 cells 16.9 -> 14.5 us with 2, 32768 cells best
-    // with 4).  Up to 32 rows: 4 rows while the workgroups number at most two
-    // per CU, else 8 (measured against 16 at b = 2, 4, 8 with 4 query heads
-    // per kv head: 4096 cells 35.6 / 44.3 / 44.4 -> 18.9 / 21.6 / 31.4 us,
-    // 32768 cells 89 / 112 / 180 -> 73 / 109 / 179 us).  More rows: 16.
+    // Rows per workgroup (every choice gives the same bits), from a sweep of
+    // 1, 2, 4, 8 and 16 on MI355X at Qwen3-8B heads (32 query, 8 kv), 1024,
+    // 4096 and 32768 cells, b = 1, 2, 4, 8.  Single-token decode (a kv head's
+    // rows fit in 4): split them over 2 or 4 workgroups while that leaves no
+    // more workgroups than CUs (1024 cells: 1 row, 9.9 us; 4096: 2 rows, 12.9
+    // us; 32768: 4 rows, 40.6 us).  More rows: the most rows, at most 8, that
+    // still give two workgroups per CU, else one row (1024 cells, b = 2, 4,
+    // 8: 10.4 / 11.8 / 13.5 us against 14.7 / 14.8 / 15.1 with 4 rows; 32768
+    // cells, b = 8: 8 rows 119 us, 4 rows 137, 16 rows 131; b = 16: 8 rows
+    // 23 / 42 / 240 us at 1024 / 4096 / 32768 cells against 16 rows 37 / 45 /
+    // 260).
     const int64_t tiles = static_cast<int64_t>(a.nc) * Hkv;
     const int64_t nr = static_cast<int64_t>(b) * a.G;  // rows of one kv head
     const int cus = device_info().cus;
-    int rm = 16;
+    int rm;
     if (nr <= 4) {
         rm = 4;
         while (rm > 1 && tiles * ((nr + rm / 2 - 1) / (rm / 2)) <= cus) rm /= 2;
-    } else if (nr <= 32) {
-        rm = tiles * ((nr + 3) / 4) <= 2 * cus ? 4 : 8;
+    } else {
+        rm = 8;
+        while (rm > 1 && tiles * ((nr + rm - 1) / rm) < 2 * cus) rm /= 2;
     }
     const int64_t nrg = (nr + rm - 1) / rm;
     const int64_t wgs = (tiles + kXcds - 1) / kXcds * kXcds * nrg;  // every XCD gets whole tiles
@@ -479,8 +483,7 @@ hipError_t launch_attn_decode(const uint16_t *q, const uint16_t *k, const uint16
         case 1: hipLaunchKernelGGL(k_attn_chunk<1>, grid, dim3(kThreads), 0, st, a); break;
         case 2: hipLaunchKernelGGL(k_attn_chunk<2>, grid, dim3(kThreads), 0, st, a); break;
         case 4: hipLaunchKernelGGL(k_attn_chunk<4>, grid, dim3(kThreads), 0, st, a); break;
-        case 8: hipLaunchKernelGGL(k_attn_chunk<8>, grid, dim3(kThreads), 0, st, a); break;
-        default: hipLaunchKernelGGL(k_attn_chunk<16>, grid, dim3(kThreads), 0, st, a); break;
+        default: hipLaunchKernelGGL(k_attn_chunk<8>, grid, dim3(kThreads), 0, st, a); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !merge) return e;

@@ -105,12 +105,13 @@ def test_cache_allocation_and_strides_do_not_matter(iqd):
     del t
 
 
-@pytest.mark.parametrize("cells,b", [(2049, 8), (5600, 3), (9000, 2)])
+@pytest.mark.parametrize("cells,b", [(4100, 8), (8300, 3), (16500, 2), (2049, 8), (5600, 3), (9000, 2)])
 def test_row_groups_of_eight(iqd, cells, b):
-    """Qwen3-8B heads with more (chunk, kv head) tiles than two per CU take
-    workgroups of up to 8 rows on a 256-CU chip: 32 rows as four full groups,
-    12 rows as a full group and a ragged one of 4, 8 rows as one.  Sampled
-    heads against the oracle; every row equals its token decoded alone."""
+    """Qwen3-8B heads at contexts long enough for workgroups of 8 rows that
+    still number two per CU on a 256-CU chip: 32 rows as four full groups
+    (4100 cells), 12 rows as a full group and a ragged one of 4 (8300), 8 rows
+    as one (16500); shorter contexts take groups of 4 rows.  Sampled heads
+    against the oracle; every row equals its token decoded alone."""
     case = W.attn_case(W.SEED_ATTN + 3 * cells + b, b, cells)
     kd, vd = dev(case.k), dev(case.v)
     got = run(iqd, case, k=kd, v=vd)
