@@ -258,9 +258,11 @@ int w8a8_linear_bf16(const void *x_bf16, const int8_t *w, const float *s_w, int6
     if (!aligned(x_bf16, 16) || !aligned(w, 16) || !aligned(s_w, 4) || !aligned(y_bf16, 2) ||
         (q_out && !aligned(q_out, 16)) || (s_a_out && !aligned(s_a_out, 4)))
         return IQD_ERR_ALIGN;
+    const bool dot4_fused = b == 1 && K > 4096 && N <= K && iqd::w8a8_matvec_fused_ok(1, static_cast<int>(N),
+                                                                                     static_cast<int>(K));
     const bool fused = (b <= kMatvecMaxB && iqd::w8a8_mfvec_fused_ok(static_cast<int>(b), static_cast<int>(N),
                                                                     static_cast<int>(K))) ||
-                       (b == 1 && K > 8192 && iqd::w8a8_matvec_fused_ok(1, static_cast<int>(N), static_cast<int>(K)));
+                       dot4_fused;
     const size_t ws = (!fused && (!q_out || !s_a_out)) ? ws_w8a8_bf16(b, K) : 0;
     if (ws > 0) {
         if (!workspace || workspace_bytes < ws) return IQD_ERR_WORKSPACE;
@@ -276,10 +278,11 @@ int w8a8_linear_bf16(const void *x_bf16, const int8_t *w, const float *s_w, int6
     const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
     uint16_t *y = static_cast<uint16_t *>(y_bf16);
     const int bi = static_cast<int>(b), Ni = static_cast<int>(N), Ki = static_cast<int>(K);
-    // One token with rows longer than 8192: the dot4 kernel with the
-    // quantization fused in (Qwen3-8B down at b = 1: 12.8 against 13.4 us).
-    if (b == 1 && K > 8192 && iqd::w8a8_matvec_fused_ok(bi, Ni, Ki))
-        return hip_status(iqd::launch_w8a8_matvec_fused(x, w, s_w, bi, Ni, Ki, y, q_out, s_a_out, hs));
+    // One token with rows longer than 4096 and no more rows than K: the dot4
+    // kernel with the quantization fused in (Qwen3-8B down at b = 1: 12.8
+    // against 13.4 us; Qwen3-14B o: 8.6 against 9.6 us; wider matrices, such
+    // as the 14B qkv and gate_up, stay on the matrix-core kernel).
+    if (dot4_fused) return hip_status(iqd::launch_w8a8_matvec_fused(x, w, s_w, bi, Ni, Ki, y, q_out, s_a_out, hs));
     if (fused) return hip_status(iqd::launch_w8a8_mfvec_fused(x, w, s_w, bi, Ni, Ki, y, q_out, s_a_out, hs));
     int8_t *q = q_out ? q_out : static_cast<int8_t *>(workspace);
     float *s_a = s_a_out ? s_a_out : reinterpret_cast<float *>(static_cast<char *>(workspace) + round16(qbytes));

@@ -82,11 +82,13 @@ hipError_t launch_b(const MvArgs &a, hipStream_t st, int *grid_out = nullptr) {
 
 // The matrix-core kernel (w8a8_mfvec.hip) costs about the same for any
 // b <= 16, while the dot4 kernel's work grows with b: on MI355X the dot4
-// kernel wins at b = 1 and, on matrices of at most 512 tiles of 16 rows with
-// K <= 8192, at b = 2; the matrix-core kernel wins everywhere else.
+// kernel wins at b = 1 and, on matrices of at most 384 tiles of 16 rows with
+// K <= 8192 (the Qwen3-8B o and qkv), at b = 2; the matrix-core kernel wins
+// everywhere else (the Qwen3-14B qkv, 448 tiles, at b = 2: 9.6 against
+// 10.7 us).
 bool use_mfvec(int b, int N, int K) {
     if (b == 1) return false;
-    if (b == 2 && (N + 15) / 16 <= 512 && K <= 8192) return false;
+    if (b == 2 && (N + 15) / 16 <= 384 && K <= 8192) return false;
     return w8a8_mfvec_fits(b, N, K);
 }
 
