@@ -57,6 +57,24 @@ def test_argmax_ties_across_workgroups(iqd):
     assert host(am).tolist() == [9, 9, 123456, 9, 0]
 
 
+@pytest.mark.parametrize("N", [1, 7, 17, 300])
+def test_lm_head_tiny_vocab(iqd, N):
+    """Vocabularies smaller than a tile or a workgroup's rows: every logit and
+    argmax against the oracle at b = 1 (chunked re-read), 2..16 (keys per
+    workgroup) and 17 (a pass of 16, then one of a single token)."""
+    g = W.rng(90 + N)
+    K = 256
+    w = W.int8_weights(g, N, K)
+    s_w = W.log_uniform_scales(g, N)
+    x = W.normal_bf16(g, 17, K)
+    oq, osa = oracle.quantize_token(x)
+    for b in (1, 2, 5, 16, 17):
+        ol, oa = oracle.lm_head_argmax(oq[:b], osa[:b], w, s_w)
+        lg, am = iqd.lm_head_argmax(dev(oq[:b]), dev(osa[:b]), dev(w), dev(s_w))
+        assert_bits_equal(host_bits(lg), ol, f"N={N} logits b={b}")
+        assert_bits_equal(host(am), oa, f"N={N} argmax b={b}")
+
+
 def test_lm_head_small_full_oracle(iqd):
     g = W.rng(77)
     N, K = 5003, 512
