@@ -249,10 +249,9 @@ int kq4_linear(const int8_t *q, const float *d_a, const uint8_t *ql, const uint8
  *   logits_bf16  out bf16 [b, N], or NULL to keep the logits in the workspace
  *   argmax       out int32 [b]
  *   workspace    iqd_workspace_bytes(IQD_OP_LM_HEAD, b, N, K, 1) bytes, 16-byte
- *                aligned: the logits when logits_bf16 is NULL, then 16 KiB of
- *                argmax scratch per token for min(b, 16) tokens (one 64-bit
- *                key per token and mat-vec workgroup; the logits are not
- *                read back)
+ *                aligned: the logits when logits_bf16 is NULL, then 256 KiB
+ *                of argmax scratch (one 64-bit key per token and mat-vec
+ *                workgroup; the logits are not read back)
  * Requires N <= 2^31 - 1.
  */
 int lm_head_argmax(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int64_t b,
@@ -271,8 +270,8 @@ int lm_head_argmax(const int8_t *q, const float *s_a, const int8_t *w, const flo
  * Same arguments, results and bits as lm_head_argmax.  Needs
  * iqd_workspace_bytes(IQD_OP_LM_HEAD, b, N, K, 1) <= IQD_STATIC_SCRATCH_BYTES
  * when logits_bf16 is NULL (b * N * 2 bytes of logits plus the argmax
- * scratch), and 16 KiB per token for min(b, 16) tokens when the caller
- * passes logits; larger sizes return IQD_ERR_WORKSPACE with nothing written.
+ * scratch), and 256 KiB when the caller passes logits; larger sizes return
+ * IQD_ERR_WORKSPACE with nothing written.
  * Every call on one GPU shares that GPU's array: calls that overlap on one
  * GPU (on different streams or host threads) race on it and must be
  * serialised by the caller.  Nothing in the array needs to start at zero.

@@ -126,14 +126,13 @@ size_t ws_w8a8(int64_t b, int64_t N, int32_t split) {
 size_t ws_w8a8_bf16(int64_t b, int64_t K) { return round16(static_cast<size_t>(b) * K) + round16(static_cast<size_t>(b) * 4); }
 
 // [logits bf16 [b, N] when the caller passes none][argmax keys u64 of one pass
-// of at most kMatvecMaxB tokens: one per (token, mat-vec workgroup), or for a
-// one-token pass one per (token, chunk of 4096 logits)]
+// of at most kMatvecMaxB tokens: one per (token, mat-vec workgroup), at most
+// kArgKeysMaxGrid in all]
 size_t ws_lm_head_logits(int64_t b, int64_t N, bool have_logits) {
     return have_logits ? 0 : round16(static_cast<size_t>(b) * N * 2);
 }
 size_t ws_lm_head(int64_t b, int64_t N, bool have_logits) {
-    const int64_t bp = b < kMatvecMaxB ? b : kMatvecMaxB;
-    return ws_lm_head_logits(b, N, have_logits) + static_cast<size_t>(bp) * iqd::kArgKeysMaxGrid * 8;
+    return ws_lm_head_logits(b, N, have_logits) + static_cast<size_t>(iqd::kArgKeysMaxGrid) * 8;
 }
 
 }  // namespace
@@ -434,20 +433,14 @@ int lm_head_run(const int8_t *q, const float *s_a, const int8_t *w, const float 
                                                   ws_lm_head_logits(b, N, logits_bf16 != nullptr));
     const int Ni = static_cast<int>(N), Ki = static_cast<int>(K);
     // Per pass of at most kMatvecMaxB tokens: the mat-vec writes the logits
-    // and one argmax key per (token, workgroup); the fold picks each token's
-    // winner.  The next pass reuses the keys after the fold (stream order).
+    // and one argmax key per (token, workgroup), at most kArgKeysMaxGrid in
+    // all; the fold picks each token's winner.  The next pass reuses the keys
+    // after the fold (stream order).
     for (int64_t t0 = 0; t0 < b; t0 += kMatvecMaxB) {
         const int bc = static_cast<int>(b - t0 < kMatvecMaxB ? b - t0 : kMatvecMaxB);
         int nkeys = 0;
-        hipError_t e;
-        if (bc == 1 && iqd::argmax_chunks(Ni) <= iqd::kArgKeysMaxGrid) {  // one token: chunked re-read, faster there
-            e = iqd::launch_w8a8_matvec(q + t0 * K, s_a + t0, w, s_w, 1, Ni, Ki, logits + t0 * N, 1, nullptr, hs);
-            if (e == hipSuccess) e = iqd::launch_argmax_partial(logits + t0 * N, 1, Ni, keys, hs);
-            nkeys = iqd::argmax_chunks(Ni);
-        } else {
-            e = iqd::launch_w8a8_matvec_keys(q + t0 * K, s_a + t0, w, s_w, bc, Ni, Ki, logits + t0 * N, keys, &nkeys,
-                                             hs);
-        }
+        hipError_t e = iqd::launch_w8a8_matvec_keys(q + t0 * K, s_a + t0, w, s_w, bc, Ni, Ki, logits + t0 * N, keys,
+                                                    iqd::kArgKeysMaxGrid / bc, &nkeys, hs);
         if (e == hipSuccess) e = iqd::launch_argmax_fold(keys, bc, nkeys, argmax + t0, hs);
         if (e != hipSuccess) return hip_status(e);
     }

@@ -74,19 +74,15 @@ hipError_t launch_kq4_matvec(const int8_t *q, const float *d_a, const uint8_t *q
 
 // The LM head: the W8A8 mat-vec (1 <= b <= 16, split 1) that also leaves, per
 // workgroup g and token t, the largest argmax key of the logits it wrote at
-// keys[t * grid + g]; *grid receives the grid size (at most
-// kArgKeysMaxGrid).  launch_argmax_fold then gives out[t], the smallest index
-// of row t's maximum.
-constexpr int kArgKeysMaxGrid = 2048;
+// keys[t * grid + g]; *grid receives the grid size (at most keys_cap).
+// launch_argmax_fold then gives out[t], the smallest index of row t's
+// maximum (at most kArgKeysMaxGrid keys per token).
+constexpr int kArgKeysMaxGrid = 32768;
 hipError_t launch_w8a8_matvec_keys(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int b, int N,
-                                   int K, uint16_t *y, uint64_t *keys, int *grid, hipStream_t st);
+                                   int K, uint16_t *y, uint64_t *keys, int keys_cap, int *grid, hipStream_t st);
 hipError_t launch_w8a8_mfvec_keys(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int b, int N,
-                                  int K, uint16_t *y, uint64_t *keys, int *grid, hipStream_t st);
+                                  int K, uint16_t *y, uint64_t *keys, int keys_cap, int *grid, hipStream_t st);
 hipError_t launch_argmax_fold(const uint64_t *keys, int b, int nkeys, int32_t *out, hipStream_t st);
-// Or from stored logits [b, N]: one key per (token, chunk of 4096 logits),
-// keys[t * argmax_chunks(N) + c] (needs argmax_chunks(N) <= kArgKeysMaxGrid).
-int argmax_chunks(int N);
-hipError_t launch_argmax_partial(const uint16_t *logits, int b, int N, uint64_t *keys, hipStream_t st);
 
 // FP8 (E4M3) W8A8: per-token quantizer and the fixed-tree mat-vec (1 <= b <= 16;
 // split > 1 writes fp32 subtree roots [split, b, N] for launch_fp8_combine).

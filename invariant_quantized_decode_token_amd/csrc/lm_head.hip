@@ -8,17 +8,14 @@
 // Each candidate is a 64-bit key (argmax_key in device.hpp): the bf16 value
 // mapped to an order-preserving integer, then the complemented index.  The
 // row maximum of the keys is unique and does not depend on the order in
-// which keys are compared, so any reduction tree gives it.  Two ways in:
-//  * the logits mat-vec (launch_w8a8_matvec_keys) leaves one key per
-//    workgroup and token, the largest of the outputs that workgroup wrote, so
-//    the logits are not read back;
-//  * k_argmax_partial reduces chunks of stored logits to one key each.
-// k_argmax_fold then folds a token's keys.  Measured on MI355X with the
-// Qwen3-8B head (151936 x 4096): from b = 2 the keyed mat-vec saves 2-4 us
-// per call; at b = 1 the mat-vec is fastest with one workgroup per row group
-// (19k workgroups), whose keys take longer to fold than the chunked re-read
-// of 300 KB of logits (a persistent keyed grid cost 4 us more), so one token
-// re-reads its logits.
+// which keys are compared, so any reduction tree gives it.  The logits
+// mat-vec (launch_w8a8_matvec_keys) leaves one key per workgroup and token,
+// the largest of the outputs that workgroup wrote, so the logits are never
+// read back; k_argmax_fold folds a token's keys.  Measured on MI355X with the
+// Qwen3-8B head (151936 x 4096), against a chunked re-read of the stored
+// logits: 2-4 us faster per call from b = 2, the same at b = 1 (the dot4
+// mat-vec's 18,992 workgroups each leave a key; a persistent keyed grid of
+// 1024-4096 workgroups cost 4-7 us, its last row groups ending unevenly).
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -26,9 +23,6 @@ namespace iqd {
 namespace {
 
 constexpr int kFoldThreads = 1024;
-constexpr int kFoldPerThread = (kArgKeysMaxGrid + kFoldThreads - 1) / kFoldThreads;  // all key loads in flight at once
-constexpr int kArgThreads = 256;
-constexpr int kArgPerThread = 16;
 
 template <int NT>
 __device__ __forceinline__ uint64_t block_max(uint64_t best) {
@@ -43,60 +37,38 @@ __device__ __forceinline__ uint64_t block_max(uint64_t best) {
     return k;
 }
 
-// Workgroup (c, t) reduces logits [c * C, (c + 1) * C) of token t,
-// C = kArgThreads * kArgPerThread, to one key.  All of a thread's loads are
-// issued before the first is used.
-__global__ __launch_bounds__(kArgThreads) void k_argmax_partial(const uint16_t *__restrict__ logits, int N,
-                                                                int nchunk, uint64_t *__restrict__ part) {
-    const int c = blockIdx.x, t = blockIdx.y;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(logits + static_cast<int64_t>(t) * N), 0, 2 * N, 0x00020000);
-    const int n0 = c * kArgThreads * kArgPerThread + static_cast<int>(threadIdx.x);
-    uint32_t h[kArgPerThread];
-#pragma unroll
-    for (int j = 0; j < kArgPerThread; ++j) h[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * (n0 + j * kArgThreads), 0, 0);
-    uint64_t best = 0;
-#pragma unroll
-    for (int j = 0; j < kArgPerThread; ++j) {
-        const int n = n0 + j * kArgThreads;
-        if (n < N) best = umax64(best, argmax_key(h[j], static_cast<uint32_t>(n)));
-    }
-    const uint64_t k = block_max<kArgThreads>(best);
-    if (threadIdx.x == 0) part[static_cast<int64_t>(t) * nchunk + c] = k;
-}
-
-// One workgroup per token folds its nkeys (<= kArgKeysMaxGrid) keys.
+// One workgroup per token folds its nkeys (<= PT * kFoldThreads) keys; every
+// key load is in flight at once (buffer loads: keys past nkeys read zeros,
+// which never win).
+template <int PT>
 __global__ __launch_bounds__(kFoldThreads) void k_argmax_fold(const uint64_t *__restrict__ keys, int nkeys,
                                                               int32_t *__restrict__ out) {
     const int t = blockIdx.x;
-    const uint64_t *kt = keys + static_cast<int64_t>(t) * nkeys;
-    uint64_t k[kFoldPerThread];
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint64_t *>(keys + static_cast<int64_t>(t) * nkeys), 0, 8 * nkeys, 0x00020000);
+    uint64_t k[PT];
 #pragma unroll
-    for (int j = 0; j < kFoldPerThread; ++j) {
-        const int i = static_cast<int>(threadIdx.x) + j * kFoldThreads;
-        k[j] = i < nkeys ? kt[i] : 0;
-    }
+    for (int j = 0; j < PT; ++j)
+        k[j] = __builtin_bit_cast(
+            uint64_t, __builtin_amdgcn_raw_buffer_load_b64(kr, 8 * (static_cast<int>(threadIdx.x) + j * kFoldThreads), 0, 0));
     uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < kFoldPerThread; ++j) best = umax64(best, k[j]);
+    for (int j = 0; j < PT; ++j) best = umax64(best, k[j]);
     best = block_max<kFoldThreads>(best);
     if (threadIdx.x == 0) out[t] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(best & 0xFFFFFFFFu));
 }
 
 }  // namespace
 
-int argmax_chunks(int N) { return (N + kArgThreads * kArgPerThread - 1) / (kArgThreads * kArgPerThread); }
-
-hipError_t launch_argmax_partial(const uint16_t *logits, int b, int N, uint64_t *keys, hipStream_t st) {
-    const int nchunk = argmax_chunks(N);
-    if (nchunk > kArgKeysMaxGrid || b < 1 || b > 65535) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_argmax_partial, dim3(nchunk, b), dim3(kArgThreads), 0, st, logits, N, nchunk, keys);
-    return hipGetLastError();
-}
-
 hipError_t launch_argmax_fold(const uint64_t *keys, int b, int nkeys, int32_t *out, hipStream_t st) {
+    static_assert(kArgKeysMaxGrid <= 32 * kFoldThreads, "fold capacity");
     if (nkeys < 1 || nkeys > kArgKeysMaxGrid || b < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_argmax_fold, dim3(b), dim3(kFoldThreads), 0, st, keys, nkeys, out);
+    if (nkeys <= 2 * kFoldThreads)
+        hipLaunchKernelGGL((k_argmax_fold<2>), dim3(b), dim3(kFoldThreads), 0, st, keys, nkeys, out);
+    else if (nkeys <= 8 * kFoldThreads)
+        hipLaunchKernelGGL((k_argmax_fold<8>), dim3(b), dim3(kFoldThreads), 0, st, keys, nkeys, out);
+    else
+        hipLaunchKernelGGL((k_argmax_fold<32>), dim3(b), dim3(kFoldThreads), 0, st, keys, nkeys, out);
     return hipGetLastError();
 }
 

@@ -177,8 +177,9 @@ hipError_t launch_w8a8_matvec_fused(const uint16_t *x, const int8_t *w, const fl
 }
 
 hipError_t launch_w8a8_matvec_keys(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int b, int N,
-                                   int K, uint16_t *y, uint64_t *keys, int *grid, hipStream_t st) {
-    if (use_mfvec(b, N, K)) return launch_w8a8_mfvec_keys(q, s_a, w, s_w, b, N, K, y, keys, grid, st);
+                                   int K, uint16_t *y, uint64_t *keys, int keys_cap, int *grid, hipStream_t st) {
+    if (keys_cap < 1) return hipErrorInvalidValue;
+    if (use_mfvec(b, N, K)) return launch_w8a8_mfvec_keys(q, s_a, w, s_w, b, N, K, y, keys, keys_cap, grid, st);
     MvArgs a{};
     a.q = q;
     a.s_a = s_a;
@@ -188,6 +189,7 @@ hipError_t launch_w8a8_matvec_keys(const int8_t *q, const float *s_a, const int8
     a.K = K;
     a.y = y;
     a.keys = keys;
+    a.keys_cap = keys_cap;
     a.split = 1;
     switch (b) {
         case 1: return launch_b<1, true>(a, st, grid);

@@ -21,6 +21,7 @@ struct MvArgs {
     uint16_t *y;
     int32_t *part;  // [split, B, N] when split > 1
     uint64_t *keys; // KEYS: [B][gridDim.x], each workgroup's largest argmax key per token
+    int keys_cap;   // KEYS (host side): the most workgroups the keys may cover
     int split;
     int ks;      // waves sharing one row group along K (divides the wave count)
     int nsteps;  // row-group steps: ceil(N / rows per step)
@@ -300,8 +301,8 @@ __global__ __launch_bounds__(256) void k_w8a8_combine(const int32_t *__restrict_
 // (row group, K part) units for about 16 waves per CU; grid = 0 gives one
 // workgroup per row-group step (with LDS: at most as many workgroups as fit,
 // persistent over the steps, so that activations are staged once each).
-// KEYS: the grid is capped at kArgKeysMaxGrid (the kernel is persistent over
-// row groups) and *grid_out receives it.
+// KEYS: the grid is capped at a.keys_cap (the kernel is persistent over row
+// groups) and *grid_out receives it.
 template <int B, int RS, int U, int NW, int D, int XB = 0, bool KEYS = false>
 hipError_t mv_launch(MvArgs a, hipStream_t st, int cus, int ks, int grid, bool lds = false, int *grid_out = nullptr) {
     static_assert(XB == 0 || B <= 2, "fused quantization: one or two tokens (the kernel's token test)");
@@ -324,7 +325,7 @@ hipError_t mv_launch(MvArgs a, hipStream_t st, int cus, int ks, int grid, bool l
     if constexpr (XB == 0) {
         if (!lds) {
             if (grid <= 0 || grid > a.nsteps) grid = a.nsteps;
-            if (KEYS && grid > kArgKeysMaxGrid) grid = kArgKeysMaxGrid;
+            if (KEYS && grid > a.keys_cap) grid = a.keys_cap;
             if (grid_out) *grid_out = grid;
             hipLaunchKernelGGL((k_w8a8_matvec<B, RS, U, NW, D, false, 0, KEYS>), dim3(grid, a.split), dim3(NW * kWave),
                                0, st, a);
@@ -347,7 +348,7 @@ hipError_t mv_launch(MvArgs a, hipStream_t st, int cus, int ks, int grid, bool l
         grid = cus * per_cu;
     }
     if (grid > a.nsteps) grid = a.nsteps;
-    if (KEYS && grid > kArgKeysMaxGrid) grid = kArgKeysMaxGrid;
+    if (KEYS && grid > a.keys_cap) grid = a.keys_cap;
     if (grid_out) *grid_out = grid;
     hipLaunchKernelGGL((k_w8a8_matvec<B, RS, U, NW, D, true, XB, KEYS>), dim3(grid, a.split), dim3(NW * kWave), smem,
                        st, a);

@@ -61,6 +61,7 @@ struct MfvArgs {
     int b, N, K;
     uint16_t *y;
     uint64_t *keys;  // KEYS: [b][gridDim.x], each workgroup's largest argmax key per token
+    int keys_cap;    // KEYS (host side): the most workgroups the keys may cover
     int ntiles;  // ceil(N / 16)
     int nch;     // chunks per tile per wave
 };
@@ -388,7 +389,7 @@ hipError_t launch_x(const MfvArgs &a, int grid, int smem, hipStream_t st, int *g
         grid = (per_cu < 1 ? 1 : per_cu) * device_info().cus;
     }
     if (grid > ngroups) grid = ngroups;
-    if (KEYS && grid > kArgKeysMaxGrid) grid = kArgKeysMaxGrid;  // the kernel walks tiles with a grid stride
+    if (KEYS && grid > a.keys_cap) grid = a.keys_cap;  // the kernel walks tiles with a grid stride
     if (grid_out) *grid_out = grid;
     hipLaunchKernelGGL((k_w8a8_mfvec<NW, KS, U, D, XB, WFIRST, FUSE, KEYS>), dim3(grid), dim3(NW * kWave), smem, st,
                        a);
@@ -502,7 +503,7 @@ hipError_t launch_w8a8_mfvec(const int8_t *q, const float *s_a, const int8_t *w,
 }
 
 hipError_t launch_w8a8_mfvec_keys(const int8_t *q, const float *s_a, const int8_t *w, const float *s_w, int b, int N,
-                                  int K, uint16_t *y, uint64_t *keys, int *grid, hipStream_t st) {
+                                  int K, uint16_t *y, uint64_t *keys, int keys_cap, int *grid, hipStream_t st) {
     if (!w8a8_mfvec_fits(b, N, K)) return hipErrorInvalidValue;
     MfvArgs a{};
     a.q = q;
@@ -514,6 +515,7 @@ hipError_t launch_w8a8_mfvec_keys(const int8_t *q, const float *s_a, const int8_
     a.K = K;
     a.y = y;
     a.keys = keys;
+    a.keys_cap = keys_cap;
     return launch_pick<false, true>(pick(b, N, K), a, st, grid);
 }
 

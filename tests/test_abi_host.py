@@ -59,9 +59,9 @@ def test_workspace_bytes():
     assert iqd.workspace_bytes(L.IQD_OP_BLOCKQ8, 16, 4096, 12288, 16) == 16 * 16 * 4096 * 4
     assert iqd.workspace_bytes(L.IQD_OP_BLOCKQ8, 16, 4096, 4096, 8) == 8 * 16 * 4096 * 4  # 16-leaf subtrees
     assert iqd.workspace_bytes(L.IQD_OP_BLOCKQ8, 16, 4096, 256, 16) == 0   # 16 > L = 8
-    # logits, then argmax keys: 8 bytes per (token, mat-vec workgroup), at most 2048 workgroups, 16 tokens a pass
-    assert iqd.workspace_bytes(L.IQD_OP_LM_HEAD, 5, 151936, 4096, 1) == (5 * 151936 * 2 + 15) // 16 * 16 + 5 * 2048 * 8
-    assert iqd.workspace_bytes(L.IQD_OP_LM_HEAD, 40, 1000, 512, 1) == 40 * 1000 * 2 + 16 * 2048 * 8
+    # logits, then argmax keys: 8 bytes per (token, mat-vec workgroup), 32768 keys for a pass of up to 16 tokens
+    assert iqd.workspace_bytes(L.IQD_OP_LM_HEAD, 5, 151936, 4096, 1) == (5 * 151936 * 2 + 15) // 16 * 16 + 32768 * 8
+    assert iqd.workspace_bytes(L.IQD_OP_LM_HEAD, 40, 1000, 512, 1) == 40 * 1000 * 2 + 32768 * 8
 
 
 A = 1 << 20  # fake, 16-byte aligned, never dereferenced
