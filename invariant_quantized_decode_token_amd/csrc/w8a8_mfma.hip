@@ -16,8 +16,11 @@
 // tokens, BN weight rows); each wave owns a (BM/GM) x (BN/GN) sub-tile of
 // v_mfma_i32_16x16x64_i8 accumulators.  K advances 128 bytes per stage.
 //  * Operands go from global memory straight into LDS (buffer loads with the
-//    LDS destination, 16 bytes per lane): an S-stage ring, S - 1 stages in
-//    flight, one barrier per stage, no registers spent on staging.
+//    LDS destination, 16 bytes per lane): an S-stage ring, one barrier per
+//    stage, no registers spent on staging.
+//  * The fragment reads of stage st + 1 are issued between the matrix
+//    operations of stage st, so that LDS reads and products overlap within
+//    a wave (two fragment register sets); loads run S - 2 stages ahead.
 //  * A load instruction fills 1 KiB of LDS in lane order.  Each lane picks
 //    the global 16 bytes that belong at its LDS slot: chunk c of row r is
 //    kept at slot c ^ ((r >> 1) & 7) of the row, so the 16 rows a fragment
@@ -71,18 +74,12 @@ __device__ __forceinline__ v4i lds_read(uint32_t addr) {
 // Wait for the outstanding LDS reads and mark the fragments as written by the
 // wait, so that no use of them is scheduled before it.
 template <int N>
-__device__ __forceinline__ void lgkm_tie(v4i (&f)[N]) {
-    if constexpr (N == 4) {
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3])::"memory");
-    } else if constexpr (N == 6) {
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5])::"memory");
-    } else {
-        static_assert(N == 8, "fragments per K step");
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]), "+v"(f[6]),
-                       "+v"(f[7])::"memory");
-    }
+__device__ __forceinline__ void lgkm_tie(v4i (&f)[2][N]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int x = 0; x < N; ++x) asm volatile("" : "+v"(f[h][x]));
 }
 
 // Byte offset, within a stage, of logical chunk c of staged row `row`.
@@ -179,31 +176,52 @@ __global__ __launch_bounds__(64 * GM * GN) void k_w8a8_mfma(const int8_t *__rest
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
+    static_assert(S >= 3, "stage st + 1 is read while stage st is multiplied");
 #pragma unroll
     for (int s = 0; s < S - 1; ++s) stage_load(s, s);
-    for (int st = 0; st < nst; ++st) {
-        wait_vm<(PA + PB) * (S - 2)>();  // this wave's loads of stage st have landed
-        __builtin_amdgcn_s_barrier();     // everyone's have, and everyone is done with stage st - 1
-        stage_load(st + S - 1, (st + S - 1) % S);  // into stage st - 1's slot
+    // Stage 0 in LDS for every wave, then its fragments.
+    wait_vm<(PA + PB) * (S - 2)>();
+    __builtin_amdgcn_s_barrier();
+    auto read_frags = [&](v4i (&f)[2][FM + FN], int st) __attribute__((always_inline)) {
         const uint32_t sb = lds_base + static_cast<uint32_t>((st % S) * STAGE);
-        v4i f0[FM + FN], f1[FM + FN];
 #pragma unroll
-        for (int x = 0; x < FM + FN; ++x) f0[x] = lds_read(sb + fa[0][x]);
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int x = 0; x < FM + FN; ++x) f1[x] = lds_read(sb + fa[1][x]);
-        lgkm_tie<FM + FN>(f0);
+            for (int x = 0; x < FM + FN; ++x) f[h][x] = lds_read(sb + fa[h][x]);
+    };
+    v4i fx[2][FM + FN], fy[2][FM + FN];
+    read_frags(fx, 0);
+    // Step st: wait for the fragments of stage st (read during step st - 1)
+    // and for this wave's loads of stage st + 1; the barrier then tells that
+    // every wave's loads of stage st + 1 have landed and that every wave has
+    // its fragments of stage st - 1, whose slot takes stage st + S - 1.  The
+    // products of stage st follow, each with one fragment read of stage
+    // st + 1 behind it.
+    auto step = [&](v4i (&cur)[2][FM + FN], v4i (&nxt)[2][FM + FN], int st) __attribute__((always_inline)) {
+        lgkm_tie<FM + FN>(cur);
+        wait_vm<(PA + PB) * (S - 3)>();
+        __builtin_amdgcn_s_barrier();
+        stage_load(st + S - 1, (st + S - 1) % S);
+        const uint32_t sb = lds_base + static_cast<uint32_t>(((st + 1) % S) * STAGE);
+        constexpr int NR = 2 * (FM + FN), NM = 2 * FM * FN;
+        static_assert(NM >= NR, "one fragment read per product at most");
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f0[i], f0[FM + j], acc[i][j], 0, 0, 0);
-        lgkm_tie<FM + FN>(f1);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f1[i], f1[FM + j], acc[i][j], 0, 0, 0);
+        for (int m = 0; m < NM; ++m) {
+            const int h = m / (FM * FN), i = (m % (FM * FN)) / FN, j = m % FN;
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur[h][i], cur[h][FM + j], acc[i][j], 0, 0, 0);
+            if (m < NR) nxt[m / (FM + FN)][m % (FM + FN)] = lds_read(sb + fa[m / (FM + FN)][m % (FM + FN)]);
+            __builtin_amdgcn_sched_barrier(0);  // keep the product / read order
+        }
+    };
+    int st = 0;
+    for (; st + 1 < nst; st += 2) {
+        step(fx, fy, st);
+        step(fy, fx, st + 1);
     }
+    if (st < nst) step(fx, fy, st);
+    // The last step read stage nst (zeros or a tile edge), which nothing uses;
+    // its registers must land before they are reused.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
     if (part) {
         // Exact int32 partial sums of this split, part[split][M][N]; the
@@ -311,21 +329,20 @@ hipError_t launch_w8a8_mfma(const int8_t *q, const float *s_a, const int8_t *w, 
         return hipSuccess;
     }
     // Tile choice, measured at b = 512 on the Qwen3-8B layers (weights read
-    // from HBM) against 64- to 256-token and -row tiles, 4 or 8 waves and
-    // rings of 2 to 5 stages; 8 waves throughout:
-    //  * 128 x 128 tiles with 2 stages (two workgroups per CU) while they,
-    //    times the K splits, number at least two per CU (gate_up);
-    //  * else 64 x 128 tiles with a 4-stage ring (one workgroup per CU) when
-    //    they fill at most one round of CUs (o and down: 17.7 and 40.0 us
-    //    against 19.1 and 44.5 us with the 128 x 64, 3-stage tiles);
-    //  * else 128 x 128 tiles with a 4-stage ring (qkv: 24.3 against 25.4 us;
-    //    its 384 64 x 128 tiles take 1.5 rounds and 30 us).
+    // from HBM, eight copies in rotation), 8 waves throughout, one workgroup
+    // per CU (the rings take 96-128 KiB of LDS):
+    //  * 64 x 128 tiles (4 stages) when they, times the K splits, fill at
+    //    most one round of CUs and K <= 8192 (o: 17.0 us against 17.9 with
+    //    the 128 x 64 tiles);
+    //  * 128 x 64 tiles (5 stages) for such shapes with longer rows (down,
+    //    K = 12288: 45.8 against 49.0 us);
+    //  * else 128 x 128 tiles (4 stages; qkv 22.7 and gate_up 73.6 us, 384
+    //    and 1536 narrow tiles would take 1.5 and 6 rounds).
     const int cus = device_info().cus;
-    const int64_t big = static_cast<int64_t>((b + 127) / 128) * ((N + 127) / 128) * split;
     const int64_t narrow = static_cast<int64_t>((b + 63) / 64) * ((N + 127) / 128) * split;
-    hipError_t e = big >= 2 * cus   ? launch_tiles<128, 128, 2, 2, 4>(q, s_a, w, s_w, b, N, K, y, split, part, st)
-                   : narrow <= cus ? launch_tiles<64, 128, 4, 2, 4>(q, s_a, w, s_w, b, N, K, y, split, part, st)
-                                   : launch_tiles<128, 128, 4, 4, 2>(q, s_a, w, s_w, b, N, K, y, split, part, st);
+    hipError_t e = narrow > cus ? launch_tiles<128, 128, 4, 2, 4>(q, s_a, w, s_w, b, N, K, y, split, part, st)
+                   : K <= 8192  ? launch_tiles<64, 128, 4, 2, 4>(q, s_a, w, s_w, b, N, K, y, split, part, st)
+                                : launch_tiles<128, 64, 5, 4, 2>(q, s_a, w, s_w, b, N, K, y, split, part, st);
     if (e != hipSuccess || split == 1) return e;
     return launch_w8a8_combine(part, s_a, s_w, b, N, split, y, st);
 }

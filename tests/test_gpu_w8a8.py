@@ -130,14 +130,17 @@ def test_matrix_core_shape_classes(iqd, N, K):
         assert_bits_equal(host_bits(y), ref[:b], f"N={N} K={K} b={b} vs b=1")
 
 
-# Both tile classes of the matrix-core GEMM for b > 16, with token and row
-# counts that are no multiple of any tile: 128 x 64 tiles (fewer than two
-# 128 x 128 tiles per CU; one and two M tiles, K of 2 and 8 stages plus a
-# ragged one) and 128 x 128 tiles.  Sampled rows against the oracle, every
-# row against the mat-vec over 16-token chunks.  Every split of K gives the
-# same bits, including splits left with no stage (K = 272 has three 128-byte
-# stages; splits 4 and 8 leave some workgroups only zero partials).
-@pytest.mark.parametrize("b,N,K", [(100, 20000, 272), (130, 2000, 1040), (300, 33000, 272)])
+# The three tile classes of the matrix-core GEMM for b > 16, with token and
+# row counts that are no multiple of any tile: 64 x 128 tiles (at most one
+# round of them, K <= 8192: three M tiles, 8 stages plus a ragged one),
+# 128 x 64 tiles with a 5-stage ring (the same for longer rows: 64 stages
+# plus a ragged one) and 128 x 128 tiles (more than a round of narrow tiles;
+# split 8 of the second shape moves there too).  Sampled rows against the
+# oracle, every row against the mat-vec over 16-token chunks.  Every split of
+# K gives the same bits, including splits left with no stage (K = 272 has
+# three 128-byte stages; splits 4 and 8 leave some workgroups only zero
+# partials).
+@pytest.mark.parametrize("b,N,K", [(100, 20000, 272), (130, 2000, 1040), (70, 1000, 8208), (300, 33000, 272)])
 def test_prefill_tile_classes_ragged(iqd, b, N, K):
     t = torch()
     g = W.rng(b * 7 + N + K)
