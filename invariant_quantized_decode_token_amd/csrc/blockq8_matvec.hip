@@ -71,6 +71,7 @@ struct BqArgs {
     int nslots;  // max(1, L / 32) chunk slots in the whole tree
     int ks;      // waves sharing a row group (aligned sub-ranges of slots)
     int nsteps;
+    int nb;      // tokens: at most the kernel's B (tokens past nb read zeros and write nothing)
 };
 
 // Insert the root of slot i (0-based within an aligned power-of-two range)
@@ -167,8 +168,8 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
     constexpr int NPH = NP >= 2 ? NP / 2 : 1;
 
     // Activations and their scales: one buffer for all tokens (b * K < 2^31).
-    const __amdgpu_buffer_rsrc_t qr = buf_rsrc(a.q, static_cast<int64_t>(B) * K);
-    const __amdgpu_buffer_rsrc_t dar = buf_rsrc(a.d_a, static_cast<int64_t>(B) * m * 4);
+    const __amdgpu_buffer_rsrc_t qr = buf_rsrc(a.q, static_cast<int64_t>(a.nb) * K);
+    const __amdgpu_buffer_rsrc_t dar = buf_rsrc(a.d_a, static_cast<int64_t>(a.nb) * m * 4);
 
     for (int step = blockIdx.x; step < a.nsteps; step += gridDim.x) {
         const int row0 = (step * rgs + rg) * RS;
@@ -352,11 +353,11 @@ __global__ __launch_bounds__(kBqThreads) void k_blockq8_matvec(BqArgs a) {
             const int r = idx / B;
             const int t = idx - r * B;
             const int row = row0 + r;
-            if (row < N) {
+            if (row < N && t < a.nb) {
                 if (a.split == 1)
                     a.y[static_cast<int64_t>(t) * N + row] = bf16_rne(root);
                 else
-                    a.part[(static_cast<int64_t>(s) * B + t) * N + row] = root;
+                    a.part[(static_cast<int64_t>(s) * a.nb + t) * N + row] = root;
             }
         }
         if (ks > 1) __syncthreads();
@@ -406,8 +407,15 @@ hipError_t launch_b(const BqArgs &base, hipStream_t st) {
     return launch_rs<B, RS, 1, FMT>(a, grid, st);
 }
 
+// q8_0 at 11 <= b <= 15 runs the 16-token kernel (the other tokens read
+// zeros and are not written): measured on MI355X at 12288 -> 4096, 28.4-29.1
+// us against 32.0-35.1 with the b-token kernels (the same bits); the kq6 and
+// kq4 kernels at those b are as fast as or faster than their 16-token ones.
 template <int FMT>
-hipError_t launch_any_b(const BqArgs &a, int b, hipStream_t st) {
+hipError_t launch_any_b(const BqArgs &base, int b, hipStream_t st) {
+    BqArgs a = base;
+    a.nb = b;
+    if (FMT == kFmtQ8 && b >= 11 && b <= 15) b = 16;
     switch (b) {
         case 1: return launch_b<1, FMT>(a, st);
         case 2: return launch_b<2, FMT>(a, st);
