@@ -65,7 +65,13 @@ hipError_t launch_cfg(const MvArgs &a, hipStream_t st, int ks, bool lds, int *gr
 template <int B, bool KEYS = false>
 hipError_t launch_b(const MvArgs &a, hipStream_t st, int *grid_out = nullptr) {
     const int64_t wbytes = static_cast<int64_t>(a.N) * a.K;
-    const bool big = wbytes >= kLdsMinWeightBytes && static_cast<int64_t>(B) * a.K / a.split <= 128 * 1024;
+    // Past 8 tokens the LDS-staged configuration pays only while the
+    // activations leave room for a second workgroup (12288 -> 4096 at b = 10,
+    // 120 KiB of activations: 21.1 us staged against 15.7 read through L1);
+    // up to 8 tokens its 16-wave workgroups pay up to 128 KiB (Qwen3-14B down,
+    // 17408 -> 5120 at b = 7: 25.0 against 28.8 us).
+    const int64_t act_bytes = static_cast<int64_t>(B) * a.K / a.split;
+    const bool big = wbytes >= kLdsMinWeightBytes && act_bytes <= (B <= 8 ? 128 : 64) * 1024;
     if constexpr (B <= 4) {
         // K split over all four waves of a row group past K = 4096 (b = 1:
         // 12288 -> 4096 10.3 against 11.0 us with two; 5120 -> 5120 7.1

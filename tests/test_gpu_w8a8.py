@@ -104,12 +104,15 @@ def test_ragged_shapes_full_oracle(iqd, N, K):
         assert_bits_equal(host_bits(y), oy, f"N={N} K={K} b={b}")
 
 
-@pytest.mark.parametrize("N,K", [(4100, 1040), (8200, 2064), (4097, 272), (24592, 4096)])
+@pytest.mark.parametrize("N,K", [(4100, 1040), (8200, 2064), (4097, 272), (24592, 4096), (4100, 12304)])
 def test_matrix_core_shape_classes(iqd, N, K):
     """Shapes on both sides of the matrix-core mat-vec's launch classes (256
     and 512 tiles of 16 rows, a persistent grid past 256 workgroups), with N
     not a multiple of 16 and K not a multiple of 256, at every b <= 16;
-    rows sampled against the oracle, all rows against b = 1."""
+    rows sampled against the oracle, all rows against b = 1.  The long rows
+    (K = 12304, 50 MB of weights) take the dot4 kernel from b = 9, where the
+    activations no longer fit the matrix-core kernel's LDS, with its
+    activations read through L1 rather than staged."""
     t = torch()
     g = W.rng(N * 31 + K)
     w = W.int8_weights(g, N, K)
