@@ -193,6 +193,12 @@ __global__ __launch_bounds__(NW * kWave) void k_blockq8_mfvec(Bq8Args a) {
         da[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dar, v < nd ? 4 * v : kOob, 0, 0));
     }
     QChunk<U> ring[D];
+    // Every wave's activation loads go out before any wave's weight loads:
+    // behind the weights (HBM misses) they took 4-7 us to land; with the
+    // barrier the call at 4096 -> 4096, b = 9..16 took 10.8-11.1 against
+    // 12.4-13.1 us (per-wave timestamps showed the staging shrink from about
+    // 9000-15000 to 5000-9600 clocks).
+    __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int i = 0; i < D - 1; ++i) ring[i] = load_chunk(i);
     auto put = [&](int base) __attribute__((always_inline)) {
