@@ -696,7 +696,64 @@ def run_extra(iqd, W, np, torch, dev, time_fn, copies_past_cache):
             ext.append({"op": "attn_decode", "cells": cells, "Hq": Hq, "Hkv": Hkv, "D": D, "b": b,
                         "us": round(us, 2), "kv_GBs": round(kv_bytes / (us * 1e-6) / 1e9, 1)})
         del ks, vs
+    ext += run_shards(iqd, W, np, torch, dev, time_fn, copies_past_cache)
     return ext
+
+
+def run_shards(iqd, W, np, torch, dev, time_fn, copies_past_cache):
+    """One GPU's share of an 8-way tensor-parallel Qwen3-8B decode layer at
+    its real shape: column shards of qkv, o and gate_up (N / 8 weight rows),
+    a K shard of down (K / 8, whose int32 partial sums an exact all-reduce
+    would add; timed here as the same mat-vec with its epilogue) and a
+    vocabulary shard of the LM head (151936 / 8 rows).  Weight copies in
+    rotation past the cache, as for the other rows."""
+    G = 8
+    res = []
+    for li in range(4):
+        L = W.qwen3_8b_layer(li, tokens=8)
+        if L.name == "down":
+            w = np.ascontiguousarray(L.w[:, : L.K // G])
+            x, K, N, kind = L.x[:, : L.K // G], L.K // G, L.N, "K shard"
+        else:
+            w = np.ascontiguousarray(L.w[: L.N // G])
+            x, K, N, kind = L.x, L.K, L.N // G, "column shard"
+        s_w = np.ascontiguousarray(L.s_w[:N])
+        nc = copies_past_cache(N * K)
+        w0 = torch.from_numpy(w).to(dev)
+        wsl = [w0] + [w0.clone() for _ in range(nc - 1)]
+        swd = torch.from_numpy(s_w).to(dev)
+        xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        for b in (1, 8):
+            y = torch.empty((b, N), dtype=torch.bfloat16, device=dev)
+            wsp = torch.empty((max(16, iqd.workspace_bytes(iqd.IQD_OP_W8A8_BF16, b, N, K, 1)),), dtype=torch.uint8,
+                              device=dev)
+
+            def f(b=b, y=y, wsp=wsp):
+                for c in range(nc):
+                    iqd.w8a8_linear_bf16(xd[:b], wsl[c], swd, y=y, workspace=wsp)
+            us = time_fn(f) * 1e3 / nc
+            res.append({"op": "shard_8way", "layer": L.name, "kind": kind, "K": K, "N": N, "b": b, "us": round(us, 2),
+                        "weight_GBs": round((N * K + 4 * N) / (us * 1e-6) / 1e9, 1)})
+        del wsl, w0
+    Lh = W.lm_head_layer(tokens=8)
+    N = Lh.N // G
+    nc = copies_past_cache(N * Lh.K)
+    w0 = torch.from_numpy(np.ascontiguousarray(Lh.w[:N])).to(dev)
+    wsl = [w0] + [w0.clone() for _ in range(nc - 1)]
+    swd = torch.from_numpy(np.ascontiguousarray(Lh.s_w[:N])).to(dev)
+    q, sa = iqd.quantize_activations(torch.from_numpy(Lh.x.view(np.int16)).view(torch.bfloat16).to(dev))
+    for b in (1, 8):
+        am = torch.empty((b,), dtype=torch.int32, device=dev)
+        wsp = torch.empty((iqd.workspace_bytes(iqd.IQD_OP_LM_HEAD, b, N, Lh.K, 1),), dtype=torch.uint8, device=dev)
+
+        def fh(b=b, am=am, wsp=wsp):
+            for c in range(nc):
+                iqd.lm_head_argmax(q[:b], sa[:b], wsl[c], swd, logits=False, argmax=am, workspace=wsp)
+        us = time_fn(fh) * 1e3 / nc
+        res.append({"op": "shard_8way", "layer": "lm_head", "kind": "vocabulary shard", "K": Lh.K, "N": N, "b": b,
+                    "us": round(us, 2), "weight_GBs": round((N * Lh.K + 4 * N) / (us * 1e-6) / 1e9, 1)})
+    del wsl, w0
+    return res
 
 
 def run_cpu_baseline(np, layers, step_out, step_weight_bytes):
