@@ -44,6 +44,19 @@ def test_quantize_token_parity(iqd, shape):
     assert_bits_equal(host(s).view(np.uint32), os_.view(np.uint32), "s_a")
 
 
+@pytest.mark.parametrize("K", [512, 4096, 8192, 12288, 32768, 65536, 65552])
+def test_quantize_token_edge_rows(iqd, K):
+    """The standalone quantizer's kernels (one per row length class, the
+    last one the two-pass kernel) on rows aimed at its quotient's fast path
+    and its correctly rounded fallback: exact ties of x / s, a subnormal s
+    whose reciprocal overflows, a zero row, values near the bf16 top."""
+    x = _edge_rows(K)
+    oq, os_ = oracle.quantize_token(x)
+    q, s = gpu_quant(iqd, x)
+    assert_bits_equal(host(q), oq, f"K={K} q")
+    assert_bits_equal(host(s).view(np.uint32), os_.view(np.uint32), f"K={K} s_a")
+
+
 def test_quantize_token_qwen3_activations(iqd):
     for i in range(4):
         L = W.qwen3_8b_layer(i, tokens=512)
