@@ -21,7 +21,8 @@ oracle's: `mismatches` counts the differing bf16 outputs.  Both must be 0;
 the run exits with status 1 otherwise (after printing its line).
 
 value = weight bytes streamed per step (int8 weights + fp32 scales) / step
-time (the median of 10 timed groups of steps), in GB/s.  The roofline object
+time (the median of 10 timed groups of steps, each group one replay of a
+graph that holds its steps back to back), in GB/s.  The roofline object
 times the dominant kernels, the 32 W8A8 mat-vec launches of a step (on the
 step's quantized activations), alone with HIP events on the stream they run
 on, next to a plain streaming read of the same weight bytes per launch (the
@@ -131,7 +132,12 @@ def main():
     def bits(t):
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
-    def capture(fn):
+    def capture(fn, rep=1):
+        """A HIP graph of `rep` back-to-back runs of fn.  Each graph replay
+        costs about 4-5 us of fixed GPU time on MI355X (measured: a plain read
+        of 16.8 MB per launch took 4.34 us per launch in replays of 8 launches,
+        3.84 us in replays of 128), which a decode loop pays once per captured
+        step of hundreds of launches; timed graphs therefore hold many launches."""
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -140,7 +146,8 @@ def main():
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            fn()
+            for _ in range(rep):
+                fn()
         torch.cuda.synchronize()
         return g
 
@@ -157,11 +164,19 @@ def main():
         return e0.elapsed_time(e1) / reps  # ms per replay
 
     def time_fn(fn, reps=10):
-        """ms per replay of fn's graph: the median of 10 timed repeats of `reps`
-        replays each; time_fn.last keeps (median, minimum)."""
+        """ms per run of fn: fn is captured `rep` times into one graph, with
+        rep chosen so that a replay lasts at least about 1 ms of GPU time
+        (at most 64 runs), and the result is the median of 10 timed repeats of
+        `reps` replays each, divided by rep; time_fn.last keeps (median, minimum)."""
         g = capture(fn)
         g.replay()
-        ts = sorted(time_graph(g, reps) for _ in range(10))
+        one = time_graph(g, 3)
+        rep = max(1, min(64, int(1.0 / max(one, 1e-3))))
+        if rep > 1:
+            del g
+            g = capture(fn, rep)
+            g.replay()
+        ts = sorted(time_graph(g, reps) / rep for _ in range(10))
         med = 0.5 * (ts[4] + ts[5])
         time_fn.last = (med, ts[0])
         return med
@@ -237,24 +252,35 @@ def main():
                     "bitwise against the same token computed alone (b=1)"}
 
     # ---- the step: REPEATS timed groups, median and minimum ---------------------
-    g_step = capture(step)
-    for _ in range(args.warmup):
-        g_step.replay()
-    torch.cuda.synchronize()
+    # Each group of n steps is one replay of a graph holding n back-to-back
+    # steps (32 launches each), timed between HIP events: exactly K = args.steps
+    # steps are timed in all.
     groups = max(1, min(REPEATS, args.steps))
     per = [args.steps // groups + (1 if i < args.steps % groups else 0) for i in range(groups)]
-    group_ms = [time_graph(g_step, n) for n in per]
+
+    def time_groups(fn):
+        """ms per step of each timed group: one replay of a graph of n steps per group."""
+        graphs = {n: capture(fn, n) for n in sorted(set(per))}
+        for g in graphs.values():
+            g.replay()
+        torch.cuda.synchronize()
+        res = [time_graph(graphs[n], 1) / n for n in per]
+        graphs.clear()
+        return res
+
+    g_warm = capture(step)
+    for _ in range(args.warmup):
+        g_warm.replay()
+    torch.cuda.synchronize()
+    del g_warm
+    group_ms = time_groups(step)
     ms = statistics.median(group_ms)
     ms_min = min(group_ms)
     value = step_weight_bytes / (ms * 1e-3) / 1e9
     log(f"step: {ms:.4f} ms (median of {groups}), {value:.0f} GB/s")
 
     # ---- the same work as separate quantize + linear calls -------------------------
-    g_sep = capture(step_separate)
-    for _ in range(3):
-        g_sep.replay()
-    ms_sep = time_graph(g_sep, args.steps)
-    del g_sep
+    ms_sep = statistics.median(time_groups(step_separate))
 
     # ---- dominant kernel alone: the 32 W8A8 mat-vec launches of a step ------------
     # (w8a8_linear on the step's quantized activations: k_w8a8_matvec at b = 1
@@ -267,12 +293,8 @@ def main():
             c = bi % COPIES
             for li, L in enumerate(layers):
                 iqd.w8a8_linear(qs[li][:b], sas[li][:b], wsets[li][c], swsets[li], y=ys[(li, b)])
-    g_mv = capture(step_linear)
-    for _ in range(3):
-        g_mv.replay()
-    mv_ms = [time_graph(g_mv, n) for n in per]
+    mv_ms = time_groups(step_linear)
     ms_mv = statistics.median(mv_ms)
-    del g_mv
     n_launch = len(B_LIST) * len(layers)
     mv_bytes = sum(linear_bytes(L, b) for b in B_LIST for L in layers)
     avg_us = ms_mv * 1e3 / n_launch
@@ -289,11 +311,7 @@ def main():
             c = bi % COPIES
             for li in range(len(layers)):
                 iqd.read_ceiling(wsets[li][c], sink)
-    g_rd = capture(step_read)
-    for _ in range(3):
-        g_rd.replay()
-    ms_rd = statistics.median([time_graph(g_rd, n) for n in per])
-    del g_rd
+    ms_rd = statistics.median(time_groups(step_read))
     read_us_by_layer = {}
     for li, L in enumerate(layers):
         def rd(li=li):
@@ -340,8 +358,8 @@ def main():
             "weight_bytes_per_step": step_weight_bytes,
             "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
             "tokens_per_s_equiv": round(sum(B_LIST) / (ms * 1e-3), 1),
-            "timing": f"{groups} timed groups of {per[0]} step(s) (graph replays between HIP events); "
-                      "ms_per_step is their median",
+            "timing": f"{groups} timed groups of {per[0]} step(s), each group one replay of a graph of its "
+                      "steps back to back, between HIP events; ms_per_step is their median",
             "ms_per_step_min": round(ms_min, 5),
             "ms_per_step_groups": [round(v, 5) for v in group_ms],
             "separate_calls_ms_per_step": round(ms_sep, 5),
