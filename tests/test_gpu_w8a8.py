@@ -325,6 +325,64 @@ def _edge_rows(K):
     return rows  # row 0 stays all zero
 
 
+def _every_quotient_rows(nrows, K, seed):
+    """Token rows that each hold every bf16 value of magnitude in
+    [amax / 512, amax], both signs, in a seeded order, zeros after them; each
+    row has its own amax (bf16, exponent uniform in [-6, 10], mantissa
+    uniform). So for the row's scale s = amax / 127 every quotient x / s of
+    magnitude at least 1/4 occurs, with whatever lies near a half-integer:
+    the quantizers' fast path and their fallback to the correctly rounded
+    division both meet every value that scale can produce."""
+    g = W.rng(seed)
+    rows = np.zeros((nrows, K), np.uint16)
+    for i in range(nrows):
+        e = int(g.integers(-6, 11))
+        top = ((e + 127) << 7) | int(g.integers(0, 128))
+        pos = np.arange(top - (9 << 7), top + 1, dtype=np.uint16)  # bf16 patterns order as values
+        vals = np.concatenate([pos, pos | np.uint16(0x8000)])
+        assert vals.size <= K
+        rows[i, :vals.size] = vals[g.permutation(vals.size)]
+    return rows
+
+
+def test_quantize_token_every_quotient(iqd):
+    """The standalone quantizer on 64 rows of every quotient of their scale
+    (147,584 values), bit for bit against the oracle's division."""
+    x = _every_quotient_rows(64, 2320, 4242)
+    oq, os_ = oracle.quantize_token(x)
+    q, s = gpu_quant(iqd, x)
+    assert_bits_equal(host(q), oq, "q")
+    assert_bits_equal(host(s).view(np.uint32), os_.view(np.uint32), "s_a")
+
+
+@pytest.mark.parametrize("K", [2320, 4624])
+def test_fused_quantizer_every_quotient(iqd, K):
+    """The quantization inside the fused linear kernels on the same rows:
+    K = 2320 takes the matrix-core kernel with the quantization fused in
+    (b = 1..4), K = 4624 at b = 1 the dot4 kernel with it fused in (rows longer
+    than 4096, no more outputs than K).  The quantized activations and scales
+    it writes out, and its outputs, against the oracle."""
+    t = torch()
+    g = W.rng(K + 99)
+    N = 64
+    w = W.int8_weights(g, N, K)
+    s_w = W.log_uniform_scales(g, N)
+    x = _every_quotient_rows(16, K, 77 + K)
+    oq, osa = oracle.quantize_token(x)
+    oy = oracle.w8a8(oq, osa, w, s_w)
+    xd, wd, swd = dev(x), dev(w), dev(s_w)
+    for b in ((1, 2, 3, 4) if K < 4096 else (1,)):
+        for t0 in range(0, 16, b):
+            bb = min(b, 16 - t0)
+            q_out = t.empty((bb, K), dtype=t.int8, device="cuda")
+            s_out = t.empty((bb,), dtype=t.float32, device="cuda")
+            y = iqd.w8a8_linear_bf16(xd[t0:t0 + bb], wd, swd, q_out=q_out, s_a_out=s_out)
+            what = f"K={K} b={bb} t0={t0}"
+            assert_bits_equal(host(q_out), oq[t0:t0 + bb], what + " q")
+            assert_bits_equal(host(s_out).view(np.uint32), osa[t0:t0 + bb].view(np.uint32), what + " s_a")
+            assert_bits_equal(host_bits(y), oy[t0:t0 + bb], what + " y")
+
+
 @pytest.mark.parametrize("N,K", [(256, 512), (130, 4112), (4100, 1040), (8200, 2064), (300, 12304), (6144, 4096)])
 def test_fused_bf16_matches_quantize_then_linear(iqd, N, K):
     t = torch()
