@@ -1,0 +1,164 @@
+"""GPU parity on a seeded random sweep of shapes, token counts and K splits,
+for every linear entry point (tolerance 0 ulp).
+
+The fixed-shape tests aim at known edges.  This sweep crosses the launchers'
+dispatch boundaries at shapes nobody picked by hand: the kernel chosen by b,
+by the matrix size and by the row length, the split subtrees, the tiled
+prefill path past 16 tokens and the token chunks of 16.  Each case compares
+every output bit with the oracle; the oracle's own quantizers make the int8
+and E4M3 inputs, so no input comes from the GPU.  The draws are seeded, so a
+failure names a case that replays exactly."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import assert_bits_equal, dev, host, host_bits, torch
+
+pytestmark = pytest.mark.gpu
+
+CASES = 24
+SPLIT_MAX = 64
+
+
+@pytest.fixture(scope="module")
+def iqd():
+    import invariant_quantized_decode_token_amd as m
+
+    m.load()
+    return m
+
+
+def _pow2_ceil(v: int) -> int:
+    p = 1
+    while p < v:
+        p *= 2
+    return p
+
+
+def _split(g, limit: int) -> int:
+    """1 half of the time, else a power of two up to limit (at least 1)."""
+    limit = max(1, min(SPLIT_MAX, limit))
+    if g.random() < 0.5 or limit == 1:
+        return 1
+    return 1 << int(g.integers(1, int(np.log2(limit)) + 1))
+
+
+def _shape(g, kmult: int, kmax: int, bs, budget=2.5e8):
+    """(b, N, K): K a multiple of kmult in [kmult, kmax], N in [1, 3000], and
+    b * N * K within the oracle's budget for a case."""
+    b = int(g.choice(bs))
+    K = kmult * int(g.integers(1, kmax // kmult + 1))
+    N = int(g.integers(1, 3001))
+    while b * N * K > budget and N > 1:
+        N //= 2
+    return b, N, K
+
+
+def _x(g, b, K):
+    x = W.normal_bf16(g, b, K)
+    if K >= 100:
+        x, _ = W.add_outlier_channels(g, x)
+    return x
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_w8a8_linear_random(iqd, seed):
+    g = W.rng(71000 + seed)
+    b, N, K = _shape(g, 16, 6400, [1, 2, 3, 4, 5, 7, 8, 9, 12, 16, 17, 24, 40])
+    split = _split(g, K // 16)
+    w = W.int8_weights(g, N, K)
+    s_w = W.log_uniform_scales(g, N)
+    q, s_a = oracle.quantize_token(_x(g, b, K))
+    want = oracle.w8a8(q, s_a, w, s_w)
+    y = iqd.w8a8_linear(dev(q), dev(s_a), dev(w), dev(s_w), split_k=split)
+    assert_bits_equal(host_bits(y), want, f"seed={seed} b={b} N={N} K={K} split={split}")
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_w8a8_linear_bf16_random(iqd, seed):
+    g = W.rng(72000 + seed)
+    b, N, K = _shape(g, 16, 12400, [1, 1, 2, 3, 4, 5, 6, 8, 11, 16, 20])
+    w = W.int8_weights(g, N, K)
+    s_w = W.log_uniform_scales(g, N)
+    x = _x(g, b, K)
+    q, s_a = oracle.quantize_token(x)
+    want = oracle.w8a8(q, s_a, w, s_w)
+    t = torch()
+    q_out = t.empty((b, K), dtype=t.int8, device="cuda")
+    s_out = t.empty((b,), dtype=t.float32, device="cuda")
+    y = iqd.w8a8_linear_bf16(dev(x), dev(w), dev(s_w), q_out=q_out, s_a_out=s_out)
+    what = f"seed={seed} b={b} N={N} K={K}"
+    assert_bits_equal(host_bits(y), want, what + " y")
+    assert_bits_equal(host(q_out), q, what + " q")
+    assert_bits_equal(host(s_out).view(np.uint32), s_a.view(np.uint32), what + " s_a")
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_blockq8_linear_random(iqd, seed):
+    g = W.rng(73000 + seed)
+    b, N, K = _shape(g, 32, 12800, [1, 2, 3, 4, 6, 8, 9, 11, 13, 16, 17, 20])
+    split = _split(g, _pow2_ceil(K // 32)) if b <= 16 else 1
+    w, d_w = W.q8_0_weights(g, N, K)
+    q, d_a = oracle.quantize_block32(_x(g, b, K))
+    want = oracle.blockq8(q, d_a, w, d_w)
+    y = iqd.blockq8_linear(dev(q), dev(d_a), dev(w), dev(d_w, "fp16"), split_k=split)
+    assert_bits_equal(host_bits(y), want, f"seed={seed} b={b} N={N} K={K} split={split}")
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_kq6_linear_random(iqd, seed):
+    g = W.rng(74000 + seed)
+    b, N, K = _shape(g, 256, 12800, [1, 2, 3, 4, 5, 8, 12, 16, 19])
+    split = _split(g, _pow2_ceil(K // 32)) if b <= 16 else 1
+    codes, sc, d = W.kq6_weights(g, N, K)
+    ql, qh = W.kq6_pack(codes)
+    q, d_a = oracle.quantize_block32(_x(g, b, K))
+    want = oracle.kq6_linear(q, d_a, ql, qh, sc, d)
+    y = iqd.kq6_linear(dev(q), dev(d_a), dev(ql), dev(qh), dev(sc), dev(d, "fp16"), split_k=split)
+    assert_bits_equal(host_bits(y), want, f"seed={seed} b={b} N={N} K={K} split={split}")
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_kq4_linear_random(iqd, seed):
+    g = W.rng(75000 + seed)
+    b, N, K = _shape(g, 256, 12800, [1, 2, 3, 4, 5, 8, 12, 16, 19])
+    split = _split(g, _pow2_ceil(K // 32)) if b <= 16 else 1
+    codes, scm, dm = W.kq4_weights(g, N, K)
+    ql = W.kq4_pack(codes)
+    q, d_a = oracle.quantize_block32(_x(g, b, K))
+    want = oracle.kq4_linear(q, d_a, ql, scm, dm)
+    y = iqd.kq4_linear(dev(q), dev(d_a), dev(ql), dev(scm), dev(dm, "fp16"), split_k=split)
+    assert_bits_equal(host_bits(y), want, f"seed={seed} b={b} N={N} K={K} split={split}")
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_fp8_linear_random(iqd, seed):
+    g = W.rng(76000 + seed)
+    b, N, K = _shape(g, 16, 12800, [1, 2, 3, 4, 5, 8, 12, 16, 19])
+    L = _pow2_ceil(K // 16)
+    split = _split(g, L // 64) if b <= 16 and L >= 128 else 1
+    w = W.e4m3_weight_codes(g, N, K)
+    s_w = W.log_uniform_scales(g, N, 1e-5, 1e-3)
+    q, s_a = oracle.quantize_fp8(_x(g, b, K))
+    want = oracle.fp8_linear(q, s_a, w, s_w)
+    y = iqd.fp8_linear(dev(q), dev(s_a), dev(w), dev(s_w), split_k=split)
+    assert_bits_equal(host_bits(y), want, f"seed={seed} b={b} N={N} K={K} split={split}")
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_lm_head_argmax_random(iqd, seed):
+    g = W.rng(77000 + seed)
+    b = int(g.choice([1, 2, 3, 5, 8, 16, 17, 24]))
+    K = 16 * int(g.integers(1, 160))
+    N = int(g.integers(1, 60001))
+    while b * N * K > 2.5e8 and N > 1:
+        N //= 2
+    w = W.int8_weights(g, N, K)
+    s_w = W.log_uniform_scales(g, N)
+    q, s_a = oracle.quantize_token(_x(g, b, K))
+    want_logits, want_argmax = oracle.lm_head_argmax(q, s_a, w, s_w)
+    lg, am = iqd.lm_head_argmax(dev(q), dev(s_a), dev(w), dev(s_w))
+    what = f"seed={seed} b={b} N={N} K={K}"
+    assert_bits_equal(host_bits(lg), want_logits, what + " logits")
+    assert_bits_equal(host(am), np.asarray(want_argmax, np.int32), what + " argmax")
