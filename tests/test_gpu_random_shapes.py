@@ -162,3 +162,21 @@ def test_lm_head_argmax_random(iqd, seed):
     what = f"seed={seed} b={b} N={N} K={K}"
     assert_bits_equal(host_bits(lg), want_logits, what + " logits")
     assert_bits_equal(host(am), np.asarray(want_argmax, np.int32), what + " argmax")
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_attn_decode_random(iqd, seed):
+    """Decode attention on random contexts, token counts and head layouts
+    (D = 128, Hq / Hkv up to 16), the cache allocated past the written cells
+    (those slots hold NaN patterns), every output bit against the oracle."""
+    g = W.rng(78000 + seed)
+    cells = int(g.integers(1, 5001))
+    b = int(min(cells, g.choice([1, 1, 2, 3, 4, 5, 8, 9, 16, 17])))
+    Hkv = int(g.choice([1, 2, 4, 8]))
+    G = int(g.choice([1, 2, 4, 8, 16]))
+    while b * G * Hkv * cells > 4e7 and G > 1:
+        G //= 2
+    case = W.attn_case(78000 + seed, b, cells, Hq=G * Hkv, Hkv=Hkv, capacity=cells + int(g.integers(0, 300)))
+    want = oracle.attn_decode(case.q, case.k, case.v, case.pos0, case.scale)
+    out = iqd.attn_decode(dev(case.q), dev(case.k), dev(case.v), case.pos0, float(case.scale))
+    assert_bits_equal(host_bits(out), want, f"seed={seed} b={b} cells={cells} Hq={G * Hkv} Hkv={Hkv}")
