@@ -83,6 +83,18 @@ def log(msg: str):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+class LoggedRows(list):
+    """Result rows that print a progress line as each one is added, so a long
+    run (under a profiler's counters, every dispatch serialised) shows it is
+    alive between phases."""
+
+    KEYS = ("config", "op", "layer", "K", "N", "b", "cells", "Hq")
+
+    def append(self, row):
+        super().append(row)
+        log("timed " + ", ".join(f"{k}={row[k]}" for k in self.KEYS if k in row))
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -104,6 +116,8 @@ def parse():
     p.add_argument("--no-prefill", action="store_true", help="skip timing the b=512 prefill pass")
     p.add_argument("--no-configs", action="store_true", help="skip the other configurations")
     p.add_argument("--extra", action="store_true", help="also time the FP8, k-quant and attention paths")
+    p.add_argument("--no-shards", action="store_true",
+                   help="with --extra, leave out the 8-way shard lines")
     p.add_argument("--calib", action="store_true",
                    help="end with one 256 MiB device-to-device copy (a known-size kernel for HBM counter scaling)")
     return p.parse_args()
@@ -458,7 +472,7 @@ def main():
         log("configs timed")
 
     if args.extra:
-        out["extra"] = run_extra(iqd, W, np, torch, dev, time_fn, copies_past_cache)
+        out["extra"] = run_extra(iqd, W, np, torch, dev, time_fn, copies_past_cache, args.no_shards)
         log("extra timed")
 
     if not args.no_cpu:
@@ -484,7 +498,7 @@ def main():
 def run_configs(iqd, W, np, torch, dev, to_dev_bf16, bits, time_fn, copies_past_cache, layers, wsets, swsets, xs):
     """The other configurations: per-call µs, weight GB/s, % of 8 TB/s and
     tokens/s (b / µs per call)."""
-    res = []
+    res = LoggedRows()
 
     def row(cfg, op, name, K, N, b, us, wbytes, **kw):
         # us: the median of 10 timed repeats (the time_fn call just made); us_min: their minimum, per call
@@ -632,8 +646,8 @@ def pow2_report(np, name, bits, q, s_a, own, p2, outs):
             "f3_order_disagreements": {"own": int((f3(*own) != a).sum()), "pow2": int((f3(*p2) != b).sum())}}
 
 
-def run_extra(iqd, W, np, torch, dev, time_fn, copies_past_cache):
-    ext = []
+def run_extra(iqd, W, np, torch, dev, time_fn, copies_past_cache, no_shards=False):
+    ext = LoggedRows()
     # kq6 superblocks (6.5625 bits per weight) on the Qwen3-8B o and down shapes
     for i in range(len(W.KQ6_SHAPES)):
         Lk = W.kq6_layer(i, tokens=16)
@@ -714,7 +728,8 @@ def run_extra(iqd, W, np, torch, dev, time_fn, copies_past_cache):
             ext.append({"op": "attn_decode", "cells": cells, "Hq": Hq, "Hkv": Hkv, "D": D, "b": b,
                         "us": round(us, 2), "kv_GBs": round(kv_bytes / (us * 1e-6) / 1e9, 1)})
         del ks, vs
-    ext += run_shards(iqd, W, np, torch, dev, time_fn, copies_past_cache)
+    if not no_shards:
+        ext += run_shards(iqd, W, np, torch, dev, time_fn, copies_past_cache)
     return ext
 
 
@@ -726,7 +741,7 @@ def run_shards(iqd, W, np, torch, dev, time_fn, copies_past_cache):
     vocabulary shard of the LM head (151936 / 8 rows).  Weight copies in
     rotation past the cache, as for the other rows."""
     G = 8
-    res = []
+    res = LoggedRows()
     for li in range(4):
         L = W.qwen3_8b_layer(li, tokens=8)
         if L.name == "down":
