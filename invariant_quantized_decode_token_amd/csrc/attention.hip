@@ -350,73 +350,105 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(AttnArgs a) {
 }
 
 // Merge the chunk partials of every row with two or more chunks, in
-// increasing chunk order.  One workgroup of kD threads per row; thread d owns
-// dim d.  The maximum is an exact reduction (any order).  Chunks go in
-// windows of kWin: a lane of each wave forms one chunk's weight, the wave
-// reads them back with readlane, and every load of the next window (values,
-// maxima, sums) is in flight while the current one is applied.  Two windows'
-// loads (kWin + 2 each) stay within the 63 a wave may have outstanding.
-// Measured at Qwen3-8B shapes, b = 1: 32768 cells 52.1 -> 43.9 us and 131072
-// cells 174 -> 140 us for the whole call, against one wave per row with 8
-// chunks in flight.
-constexpr int kWin = 28;
+// increasing chunk order.  One workgroup of kMergeThreads per row.  The
+// maximum is an exact reduction (any order).  The chunks go through LDS in
+// windows of kMW: a window's partial values are kMW * kD consecutive floats
+// (32 KB), which all the workgroup's threads load at once (4 x 16 bytes per
+// thread) with the window's maxima and sums; then threads 0..kD-1 (thread d
+// owns dim d) apply the window's chunks in order from LDS while the next
+// window's loads are in flight.  Two LDS buffers alternate, one barrier per
+// window.  Each row costs about one memory round trip per window, against
+// one per kD-thread register window of 28 chunks before (Qwen3-8B heads,
+// 32768 cells: 128 chunks, 7.2 us for the merge).
+constexpr int kMergeThreads = 512;
+constexpr int kMW = 64;
+constexpr int kMF4 = kMW * kD / 4 / kMergeThreads;  // 16-byte loads per thread per window
+static_assert(kMW * kD / 4 % kMergeThreads == 0, "a window is whole 16-byte loads per thread");
+static_assert(kMW <= kMergeThreads && kD <= kMergeThreads, "");
 
-__global__ __launch_bounds__(kD) void k_attn_merge(AttnArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void k_attn_merge(AttnArgs a) {
     const int64_t row = blockIdx.x;
     const int t = static_cast<int>(row / a.Hq);
     const int p = a.pos0 + t;
     const int n = p / kChunk + 1;
-    if (n < 2) return;
-    const int d = static_cast<int>(threadIdx.x);
-    const int lane = d % kWave;
+    if (n < 2) return;  // uniform over the workgroup
+    const int tid = static_cast<int>(threadIdx.x);
     const float *ml = a.ml + row * a.nc * 2;
-    const float *opart = a.o + row * a.nc * kD + d;
+    // Row `row`'s partial values: chunk c, dim d at [c * kD + d]; the base is
+    // 256-byte aligned and a row is nc * 512 bytes, so 16-byte loads line up.
+    const float4 *op = reinterpret_cast<const float4 *>(a.o + row * a.nc * kD);
+    __shared__ float4 so[2][kMW * kD / 4];
+    __shared__ float2 swl[2][kMW];  // (weight, sum) of each chunk of the window
+    __shared__ float sred[kMergeThreads / kWave];
 
-    // Window 0: values, and the lane's chunk maximum and sum.
-    float oc[kWin];
+    float4 r[kMF4];
+    float rm = 0.0f, rl = 0.0f;
+    auto issue = [&](int w0) {
 #pragma unroll
-    for (int i = 0; i < kWin; ++i) oc[i] = opart[static_cast<int64_t>(min(i, n - 1)) * kD];
-    float mc = ml[2 * min(lane, n - 1)], lc = ml[2 * min(lane, n - 1) + 1];
+        for (int j = 0; j < kMF4; ++j) {
+            const int i = tid + j * kMergeThreads;  // 16-byte slot of the window
+            const int c = w0 + i / (kD / 4);
+            r[j] = c < n ? op[static_cast<int64_t>(w0) * (kD / 4) + i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+        if (tid < kMW && w0 + tid < n) {
+            rm = ml[2 * (w0 + tid)];
+            rl = ml[2 * (w0 + tid) + 1];
+        }
+    };
+    issue(0);
 
-    float M = lane < n ? mc : -__builtin_inff();
-    for (int c = lane + kWave; c < n; c += kWave) M = fmaxf(M, ml[2 * c]);
+    float M = -__builtin_inff();
+    for (int c = tid; c < n; c += kMergeThreads) M = fmaxf(M, ml[2 * c]);
     M = fmaxf(M, xor_lane<1>(M));
     M = fmaxf(M, xor_lane<2>(M));
     M = fmaxf(M, xor_lane<4>(M));
     M = fmaxf(M, xor_lane<8>(M));
     M = fmaxf(M, xor_lane<16>(M));
     M = fmaxf(M, xor_lane<32>(M));
+    if (tid % kWave == 0) sred[tid / kWave] = M;
+    __syncthreads();
+    M = sred[0];
+#pragma unroll
+    for (int w = 1; w < kMergeThreads / kWave; ++w) M = fmaxf(M, sred[w]);
 
-    float L = 0.0f, O = 0.0f;
-    for (int c0 = 0; c0 < n; c0 += kWin) {
-        const int cn = min(kWin, n - c0);
-        const float w = attn_exp(mc - M);  // lanes past cn: unused
-        const float l = lc;
-        // The next window's loads (clamped to the last chunk; unused past n).
-        const int c1 = c0 + kWin;
-        float on[kWin];
+    // From -0: fma(w, x, -0) is w * x bit for bit (signed zeros included),
+    // so the first chunk needs no case of its own.
+    float L = -0.0f, O = -0.0f;
+    int buf = 0;
+    for (int w0 = 0; w0 < n; w0 += kMW, buf ^= 1) {
 #pragma unroll
-        for (int i = 0; i < kWin; ++i) on[i] = opart[static_cast<int64_t>(min(c1 + i, n - 1)) * kD];
-        mc = ml[2 * min(c1 + lane, n - 1)];
-        lc = ml[2 * min(c1 + lane, n - 1) + 1];
+        for (int j = 0; j < kMF4; ++j) so[buf][tid + j * kMergeThreads] = r[j];
+        if (tid < kMW) swl[buf][tid] = make_float2(attn_exp(rm - M), rl);  // slots past n: unused
+        __syncthreads();
+        if (w0 + kMW < n) issue(w0 + kMW);
+        if (tid < kD) {
+            const float *sv = reinterpret_cast<const float *>(so[buf]) + tid;
+            const int cn = min(kMW, n - w0);
+            int i = 0;
+            // Groups of 16 chunks: every LDS read of the group is issued
+            // before its chain of fused multiply-adds.
+            for (; i + 16 <= cn; i += 16) {
+                float2 wl[16];
+                float ov[16];
 #pragma unroll
-        for (int i = 0; i < kWin; ++i) {
-            if (i < cn) {  // uniform
-                const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), i));
-                const float li = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), i));
-                if (c0 + i == 0) {
-                    L = wi * li;
-                    O = wi * oc[i];
-                } else {
-                    L = __builtin_fmaf(wi, li, L);
-                    O = __builtin_fmaf(wi, oc[i], O);
+                for (int u = 0; u < 16; ++u) {
+                    wl[u] = swl[buf][i + u];
+                    ov[u] = sv[(i + u) * kD];
+                }
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    L = __builtin_fmaf(wl[u].x, wl[u].y, L);
+                    O = __builtin_fmaf(wl[u].x, ov[u], O);
                 }
             }
+            for (; i < cn; ++i) {
+                const float2 wl = swl[buf][i];
+                L = __builtin_fmaf(wl.x, wl.y, L);
+                O = __builtin_fmaf(wl.x, sv[i * kD], O);
+            }
         }
-#pragma unroll
-        for (int i = 0; i < kWin; ++i) oc[i] = on[i];
     }
-    a.out[row * kD + d] = bf16_rne(O / L);
+    if (tid < kD) a.out[row * kD + tid] = bf16_rne(O / L);
 }
 
 }  // namespace
@@ -487,7 +519,7 @@ hipError_t launch_attn_decode(const uint16_t *q, const uint16_t *k, const uint16
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !merge) return e;
-    hipLaunchKernelGGL(k_attn_merge, dim3(static_cast<unsigned>(b) * Hq), dim3(kD), 0, st, a);
+    hipLaunchKernelGGL(k_attn_merge, dim3(static_cast<unsigned>(b) * Hq), dim3(kMergeThreads), 0, st, a);
     return hipGetLastError();
 }
 
