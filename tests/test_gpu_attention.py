@@ -138,6 +138,19 @@ def test_merge_over_many_windows(iqd):
         assert_bits_equal(alone[0], got[t], f"token {t} alone")
 
 
+@pytest.mark.parametrize("cells", [16129, 16385, 32769, 33025])
+def test_merge_window_edges(iqd, cells):
+    """Rows whose chunk counts sit on the merge's 64-chunk window edges: a
+    3-token batch at the end of the context puts its rows at 63 / 63 / 64,
+    64 / 64 / 65, 128 / 128 / 129 and 129 / 129 / 130 chunks (one launch,
+    rows of different chunk counts), every output bit against the oracle."""
+    b = 3
+    case = W.attn_case(W.SEED_ATTN + cells + 5, b, cells, Hq=4, Hkv=1, capacity=cells + 3)
+    got = run(iqd, case)
+    want = oracle.attn_decode(case.q, case.k, case.v, case.pos0, case.scale)
+    assert_bits_equal(got, want, f"cells={cells}")
+
+
 @pytest.mark.parametrize("cells", [4096, 32768])
 def test_qwen3_8b_long_context_sampled_heads(iqd, cells):
     """Qwen3-8B attention (32 query heads, 8 kv heads, D = 128), b = 8 verify
