@@ -374,8 +374,10 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(AttnArgs a) {
     if (n < 2) return;  // uniform over the workgroup
     const int tid = static_cast<int>(threadIdx.x);
     const float *ml = a.ml + row * a.nc * 2;
-    // Row `row`'s partial values: chunk c, dim d at [c * kD + d]; the base is
-    // 256-byte aligned and a row is nc * 512 bytes, so 16-byte loads line up.
+    // Row `row`'s partial values: chunk c, dim d at [c * kD + d].  The
+    // workspace is 16-byte aligned (checked at the boundary), the values start
+    // a multiple of 256 bytes into it and a row is nc * 512 bytes, so the
+    // 16-byte loads line up.
     const float4 *op = reinterpret_cast<const float4 *>(a.o + row * a.nc * kD);
     __shared__ float4 so[2][kMW * kD / 4];
     __shared__ float2 swl[2][kMW];  // (weight, sum) of each chunk of the window
