@@ -373,34 +373,46 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(AttnArgs a) {
     const int n = p / kChunk + 1;
     if (n < 2) return;  // uniform over the workgroup
     const int tid = static_cast<int>(threadIdx.x);
-    const float *ml = a.ml + row * a.nc * 2;
-    // Row `row`'s partial values: chunk c, dim d at [c * kD + d].  The
-    // workspace is 16-byte aligned (checked at the boundary), the values start
-    // a multiple of 256 bytes into it and a row is nc * 512 bytes, so the
-    // 16-byte loads line up.
-    const float4 *op = reinterpret_cast<const float4 *>(a.o + row * a.nc * kD);
-    __shared__ float4 so[2][kMW * kD / 4];
+    // Row `row`'s partial values: chunk c, dim d at [c * kD + d]; its maxima
+    // and sums: (m, l) of chunk c at [2 c], [2 c + 1].  Buffer loads over the
+    // row's n chunks read zeros past them, so no load sits behind a branch.
+    // The workspace is 16-byte aligned (checked at the boundary), the values
+    // start a multiple of 256 bytes into it and a row is nc * 512 bytes, so
+    // the 16-byte loads line up.
+    const __amdgpu_buffer_rsrc_t orr = attn_rsrc(a.o + row * a.nc * kD, static_cast<int64_t>(n) * kD * 4);
+    const __amdgpu_buffer_rsrc_t mlr = attn_rsrc(a.ml + row * a.nc * 2, static_cast<int64_t>(n) * 8);
+    __shared__ v4i so[2][kMW * kD / 4];
     __shared__ float2 swl[2][kMW];  // (weight, sum) of each chunk of the window
     __shared__ float sred[kMergeThreads / kWave];
 
-    float4 r[kMF4];
+    v4i r[kMF4];
     float rm = 0.0f, rl = 0.0f;
     auto issue = [&](int w0) {
+        // Threads past the window's chunks read from an offset past the
+        // buffer (zeros, no memory access): a branch around this load would
+        // make the compiler wait for every load in flight, the next window's
+        // included, before the chain.  It goes out first, so that a wait for
+        // it leaves the window's values in flight.
+        const int off = tid < kMW ? 8 * (w0 + tid) : 0x7FFFFFF0;
+        const uint64_t u = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(mlr, off, 0, 0));
 #pragma unroll
         for (int j = 0; j < kMF4; ++j) {
             const int i = tid + j * kMergeThreads;  // 16-byte slot of the window
-            const int c = w0 + i / (kD / 4);
-            r[j] = c < n ? op[static_cast<int64_t>(w0) * (kD / 4) + i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            r[j] = __builtin_amdgcn_raw_buffer_load_b128(orr, 16 * (w0 * (kD / 4) + i), 0, 0);
         }
-        if (tid < kMW && w0 + tid < n) {
-            rm = ml[2 * (w0 + tid)];
-            rl = ml[2 * (w0 + tid) + 1];
-        }
+        rm = __uint_as_float(static_cast<uint32_t>(u));
+        rl = __uint_as_float(static_cast<uint32_t>(u >> 32));
     };
-    issue(0);
 
-    float M = -__builtin_inff();
-    for (int c = tid; c < n; c += kMergeThreads) M = fmaxf(M, ml[2 * c]);
+    // The first maxima load goes out before the first window's loads, so the
+    // wait for it leaves those in flight.
+    const float m0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mlr, 8 * tid, 0, 0));
+    issue(0);
+    float M = tid < n ? m0 : -__builtin_inff();  // zeros past n must not win
+    for (int c0 = kMergeThreads; c0 < n; c0 += kMergeThreads) {
+        const float mc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mlr, 8 * (c0 + tid), 0, 0));
+        M = c0 + tid < n ? fmaxf(M, mc) : M;
+    }
     M = fmaxf(M, xor_lane<1>(M));
     M = fmaxf(M, xor_lane<2>(M));
     M = fmaxf(M, xor_lane<4>(M));
@@ -424,7 +436,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(AttnArgs a) {
         __syncthreads();
         if (w0 + kMW < n) issue(w0 + kMW);
         if (tid < kD) {
-            const float *sv = reinterpret_cast<const float *>(so[buf]) + tid;
+            const float *sv = reinterpret_cast<const float *>(&so[buf][0]) + tid;
             const int cn = min(kMW, n - w0);
             int i = 0;
             // Groups of 16 chunks: every LDS read of the group is issued
